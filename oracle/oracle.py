@@ -1,0 +1,188 @@
+"""CPU oracle of the quantized weight sweep -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this module.  It wraps ``liboracle.so`` (plain C built with gcc,
+no SIMD intrinsics, no BLAS, no fast-math; see ``qg_oracle.c``), which shares
+no source with the GPU library.
+
+What it computes (the quantizer is the "Weights" item of the engine-internals
+list on the Quasar/q27 wiki: symmetric groupwise codes with fp16 scales,
+dequantized inside the weight-streaming product; group 32 and 4/5 bits):
+
+* ``quantize``: per row n and group g of 32 consecutive k,
+  ``s = fp16_RNE(double(max|w|) / Qmax)`` and
+  ``q = clamp(RNE(double(w) / double(s)), -Qmax, Qmax)`` (q = 0 when s = 0).
+* ``pack`` / ``unpack``: the tiled group-32 layout, written and read bit by bit.
+* ``sweep``: ``Y[m, n] = sum_k X[m, k] * (q[n, k] * s[n, k//32])`` in fp64,
+  ascending k, decoded from the packed bytes.
+* ``compare``: the acceptance test -- relative L2 over a job's Y at most 1e-4
+  and, per row m, ``max_n |Y - Yref| <= 1e-3 * ||X[m, :]||_2 * max(s)``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+REL_L2_TOL = 1e-4
+MAX_ABS_COEF = 1e-3
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.oracle_f64_to_f16.argtypes = [ctypes.c_double]
+        L.oracle_f64_to_f16.restype = ctypes.c_uint16
+        L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        L.oracle_f16_to_f64.restype = ctypes.c_double
+        L.oracle_f64_to_f16_array.argtypes = [vp, i64, vp]
+        L.oracle_f64_to_f16_array.restype = None
+        L.oracle_f16_to_f64_array.argtypes = [vp, i64, vp]
+        L.oracle_f16_to_f64_array.restype = None
+        L.oracle_packed_bytes.argtypes = [ci, i64, i64]
+        L.oracle_packed_bytes.restype = i64
+        L.oracle_quantize.argtypes = [vp, i64, i64, i64, ci, vp, vp]
+        L.oracle_quantize.restype = ci
+        L.oracle_pack.argtypes = [vp, vp, i64, i64, ci, vp]
+        L.oracle_pack.restype = ci
+        L.oracle_unpack.argtypes = [vp, i64, i64, ci, vp, vp]
+        L.oracle_unpack.restype = ci
+        L.oracle_dequant.argtypes = [vp, i64, i64, ci, i64, i64, vp]
+        L.oracle_dequant.restype = ci
+        L.oracle_sweep_f64.argtypes = [vp, i64, i64, ci, vp, i64, ci, vp, i64, vp, i64, ci]
+        L.oracle_sweep_f64.restype = ci
+        _lib = L
+    return _lib
+
+
+def _threads(n):
+    if n:
+        return int(n)
+    try:
+        c = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        c = os.cpu_count() or 1
+    return max(1, min(c, 16))
+
+
+class NonFiniteError(ValueError):
+    pass
+
+
+def f64_to_f16_bits(x) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64)).ravel()
+    out = np.empty(a.size, dtype=np.uint16)
+    lib().oracle_f64_to_f16_array(a.ctypes.data, a.size, out.ctypes.data)
+    return out.reshape(np.shape(x))
+
+
+def f16_bits_to_f64(h) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(h, dtype=np.uint16)).ravel()
+    out = np.empty(a.size, dtype=np.float64)
+    lib().oracle_f16_to_f64_array(a.ctypes.data, a.size, out.ctypes.data)
+    return out.reshape(np.shape(h))
+
+
+def packed_bytes(bits: int, N: int, K: int) -> int:
+    return int(lib().oracle_packed_bytes(bits, N, K))
+
+
+def quantize(W: np.ndarray, bits: int):
+    """Codes q (int8, [N, K]) and scale bits (uint16, [N, K/32])."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    codes = np.empty((N, K), dtype=np.int8)
+    scales = np.empty((N, K // 32), dtype=np.uint16)
+    rc = lib().oracle_quantize(W.ctypes.data, K, N, K, bits, codes.ctypes.data,
+                               scales.ctypes.data)
+    if rc == 3:
+        raise NonFiniteError("non-finite weight or fp16 scale overflow")
+    return codes, scales
+
+
+def pack(codes: np.ndarray, scales: np.ndarray, bits: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    N, K = codes.shape
+    out = np.empty(packed_bytes(bits, N, K), dtype=np.uint8)
+    lib().oracle_pack(codes.ctypes.data, scales.ctypes.data, N, K, bits, out.ctypes.data)
+    return out
+
+
+def quantize_pack(W: np.ndarray, bits: int) -> np.ndarray:
+    c, s = quantize(W, bits)
+    return pack(c, s, bits)
+
+
+def unpack(packed: np.ndarray, N: int, K: int, bits: int):
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    codes = np.empty((N, K), dtype=np.int8)
+    scales = np.empty((N, K // 32), dtype=np.uint16)
+    lib().oracle_unpack(packed.ctypes.data, N, K, bits, codes.ctypes.data, scales.ctypes.data)
+    return codes, scales
+
+
+def dequant(packed: np.ndarray, N: int, K: int, bits: int, row0: int = 0,
+            nrows: int | None = None) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    nrows = N - row0 if nrows is None else nrows
+    out = np.empty((nrows, K), dtype=np.float64)
+    rc = lib().oracle_dequant(packed.ctypes.data, N, K, bits, row0, nrows, out.ctypes.data)
+    if rc:
+        raise ValueError("row range out of bounds")
+    return out
+
+
+def sweep(packed: np.ndarray, N: int, K: int, bits: int, X: np.ndarray, cols=None,
+          nthreads: int | None = None) -> np.ndarray:
+    """Yref [M, ncols] in fp64 for X fp16 [M, K]; cols = None means all N."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    Xb = np.ascontiguousarray(np.asarray(X, dtype=np.float16)).view(np.uint16)
+    M = Xb.shape[0]
+    assert Xb.shape[1] == K
+    if cols is None:
+        c_ptr, ncols = None, N
+    else:
+        cols = np.ascontiguousarray(np.asarray(cols, dtype=np.int64))
+        c_ptr, ncols = cols.ctypes.data, cols.size
+    Y = np.empty((M, ncols), dtype=np.float64)
+    rc = lib().oracle_sweep_f64(packed.ctypes.data, N, K, bits, Xb.ctypes.data, K, M,
+                                Y.ctypes.data, ncols, c_ptr, ncols, _threads(nthreads))
+    if rc:
+        raise RuntimeError(f"oracle_sweep_f64 failed ({rc})")
+    return Y
+
+
+def compare(Y: np.ndarray, Yref: np.ndarray, X: np.ndarray, smax: float) -> dict:
+    """The acceptance test for one job (Y, Yref: [M, ncols]; X fp16 [M, K])."""
+    Y = np.asarray(Y, dtype=np.float64)
+    Yref = np.asarray(Yref, dtype=np.float64)
+    diff = Y - Yref
+    den = np.linalg.norm(Yref)
+    rel = float(np.linalg.norm(diff) / den) if den > 0 else float(np.linalg.norm(diff))
+    xn = np.linalg.norm(np.asarray(X, dtype=np.float64), axis=1)
+    bound = MAX_ABS_COEF * xn * smax
+    rowmax = np.abs(diff).max(axis=1) if diff.size else np.zeros(Y.shape[0])
+    finite = bool(np.isfinite(Y).all())
+    ok_rows = rowmax <= bound
+    return {
+        "rel_l2": rel,
+        "max_abs_ratio": float((rowmax / np.where(bound > 0, bound, 1)).max()) if rowmax.size else 0.0,
+        "finite": finite,
+        "ok": finite and rel <= REL_L2_TOL and bool(ok_rows.all()),
+    }
+
+
+def max_scale(packed: np.ndarray, N: int, K: int, bits: int) -> float:
+    _, s = unpack(packed, N, K, bits)
+    return float(np.abs(f16_bits_to_f64(s)).max())
