@@ -1,0 +1,229 @@
+"""Benchmark of the fused quantized weight sweep on one MI355X.
+
+A step is one qgemm_sweep call over the whole workload (every matrix of it,
+one launch), with weights, activations and outputs already resident in HBM.
+The headline line is the gate+up projection (34816 x 5120, 4-bit group-32,
+M = 1, single-stream decode); the same run also times the M = 6 verify
+workload (gate+up 4-bit + down 5-bit) and the full 64-layer 27B-class stack at
+M = 48 (8 slots x 6 tokens), reported in the same JSON line.
+
+Weight GB/s counts code and scale bytes (bits/8 per weight + 2 bytes per 32);
+tokens/s per sweep is M / step time.  The workloads that fit in the 256 MB
+last-level cache rotate over enough packed copies (>= 1 GB) that every step
+streams its weights from HBM.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only 2|3|4]
+       [--no-cpu] [--stack-layers L]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "weight GB/s (% of HBM peak) + verify tokens/s per sweep at M=1,6,48"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Bench:
+    def __init__(self, cfg, layers=None, rotate_bytes=1 << 30):
+        import torch
+
+        from self_speculative_verify_amd import qgemm
+        from synth import synth, workloads
+
+        self.qgemm = qgemm
+        self.wl = workloads.workload(cfg, layers) if layers else workloads.workload(cfg)
+        self.M = self.wl.Ms[0]
+        dev = torch.device("cuda:0")
+        stream = torch.cuda.current_stream()
+        maxel = max(m.N * m.K for m in self.wl.matrices)
+        tmp = torch.empty(maxel, dtype=torch.float32, device=dev)
+        packed = []
+        for m in self.wl.matrices:
+            w = tmp[: m.N * m.K].view(m.N, m.K)
+            synth.weights_gpu(m.seed, m.K, 0, m.N, workloads.SIGMA, w.data_ptr(), m.K,
+                              stream.cuda_stream, outlier_thresh=m.thresh,
+                              outlier_mult=workloads.OUTLIER_MULT)
+            packed.append(qgemm.pack(w, m.bits))
+        del tmp
+        self.weight_bytes = sum(workloads.weight_bytes(m.bits, m.N, m.K) for m in self.wl.matrices)
+        self.packed_bytes = sum(p.numel() for p in packed)
+        copies = max(1, -(-rotate_bytes // self.packed_bytes)) if self.packed_bytes < rotate_bytes else 1
+        self.copies = [packed] + [[p.clone() for p in packed] for _ in range(copies - 1)]
+        M = self.M
+        self.X = {}
+        for K in self.wl.distinct_K:
+            x = synth.x_fp16(self.wl.x_seed(K), M, K)
+            self.X[K] = torch.from_numpy(x).to(dev)
+        self.Y = [torch.empty((M, m.N), dtype=torch.float32, device=dev) for m in self.wl.matrices]
+        self.jobsets = []
+        for cp in self.copies:
+            self.jobsets.append([qgemm.make_job(p, m.bits, m.N, m.K, self.X[m.K], y, M)
+                                 for p, m, y in zip(cp, self.wl.matrices, self.Y)])
+        ws = max(qgemm.workspace_bytes(js) for js in self.jobsets)
+        self.ws = qgemm.Workspace(ws, device=dev)
+        # the job arrays are marshalled once; each step is one C call
+        self.arrays = [qgemm.job_array(js) for js in self.jobsets]
+        self.xbytes = sum(2 * M * K for K in self.wl.distinct_K)
+        self.ybytes = sum(4 * M * m.N for m in self.wl.matrices)
+        torch.cuda.synchronize()
+
+    def step(self, i):
+        q = self.qgemm
+        arr = self.arrays[i % len(self.arrays)]
+        st = q.lib().qgemm_sweep(arr, len(arr), self.ws.ptr, self.ws.nbytes, self.stream)
+        if st != q.OK:
+            raise q.QgemmError(st, "qgemm_sweep")
+
+    def run(self, steps, warmup):
+        import torch
+
+        self.stream = torch.cuda.current_stream().cuda_stream
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(steps):
+            self.step(warmup + i)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = e0.elapsed_time(e1) / steps
+        return ms, wall
+
+    def report(self, ms):
+        s = ms / 1e3
+        gbps = self.weight_bytes / s / 1e9
+        alg = self.weight_bytes + self.xbytes + self.ybytes
+        return {
+            "workload": self.wl.name,
+            "M": self.M,
+            "matrices": len(self.wl.matrices),
+            "ms_per_sweep": round(ms, 5),
+            "weight_GBps": round(gbps, 1),
+            "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "tokens_per_s": round(self.M / s, 1),
+            "alg_bytes": alg,
+            "alg_GBps": round(alg / s / 1e9, 1),
+            "weight_bytes": self.weight_bytes,
+            "rotated_copies": len(self.copies),
+        }
+
+
+def cpu_baseline():
+    """The oracle, untuned, on the host cores: the full M = 1 sweep of the
+    34816 x 5120 4-bit gate+up matrix (generation and packing untimed)."""
+    from oracle import oracle
+    from synth import synth, workloads
+
+    wl = workloads.workload(2)
+    m = wl.matrices[0]
+    W = synth.weights(m.seed, m.K, 0, m.N, workloads.SIGMA)
+    packed = oracle.quantize_pack(W, m.bits)
+    del W
+    X = synth.x_fp16(wl.x_seed(m.K), 1, m.K)
+    threads = oracle._threads(None)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.sweep(packed, m.N, m.K, m.bits, X, nthreads=threads)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0 or reps >= 20:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    wb = workloads.weight_bytes(m.bits, m.N, m.K)
+    return {"value": round(wb / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"full M=1 sweep of the 34816x5120 4-bit matrix, {reps} repetitions, "
+                      f"{dt * 1e3:.1f} ms each (fp64, scalar decode from the packed bytes)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", type=int, default=0, help="time one workload (2, 3 or 4) only")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--stack-layers", type=int, default=64)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the sweep shards "
+              "along N with no collective; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import __graft_entry__
+
+    __graft_entry__.ensure_built()
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    results = {}
+    order = [args.only] if args.only else [2, 3, 4]
+    for cfg in order:
+        log(f"[bench] workload {cfg}: building")
+        b = Bench(cfg, layers=args.stack_layers if cfg == 4 else None)
+        log(f"[bench] workload {cfg}: {len(b.wl.matrices)} matrices, {b.packed_bytes / 1e6:.1f} MB "
+            f"packed x {len(b.copies)} copies; timing {args.steps} steps")
+        ms, wall = b.run(args.steps, args.warmup)
+        results[cfg] = b.report(ms)
+        results[cfg]["wall_s"] = round(wall, 4)
+        log(f"[bench] workload {cfg}: {json.dumps(results[cfg])}")
+        del b
+        torch.cuda.empty_cache()
+
+    head = results[order[0]]
+    # dominant kernel: one sweep launch per step, so the event time per step is
+    # the kernel's average duration (launch gaps included)
+    roof = {
+        "bound": "hbm",
+        "achieved": head["alg_GBps"],
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(head["alg_GBps"] / HBM_PEAK_GBPS, 4),
+        "traffic": None,
+    }
+    line = {
+        "metric": METRIC,
+        "value": head["weight_GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_sweep"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": head["workload"], "M": head["M"],
+                   "matrices": head["matrices"]},
+        "hbm_frac": head["hbm_frac"],
+        "tokens_per_s": head["tokens_per_s"],
+        "per_M": {str(r["M"]): {k: r[k] for k in ("workload", "ms_per_sweep", "weight_GBps",
+                                                   "hbm_frac", "tokens_per_s")}
+                  for r in results.values()},
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        log("[bench] cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

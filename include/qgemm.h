@@ -1,0 +1,154 @@
+/*
+ * qgemm -- fused quantized weight sweep for MI355X (gfx950).
+ *
+ * One decode step of a self-speculative decoder streams every quantized linear
+ * weight once and multiplies it against a skinny activation panel of
+ * M = slots x (1 + draft tokens) rows, so a single weight read verifies
+ * several tokens (Quasar/q27 wiki: "decode physics" paragraph -- decode is
+ * weight-read bound and each accepted position per weight read is the lever;
+ * intro bullets -- concurrent slots share one fused weight sweep).  The
+ * weights are 4- or 5-bit symmetric group-wise codes with one fp16 scale per
+ * group, dequantized inside the product (Quasar wiki, engine-internals list,
+ * "Weights" item; group size 32 here).
+ *
+ * This header is the whole boundary: plain C, device pointers and sizes.
+ * The library allocates nothing that outlives a call and keeps no mutable
+ * global state; every buffer belongs to the caller.
+ *
+ * ---------------------------------------------------------------------------
+ * Quantizer (qgemm_pack).  W is logical [N][K] (N outputs, K inputs,
+ * Y = X * W^T).  For every row n and group g of 32 consecutive k:
+ *     amax = max |W[n,k]|                   (fp32)
+ *     s    = fp16_RNE((double)amax / Qmax)  Qmax = 7 (4-bit) or 15 (5-bit)
+ *     q    = 0 if s == 0, else clamp(RNE((double)W[n,k] / (double)s), +-Qmax)
+ *     u    = q + 2^(bits-1)                 (stored offset-binary code)
+ *
+ * Packed layout "QG32 tiled v0".  Tiles of 16 rows x 128 k; tile (rb, kt) is
+ * at byte (rb * NKT + kt) * TB, NKT = ceil(K/128), TB = 1152 (4-bit) or 1408
+ * (5-bit).  For element (n, k) let r = n mod 16, j = (k mod 128) / 32,
+ * c = (k mod 32) / 8, e = k mod 8:
+ *     low 4 bits of u  -> little-endian 32-bit word at byte 16*(r + 16c) + 4j,
+ *                         bit 4*(e >> 1) + 16*(e & 1)
+ *     bit 4 of u       -> 32-bit word at byte 1152 + 4*(r + 16c),
+ *                         bit (4 + 16*(e & 1) + 4j + (e >> 1)) mod 32  (5-bit)
+ *     s(n, 4kt + j)    -> IEEE binary16 at byte 1024 + 8r + 2j
+ * Rows n >= N and groups beyond K/32 are padding (u = 2^(bits-1), s = +0).
+ * Lane l = r + 16c of a 64-wide wave thus reads the 16 bytes at 16*l: chunk c
+ * (8 consecutive k) of the four groups of row r, already in fp16-pair order.
+ * Size: qgemm_packed_bytes(); 4.5 (4-bit) / 5.5 (5-bit) bits per weight.
+ *
+ * ---------------------------------------------------------------------------
+ * Sweep (qgemm_sweep).  For each job: Y[m][n] = sum_k X[m][k] * q[n][k] *
+ * s[n][k/32] for m < M, n < N.  X is fp16 (binary16 bits), Y is fp32 and is
+ * overwritten.  Products q*x are exact in fp32 and every group's partial sum
+ * is scaled by its fp32 scale; the result is within relative L2 1e-4 of the
+ * exact product and, per row m, within 1e-3 * ||X[m,:]||_2 * max(s) of it.
+ * Row m of Y depends only on row m of X and the matrices: for the same set of
+ * matrices in a sweep it is bitwise the same for any other rows and any M of
+ * one panel class -- GEMV M <= 8; MFMA M <= 16; MFMA 17 <= M <= 64 -- and
+ * within the tolerance above across classes.  Repeated calls are bitwise equal.
+ * ---------------------------------------------------------------------------
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QGEMM_OK = 0,
+  QGEMM_ERR_INVALID_ARG = 1,  /* an argument fails the rules below; nothing enqueued */
+  QGEMM_ERR_UNSUPPORTED = 2,  /* valid arguments this build cannot run (e.g. path) */
+  QGEMM_ERR_NONFINITE = 3,    /* pack: NaN/Inf weight or a scale that overflows fp16 */
+  QGEMM_ERR_HIP = 4           /* a HIP runtime call or launch failed */
+} qgemm_status;
+
+/* Which contraction a sweep uses.  AUTO picks by M (GEMV for small M, MFMA
+ * otherwise).  GEMV accepts M <= QGEMM_GEMV_MAX_M; MFMA accepts any M. */
+typedef enum {
+  QGEMM_PATH_AUTO = 0,
+  QGEMM_PATH_GEMV = 1,
+  QGEMM_PATH_MFMA = 2
+} qgemm_path;
+
+#define QGEMM_MAX_M 64
+#define QGEMM_GEMV_MAX_M 8
+
+/* One matrix of a sweep.  Pointers are device pointers.
+ *   packed : QG32 tiled buffer from qgemm_pack, 256-byte aligned, read-only
+ *   bits   : 4 or 5, as packed
+ *   N, K   : N >= 1; K >= 32 and K % 32 == 0
+ *   X      : binary16 [M][ldx], 16-byte aligned, ldx % 8 == 0, ldx >= K
+ *   Y      : fp32 [M][ldy], 16-byte aligned, ldy % 4 == 0, ldy >= N
+ *   M      : 1 .. QGEMM_MAX_M
+ * Y must not overlap X, any packed buffer or another job's Y. */
+typedef struct {
+  const void* packed;
+  const uint16_t* X;
+  float* Y;
+  int64_t N;
+  int64_t K;
+  int64_t ldx;
+  int64_t ldy;
+  int32_t M;
+  int32_t bits;
+} qgemm_job;
+
+/* Bytes of the packed buffer for an N x K matrix; 0 when the shape or bits
+ * are invalid. */
+size_t qgemm_packed_bytes(int bits, int64_t N, int64_t K);
+
+/* Quantize and pack W (fp32 device buffer, row stride ldw >= K floats) into
+ * `packed` (qgemm_packed_bytes() bytes, 256-byte aligned), padding included.
+ * Enqueued on `stream` (a hipStream_t; NULL = default stream), then the call
+ * synchronizes that stream once to report QGEMM_ERR_NONFINITE (the packed
+ * contents are then unspecified).  Packing is an offline step: it may allocate
+ * and free a 4-byte device flag inside the call. */
+qgemm_status qgemm_pack(const float* W, int64_t ldw, int64_t N, int64_t K, int bits,
+                        void* packed, void* stream);
+
+/* Workspace bytes the sweep of these jobs on this path needs (a device buffer
+ * the caller owns, 256-byte aligned); 0 when the jobs are invalid.  It holds
+ * the job table (more than 12 jobs), split-K arrival counters and partial
+ * sums.  The buffer must be zero-filled before its first use (for instance
+ * with qgemm_workspace_init); every completed sweep leaves its counters at
+ * zero again.  A workspace serves one sweep at a time: sweeps that overlap on
+ * one workspace race. */
+size_t qgemm_workspace_bytes(const qgemm_job* jobs, int njobs, int path);
+
+/* Zero-fill `ws_bytes` (a multiple of 4) of a workspace with a fill kernel on
+ * `stream` (no memset node, so it may be captured in a graph). */
+qgemm_status qgemm_workspace_init(void* workspace, size_t ws_bytes, void* stream);
+
+/* Y = X * W^T for every job on `stream`: one kernel launch per kernel class
+ * (jobs of equal panel height share one launch).  Asynchronous: argument
+ * errors return before anything is enqueued; launch failures return
+ * QGEMM_ERR_HIP; device faults surface at the caller's next synchronization.
+ * The `jobs` array is host memory read during the call. */
+qgemm_status qgemm_sweep(const qgemm_job* jobs, int njobs, void* workspace, size_t ws_bytes,
+                         void* stream);
+
+/* As qgemm_sweep with an explicit path (qgemm_path).  GEMV with any job's
+ * M > QGEMM_GEMV_MAX_M is QGEMM_ERR_INVALID_ARG. */
+qgemm_status qgemm_sweep_path(const qgemm_job* jobs, int njobs, int path, void* workspace,
+                              size_t ws_bytes, void* stream);
+
+/* The argument checks of qgemm_sweep_path alone (host only, no HIP call). */
+qgemm_status qgemm_validate(const qgemm_job* jobs, int njobs, int path, void* workspace,
+                            size_t ws_bytes);
+
+/* The path AUTO takes for panel height M (QGEMM_PATH_GEMV or _MFMA), or -1. */
+int qgemm_auto_path(int M);
+
+/* Static description of a status code. */
+const char* qgemm_status_string(qgemm_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

@@ -1,0 +1,181 @@
+"""Python binding of ``libqgemm.so`` (argument marshalling only).
+
+Every step of the sweep runs in the HIP library; this module turns torch
+device tensors into the plain pointers and sizes of the C boundary
+(``include/qgemm.h``) and raises on a non-OK status.  There is no fallback:
+if the library is missing or a call fails, it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemm.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NONFINITE, ERR_HIP = 0, 1, 2, 3, 4
+PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
+MAX_M = 64
+GEMV_MAX_M = 8
+
+# every symbol the boundary header declares
+EXPORTS = (
+    "qgemm_packed_bytes", "qgemm_pack", "qgemm_workspace_bytes", "qgemm_workspace_init",
+    "qgemm_sweep", "qgemm_sweep_path", "qgemm_validate", "qgemm_auto_path",
+    "qgemm_status_string",
+)
+
+
+class QgemmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class Job(ctypes.Structure):
+    """Mirror of ``qgemm_job``."""
+    _fields_ = [
+        ("packed", ctypes.c_void_p),
+        ("X", ctypes.c_void_p),
+        ("Y", ctypes.c_void_p),
+        ("N", ctypes.c_int64),
+        ("K", ctypes.c_int64),
+        ("ldx", ctypes.c_int64),
+        ("ldy", ctypes.c_int64),
+        ("M", ctypes.c_int32),
+        ("bits", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        jp = ctypes.POINTER(Job)
+        L.qgemm_packed_bytes.argtypes = [ci, i64, i64]
+        L.qgemm_packed_bytes.restype = sz
+        L.qgemm_pack.argtypes = [vp, i64, i64, i64, ci, vp, vp]
+        L.qgemm_pack.restype = ci
+        L.qgemm_workspace_bytes.argtypes = [jp, ci, ci]
+        L.qgemm_workspace_bytes.restype = sz
+        L.qgemm_workspace_init.argtypes = [vp, sz, vp]
+        L.qgemm_workspace_init.restype = ci
+        L.qgemm_sweep.argtypes = [jp, ci, vp, sz, vp]
+        L.qgemm_sweep.restype = ci
+        L.qgemm_sweep_path.argtypes = [jp, ci, ci, vp, sz, vp]
+        L.qgemm_sweep_path.restype = ci
+        L.qgemm_validate.argtypes = [jp, ci, ci, vp, sz]
+        L.qgemm_validate.restype = ci
+        L.qgemm_auto_path.argtypes = [ci]
+        L.qgemm_auto_path.restype = ci
+        L.qgemm_status_string.argtypes = [ci]
+        L.qgemm_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().qgemm_status_string(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != OK:
+        raise QgemmError(status, what)
+
+
+def _stream_ptr(stream) -> int:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def packed_bytes(bits: int, N: int, K: int) -> int:
+    return int(lib().qgemm_packed_bytes(bits, N, K))
+
+
+def auto_path(M: int) -> int:
+    return int(lib().qgemm_auto_path(M))
+
+
+def pack(W, bits: int, out=None, stream=None):
+    """Quantize and pack a CUDA fp32 [N, K] tensor; returns the uint8 buffer."""
+    import torch
+
+    assert W.is_cuda and W.dtype == torch.float32 and W.dim() == 2 and W.stride(1) == 1
+    N, K = W.shape
+    nbytes = packed_bytes(bits, N, K)
+    if nbytes == 0:
+        raise QgemmError(ERR_INVALID_ARG, "qgemm_packed_bytes")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    assert out.numel() >= nbytes and out.is_cuda
+    _check(lib().qgemm_pack(W.data_ptr(), W.stride(0), N, K, bits, out.data_ptr(),
+                            _stream_ptr(stream)), "qgemm_pack")
+    return out
+
+
+def make_job(packed, bits: int, N: int, K: int, X, Y, M: int) -> Job:
+    """Job for packed [N, K] weights, X fp16 [>=M, K] and Y fp32 [>=M, N] tensors."""
+    return Job(packed.data_ptr(), X.data_ptr(), Y.data_ptr(), N, K, X.stride(0), Y.stride(0), M, bits)
+
+
+def job_array(jobs):
+    arr = (Job * len(jobs))(*jobs)
+    return arr
+
+
+def workspace_bytes(jobs, path: int = PATH_AUTO) -> int:
+    arr = job_array(jobs)
+    return int(lib().qgemm_workspace_bytes(arr, len(jobs), path))
+
+
+class Workspace:
+    """A zero-initialised device workspace large enough for a set of sweeps."""
+
+    def __init__(self, nbytes: int, device="cuda", stream=None):
+        import torch
+
+        nbytes = max(256, (int(nbytes) + 255) // 256 * 256)
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _check(lib().qgemm_workspace_init(self.buf.data_ptr(), nbytes, _stream_ptr(stream)),
+               "qgemm_workspace_init")
+
+    @property
+    def ptr(self) -> int:
+        return self.buf.data_ptr()
+
+    @property
+    def nbytes(self) -> int:
+        return self.buf.numel()
+
+
+def sweep(jobs, workspace: Workspace, path: int = PATH_AUTO, stream=None) -> None:
+    arr = job_array(jobs)
+    _check(lib().qgemm_sweep_path(arr, len(jobs), path, workspace.ptr, workspace.nbytes,
+                                  _stream_ptr(stream)), "qgemm_sweep_path")
+
+
+def validate(jobs, path: int = PATH_AUTO, workspace_ptr: int = 0, ws_bytes: int = 0) -> int:
+    arr = job_array(jobs)
+    return int(lib().qgemm_validate(arr, len(jobs), path, workspace_ptr, ws_bytes))
+
+
+def sweep_one(packed, bits: int, N: int, K: int, X, M: int, Y=None, path: int = PATH_AUTO,
+              stream=None):
+    """Convenience: one matrix, fresh workspace, returns Y fp32 [M, N]."""
+    import torch
+
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=packed.device)
+    job = make_job(packed, bits, N, K, X, Y, M)
+    ws = Workspace(workspace_bytes([job], path), device=packed.device, stream=stream)
+    sweep([job], ws, path, stream)
+    return Y

@@ -1,0 +1,115 @@
+"""The C boundary on the CPU: the library loads, exports what the header
+declares, and validates arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import __graft_entry__
+from oracle import oracle
+from self_speculative_verify_amd import qgemm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib_built():
+    __graft_entry__.ensure_built("qgemm")
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "qgemm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(qgemm_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_match_header():
+    names = _header_functions()
+    assert names == sorted(qgemm.EXPORTS)
+    L = ctypes.CDLL(qgemm.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_packed_bytes_agrees_with_oracle():
+    for bits in (4, 5):
+        for N, K in [(1, 32), (15, 96), (16, 128), (1024, 1024), (34816, 5120), (5120, 17408),
+                     (7168, 5120), (33, 416)]:
+            assert qgemm.packed_bytes(bits, N, K) == oracle.packed_bytes(bits, N, K) > 0
+    assert qgemm.packed_bytes(3, 16, 128) == 0
+    assert qgemm.packed_bytes(4, 16, 100) == 0
+    assert qgemm.packed_bytes(4, 0, 128) == 0
+    assert qgemm.packed_bytes(4, 16, 0) == 0
+
+
+def test_auto_path_table():
+    for M in range(1, 65):
+        want = qgemm.PATH_GEMV if M <= 4 else qgemm.PATH_MFMA
+        assert qgemm.auto_path(M) == want
+    assert qgemm.auto_path(0) == -1 and qgemm.auto_path(65) == -1
+
+
+def _job(**kw):
+    base = dict(packed=0x100000, X=0x200000, Y=0x10000000, N=64, K=256, ldx=256, ldy=64, M=4, bits=4)
+    base.update(kw)
+    return qgemm.Job(base["packed"], base["X"], base["Y"], base["N"], base["K"], base["ldx"],
+                     base["ldy"], base["M"], base["bits"])
+
+
+BAD = [
+    dict(M=0), dict(M=65), dict(bits=3), dict(bits=8), dict(K=100), dict(K=0), dict(N=0),
+    dict(packed=0), dict(X=0), dict(Y=0), dict(packed=0x100080), dict(X=0x200008),
+    dict(Y=0x10000004), dict(ldx=255), dict(ldx=260), dict(ldy=63), dict(ldy=66),
+    dict(Y=0x200000),                      # Y overlaps X
+    dict(Y=0x100000 + 256),                # Y inside the packed weights
+]
+
+
+@pytest.mark.parametrize("kw", BAD)
+def test_validation_rejects(kw):
+    jobs = [_job(**kw)]
+    assert qgemm.validate(jobs, qgemm.PATH_AUTO, 0x40000000, 1 << 30) == qgemm.ERR_INVALID_ARG
+    assert qgemm.workspace_bytes(jobs) == 0
+
+
+def test_validation_accepts_and_sizes_workspace():
+    jobs = [_job(), _job(Y=0x20000000, M=33, bits=5, N=17, K=416, ldx=416, ldy=20)]
+    ws = qgemm.workspace_bytes(jobs)
+    assert ws > 0 and ws % 256 == 0
+    assert qgemm.validate(jobs, qgemm.PATH_AUTO, 0x40000000, ws) == qgemm.OK
+    assert qgemm.validate(jobs, qgemm.PATH_AUTO, 0x40000000, ws - 256) == qgemm.ERR_INVALID_ARG
+    assert qgemm.validate(jobs, qgemm.PATH_AUTO, 0x40000001, ws) == qgemm.ERR_INVALID_ARG
+    assert qgemm.validate(jobs, qgemm.PATH_AUTO, 0, ws) == qgemm.ERR_INVALID_ARG
+    # GEMV is limited to M <= 8
+    assert qgemm.validate(jobs, qgemm.PATH_GEMV, 0x40000000, 1 << 30) == qgemm.ERR_INVALID_ARG
+    assert qgemm.validate(jobs[:1], qgemm.PATH_GEMV, 0x40000000, 1 << 30) == qgemm.OK
+    assert qgemm.validate(jobs, 7, 0x40000000, 1 << 30) == qgemm.ERR_INVALID_ARG
+    assert qgemm.validate([], qgemm.PATH_AUTO, 0x40000000, 1 << 30) == qgemm.ERR_INVALID_ARG
+
+
+def test_workspace_does_not_depend_on_M_split():
+    """K slicing depends on shapes only: the workspace grows linearly in M."""
+    a = qgemm.workspace_bytes([_job(N=34816, K=5120, M=1, Y=0x100000000, ldy=34816,
+                                    packed=0x200000000, X=0x300000000, ldx=5120)])
+    b = qgemm.workspace_bytes([_job(N=34816, K=5120, M=2, Y=0x100000000, ldy=34816,
+                                    packed=0x200000000, X=0x300000000, ldx=5120)])
+    assert b > a > 0
+
+
+def test_status_strings():
+    for s in range(5):
+        assert qgemm.status_string(s)
+    assert "non-finite" in qgemm.status_string(qgemm.ERR_NONFINITE)
+
+
+def test_no_cpu_fallback_in_product_path():
+    """The package never imports the oracle and never computes on the host."""
+    pkg = os.path.join(ROOT, "self_speculative_verify_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "from oracle" not in text and "import oracle" not in text, f
+                assert "qg_oracle" not in text, f
