@@ -101,7 +101,7 @@ int kind_of(int path, int M) {
 
 int class_of(int kind, int M) {
   if (kind == kStreamGemv) return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
-  if (kind == kStreamMfma) return 16;
+  if (kind == kStreamMfma) return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 16;
   return (M + 15) / 16 * 16;
 }
 
@@ -162,7 +162,7 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path) {
       l.counters_off = off;
       off = round_up(off + (size_t)l.rbs * sizeof(int), 256);
       l.slots_off = off;
-      const int rows = l.kind == kStreamGemv ? l.cls : 16;
+      const int rows = l.cls;
       off = round_up(off + (size_t)2 * l.nwaves * rows * qg::kTileRows * sizeof(float), 256);
     }
   }
@@ -275,7 +275,7 @@ qgemm_status qgemm_sweep_path(const qgemm_job* jobs, int njobs, int path, void* 
       args.counters = (int*)(ws + l.counters_off);
       args.slots = (float*)(ws + l.slots_off);
       args.nwaves = l.nwaves;
-      args.slot_rows = l.kind == kStreamGemv ? l.cls : 16;
+      args.slot_rows = l.cls;
       grid = (l.nwaves + qg::kStreamWavesPerBlock - 1) / qg::kStreamWavesPerBlock;
     }
     if (qg::launch_sweep(l.kind, l.cls, args, grid, s) != hipSuccess) return QGEMM_ERR_HIP;

@@ -288,82 +288,92 @@ __device__ __forceinline__ const QG_CONST JobDesc* job_table(const SweepArgs& a)
 // other, and system-scope accesses bypass them, so no cache-wide writeback or
 // invalidate is needed on either side of the exchange.
 
-// Uniform (scalar) copy of the job fields the tile loop needs.
-struct JobRegs {
-  const uint8_t* packed;
-  const uint16_t* X;
-  int64_t ldx;
-  int32_t M, K, bits, nkt, nrb, ngroups;
-};
-
-__device__ __forceinline__ JobRegs fetch_job(const QG_CONST JobDesc* D, int j) {
-  JobRegs r;
-  r.packed = D[j].packed;
-  r.X = D[j].X;
-  r.ldx = D[j].ldx;
-  r.M = D[j].M;
-  r.K = D[j].K;
-  r.bits = D[j].bits;
-  r.nkt = D[j].nkt;
-  r.nrb = D[j].nrb;
-  r.ngroups = D[j].ngroups;
-  return r;
+// One k tile of the stream kernels.  kRagged: the tile may hold fewer than
+// four groups (the last tile of a row when K % 128 != 0).
+// MFMA: only the first NF of the lane's four accumulator rows are scaled and
+// kept (rows 4*(l/16)+i, i < NF); panels of at most 4 rows need NF = M.
+template <int BITS, int NF, bool kRagged>
+__device__ __forceinline__ void mfma1_tile(f4_t& acc, const WRegs& w, const uint8_t* xs, int lane, int gleft) {
+  const int r = lane & 15, c = lane >> 4;
+  const h2_t s01 = scale_pair(w.ws.x), s23 = scale_pair(w.ws.y);
+  const _Float16 sh[4] = {s01.x, s01.y, s23.x, s23.y};
+  const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    if (!kRagged || j < gleft) {
+      const h8_t q = unpack_chunk<BITS>(w.wc[j], w.wh, j);
+      const h8_t a = lds_h8(xs + r * kXRowBytes + 64 * j + 16 * c);
+      const f4_t p = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, q, zero, 0, 0, 0);
+      const float sj = (float)sh[j];
+#pragma unroll
+      for (int i = 0; i < NF; i++) acc[i] = __builtin_fmaf(sj, p[i], acc[i]);
+    }
+  }
 }
 
-struct Cursor {
-  int j, rb, kt;
-  JobRegs jr;
-};
+template <int BITS, int GM, bool kRagged>
+__device__ __forceinline__ void gemv1_tile(float (&acc)[GM], const WRegs& w, const uint8_t* xs, int lane,
+                                           int gleft, int M) {
+  const int c = lane >> 4;
+  const h2_t s01 = scale_pair(w.ws.x), s23 = scale_pair(w.ws.y);
+  const _Float16 sh[4] = {s01.x, s01.y, s23.x, s23.y};
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    if (!kRagged || j < gleft) {
+      const h8_t q = unpack_chunk<BITS>(w.wc[j], w.wh, j);
+      const h2_t q0 = {q[0], q[1]}, q1 = {q[2], q[3]}, q2 = {q[4], q[5]}, q3 = {q[6], q[7]};
+      const float sj = (float)sh[j];
+#pragma unroll
+      for (int m = 0; m < GM; m++) {
+        if (m < M) {
+          const h8_t x = lds_h8(xs + m * kXRowBytes + 64 * j + 16 * c);
+          const h2_t x0 = {x[0], x[1]}, x1 = {x[2], x[3]}, x2 = {x[4], x[5]}, x3 = {x[6], x[7]};
+          float d = __builtin_amdgcn_fdot2(q0, x0, 0.f, false);
+          d = __builtin_amdgcn_fdot2(q1, x1, d, false);
+          d = __builtin_amdgcn_fdot2(q2, x2, d, false);
+          d = __builtin_amdgcn_fdot2(q3, x3, d, false);
+          acc[m] = __builtin_fmaf(sj, d, acc[m]);
+        }
+      }
+    }
+  }
+}
 
+// --------------------------------------------------------------------------
+// stream kernel: panels of at most 16 rows (GEMV, or MFMA with one m block)
+// --------------------------------------------------------------------------
+// The flat sequence of (job, row block, k tile) tiles is cut into `nwaves`
+// equal contiguous ranges, one per wave, so every wave streams the same number
+// of tiles.  Within one job a wave's tiles are contiguous in memory (tile
+// index rb * NKT + kt), so the weight pointer simply advances.  A wave
+// accumulates one row block at a time; a row block whose tiles all lie in one
+// range is written to Y directly.  A row block cut by range ends gets one
+// partial sum per contributing wave, stored into that wave's slot; the last
+// contributor to arrive (per-row-block counter) adds the partials in wave
+// order -- k order -- writes Y and resets the counter to zero.  Nothing waits
+// on another wave.  The slots and counters are accessed with system-scope
+// atomics, which bypass the per-XCD L2 caches (not coherent with each other).
 template <bool kMfma, int kCap>
 struct Stream {
   static constexpr int kRows = kMfma ? 16 : kCap;                 // X rows staged in LDS
-  static constexpr int kPieces = (kRows * 16 + 63) / 64;          // 16-byte X pieces per lane
-  static constexpr int kDepth = kMfma ? 4 : (kCap <= 2 ? 6 : 4);  // tiles in flight per wave
+  static constexpr int kLoadRows = kCap;                          // X rows loaded per tile
+  static constexpr int kPieces = (kLoadRows * 16 + 63) / 64;      // 16-byte X pieces per lane
+  static constexpr int kNF = kCap < 4 ? kCap : 4;                 // MFMA accumulator rows kept
+  // tiles in flight per wave (fewer where the panel's registers need room)
+  static constexpr int kDepth = kCap == 16 ? 3 : (!kMfma && kCap == 8) ? 2 : 4;
 
   struct Regs {
     WRegs w;
     u4_t x[kPieces];
   };
 
-  static __device__ __forceinline__ void advance(Cursor& c, const QG_CONST JobDesc* D, int njobs) {
-    if (++c.kt == c.jr.nkt) {
-      c.kt = 0;
-      if (++c.rb == c.jr.nrb) {
-        c.rb = 0;
-        if (++c.j < njobs) c.jr = fetch_job(D, c.j);
-      }
-    }
-  }
-
-  static __device__ __forceinline__ void load(Regs& t, const Cursor& c, int lane) {
-    const JobRegs& d = c.jr;
-    const uint8_t* tile = d.packed + ((int64_t)c.rb * d.nkt + c.kt) * tile_bytes(d.bits);
-    load_w(t.w, tile, d.bits, lane);
-#pragma unroll
-    for (int p = 0; p < kPieces; p++) {
-      const int piece = lane + 64 * p;
-      const int row = piece >> 4, col = piece & 15;
-      t.x[p] = load_x_piece(d.X, d.ldx, row < kRows ? row : kRows, c.kt * kTileK + 8 * col, d.M, d.K);
-    }
-  }
-
-  static __device__ __forceinline__ void stage(const Regs& t, uint8_t* xs, int lane) {
-#pragma unroll
-    for (int p = 0; p < kPieces; p++) {
-      const int piece = lane + 64 * p;
-      const int row = piece >> 4, col = piece & 15;
-      if (row < kRows) *(u4_t*)(xs + row * kXRowBytes + 16 * col) = t.x[p];
-    }
-  }
-
   struct Acc {
-    f4_t mf[1];
+    f4_t mf;
     float gv[kCap];
   };
 
   static __device__ __forceinline__ void zero(Acc& a) {
-    a.mf[0] = f4_t{0.f, 0.f, 0.f, 0.f};
+    a.mf = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < kCap; m++) a.gv[m] = 0.f;
   }
@@ -373,13 +383,24 @@ struct Stream {
     return w < G - 1 ? w : G - 1;
   }
 
-  // Write the finished (or partial) sums of row block (c.j, c.rb).
-  static __device__ void flush(Acc& acc, const Cursor& c, const QG_CONST JobDesc* D, const SweepArgs& args,
-                               int64_t gw, int64_t a, int64_t b, int lane) {
-    const int M = c.jr.M, N = D[c.j].N;
-    const int64_t ldy = D[c.j].ldy, tile_begin = D[c.j].tile_begin;
-    const int rb_begin = D[c.j].rb_begin;
-    QG_GLOBAL float* Y = (QG_GLOBAL float*)D[c.j].Y;
+  // Everything a wave needs to place one row block's sums.
+  struct Ctx {
+    const QG_CONST JobDesc* D;
+    int* counters;
+    float* slots;
+    int64_t T, G;          // flat tiles, waves
+    int slot_rows;
+    int64_t gw, a, b;
+    int lane;
+  };
+
+  // Write the finished (or partial) sums of row block rb of job j.
+  static __device__ __forceinline__ void flush(Acc acc, const Ctx& cx, int j, int rb) {
+    const QG_CONST JobDesc* D = cx.D;
+    const int lane = cx.lane;
+    const int M = D[j].M, N = D[j].N, nkt = D[j].nkt;
+    const int64_t ldy = D[j].ldy;
+    QG_GLOBAL float* Y = (QG_GLOBAL float*)D[j].Y;
     if constexpr (!kMfma) {
 #pragma unroll
       for (int m = 0; m < kCap; m++) {
@@ -389,17 +410,17 @@ struct Stream {
         acc.gv[m] = v;
       }
     }
-    const int64_t first = tile_begin + (int64_t)c.rb * c.jr.nkt;
-    const int64_t last = first + c.jr.nkt - 1;
+    const int64_t first = D[j].tile_begin + (int64_t)rb * nkt;
+    const int64_t last = first + nkt - 1;
     const int nn = lane & 15;
-    const int n = c.rb * kTileRows + nn;
-    if (first >= a && last < b) {
+    const int n = rb * kTileRows + nn;
+    if (first >= cx.a && last < cx.b) {
       if (n < N) {
         if constexpr (kMfma) {
 #pragma unroll
-          for (int i = 0; i < 4; i++) {
+          for (int i = 0; i < kNF; i++) {
             const int m = 4 * (lane >> 4) + i;
-            if (m < M) Y[(int64_t)m * ldy + n] = acc.mf[0][i];
+            if (m < M) Y[(int64_t)m * ldy + n] = acc.mf[i];
           }
         } else if (lane < 16) {
 #pragma unroll
@@ -409,15 +430,15 @@ struct Stream {
       }
       return;
     }
-    const int64_t T = args.total, G = args.nwaves;
-    const int slot_floats = args.slot_rows * kTileRows;
-    const int kind = a >= first ? 0 : 1;
-    float* mine = args.slots + (gw * 2 + kind) * slot_floats;
+    const int64_t T = cx.T, G = cx.G;
+    const int slot_floats = cx.slot_rows * kTileRows;
+    const int kind = cx.a >= first ? 0 : 1;
+    float* mine = cx.slots + (cx.gw * 2 + kind) * slot_floats;
     if constexpr (kMfma) {
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
+      for (int i = 0; i < kNF; i++) {
         const int m = 4 * (lane >> 4) + i;
-        if (m < M) __hip_atomic_store(mine + m * kTileRows + nn, acc.mf[0][i], __ATOMIC_RELAXED,
+        if (m < M) __hip_atomic_store(mine + m * kTileRows + nn, acc.mf[i], __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_SYSTEM);
       }
     } else if (lane < 16) {
@@ -432,7 +453,7 @@ struct Stream {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const int64_t wf = wave_of(first, T, G), wl = wave_of(last, T, G);
     const int contributors = (int)(wl - wf + 1);
-    int* ctr = args.counters + rb_begin + c.rb;
+    int* ctr = cx.counters + D[j].rb_begin + rb;
     int old = 0;
     if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     old = __builtin_amdgcn_readfirstlane(old);
@@ -444,77 +465,131 @@ struct Stream {
       for (int64_t w = wf; w <= wl; w++) {
         const int64_t aw = w * T / G;
         const int kw = aw >= first ? 0 : 1;
-        v += __hip_atomic_load(args.slots + (w * 2 + kw) * slot_floats + e, __ATOMIC_RELAXED,
+        v += __hip_atomic_load(cx.slots + (w * 2 + kw) * slot_floats + e, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_SYSTEM);
       }
-      const int ncol = c.rb * kTileRows + col;
+      const int ncol = rb * kTileRows + col;
       if (ncol < N) Y[(int64_t)m * ldy + ncol] = v;
     }
     if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
 
-  static __device__ void run(const SweepArgs& args, uint8_t* xs) {
-    const QG_CONST JobDesc* D = job_table(args);
-    const int njobs = args.njobs;
-    const int lane = threadIdx.x & 63;
-    // wave-uniform by construction; readfirstlane lets the compiler know it
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int64_t gw = (int64_t)blockIdx.x * kStreamWavesPerBlock + wave;
-    const int64_t T = args.total, G = args.nwaves;
-    const int64_t a = gw * T / G, b = (gw + 1) * T / G;
-    if (gw >= G || a >= b) return;
-    // locate tile a
-    Cursor cc;
-    cc.j = 0;
-    while (a >= D[cc.j].tile_end) cc.j++;
-    cc.jr = fetch_job(D, cc.j);
-    {
-      const int64_t off = a - D[cc.j].tile_begin;
-      cc.rb = (int)(off / cc.jr.nkt);
-      cc.kt = (int)(off - (int64_t)cc.rb * cc.jr.nkt);
+  // xp points at X[0][kbase]; pieces with k = kbase + 8*col >= K or rows >= M
+  // read X[0][0] and are never used.
+  template <int BITS>
+  static __device__ __forceinline__ void load(Regs& t, const uint8_t* wp, const uint16_t* X, int kbase,
+                                              int lane, int M, int K, int64_t ldx) {
+    t.w.wc = __builtin_nontemporal_load(gload_ptr<u4_t>(wp + 16 * lane));
+    t.w.ws = __builtin_nontemporal_load(gload_ptr<u2_t>(wp + kScaleOff + 8 * (lane & 15)));
+    if constexpr (BITS == 5) t.w.wh = __builtin_nontemporal_load(gload_ptr<uint32_t>(wp + kHiOff + 4 * lane));
+    else t.w.wh = 0u;
+#pragma unroll
+    for (int p = 0; p < kPieces; p++) {
+      const int piece = lane + 64 * p;
+      const int row = piece >> 4, col = piece & 15;
+      const int k = kbase + 8 * col;
+      const bool ok = row < M && row < kLoadRows && k < K;
+      t.x[p] = *gload_ptr<u4_t>(X + (ok ? (int64_t)row * ldx + k : 0));
     }
-    // prefetch cursor: runs kDepth tiles ahead and stops at the range's last
-    // tile (later loads re-read it), so every step issues the same loads
-    Cursor pc = cc;
-    int64_t pf = a;
+  }
+
+  static __device__ __forceinline__ void stage(const Regs& t, uint8_t* xs, int lane) {
+#pragma unroll
+    for (int p = 0; p < kPieces; p++) {
+      const int piece = lane + 64 * p;
+      const int row = piece >> 4, col = piece & 15;
+      if (row < kLoadRows) *(u4_t*)(xs + row * kXRowBytes + 16 * col) = t.x[p];
+    }
+  }
+
+  // Tiles [s0, s1) of job j (local indices rb * NKT + kt), BITS fixed.
+  template <int BITS>
+  static __device__ __forceinline__ void segment(const Ctx& cx, int j, int64_t s0, int64_t s1, uint8_t* xs) {
+    const QG_CONST JobDesc* D = cx.D;
+    const int lane = cx.lane;
+    constexpr int TB = BITS == 4 ? kTile4 : kTile5;
+    const int nkt = D[j].nkt, ngroups = D[j].ngroups, M = D[j].M, K = D[j].K;
+    const int64_t ldx = D[j].ldx;
+    const uint8_t* packed = D[j].packed;
+    const uint16_t* X = D[j].X;
+    const bool ragged_k = (ngroups & 3) != 0;
+    // consume cursor
+    int rb = (int)(s0 / nkt);
+    int kt = (int)(s0 - (int64_t)rb * nkt);
+    // prefetch cursor: stops at the segment's last tile (later loads re-read it)
+    int64_t ps = s0;
+    int pkt = kt;
+    const uint8_t* pw = packed + s0 * TB;
+    auto pf_advance = [&]() {
+      if (ps < s1 - 1) {
+        ps++;
+        pw += TB;
+        if (++pkt == nkt) pkt = 0;
+      }
+    };
     Regs buf[kDepth];
 #pragma unroll
     for (int p = 0; p < kDepth; p++) {
-      load(buf[p], pc, lane);
-      if (pf < b - 1) {
-        advance(pc, D, njobs);
-        pf++;
-      }
+      load<BITS>(buf[p], pw, X, pkt * kTileK, lane, M, K, ldx);
+      pf_advance();
     }
     Acc acc;
     zero(acc);
-    const int64_t n = b - a;
+    const int64_t n = s1 - s0;
     for (int64_t f = 0; f < n; f += kDepth) {
 #pragma unroll
       for (int p = 0; p < kDepth; p++) {
         if (f + p < n) {
-          const int gleft = cc.jr.ngroups - 4 * cc.kt;
           stage(buf[p], xs, lane);
           __atomic_signal_fence(__ATOMIC_SEQ_CST);  // LDS writes stay before the reads
-          if (cc.jr.bits == 4) {
-            if constexpr (kMfma) mfma_tile<4, 1>(acc.mf, buf[p].w, xs, lane, gleft);
-            else gemv_tile<4, kCap>(acc.gv, buf[p].w, xs, lane, gleft, cc.jr.M);
+          const int gleft = ngroups - 4 * kt;
+          if (!ragged_k || gleft >= 4) {
+            if constexpr (kMfma) mfma1_tile<BITS, kNF, false>(acc.mf, buf[p].w, xs, lane, 4);
+            else gemv1_tile<BITS, kCap, false>(acc.gv, buf[p].w, xs, lane, 4, M);
           } else {
-            if constexpr (kMfma) mfma_tile<5, 1>(acc.mf, buf[p].w, xs, lane, gleft);
-            else gemv_tile<5, kCap>(acc.gv, buf[p].w, xs, lane, gleft, cc.jr.M);
+            if constexpr (kMfma) mfma1_tile<BITS, kNF, true>(acc.mf, buf[p].w, xs, lane, gleft);
+            else gemv1_tile<BITS, kCap, true>(acc.gv, buf[p].w, xs, lane, gleft, M);
           }
-          if (cc.kt == cc.jr.nkt - 1 || f + p == n - 1) {
-            flush(acc, cc, D, args, gw, a, b, lane);
+          if (kt == nkt - 1 || f + p == n - 1) {
+            flush(acc, cx, j, rb);
             zero(acc);
           }
-          advance(cc, D, njobs);
+          if (++kt == nkt) {
+            kt = 0;
+            rb++;
+          }
         }
-        load(buf[p], pc, lane);
-        if (pf < b - 1) {
-          advance(pc, D, njobs);
-          pf++;
-        }
+        load<BITS>(buf[p], pw, X, pkt * kTileK, lane, M, K, ldx);
+        pf_advance();
       }
+    }
+  }
+
+  static __device__ void run(const SweepArgs& args, uint8_t* xs) {
+    Ctx cx;
+    cx.D = job_table(args);
+    cx.counters = args.counters;
+    cx.slots = args.slots;
+    cx.T = args.total;
+    cx.G = args.nwaves;
+    cx.slot_rows = args.slot_rows;
+    cx.lane = threadIdx.x & 63;
+    // wave-uniform by construction; readfirstlane lets the compiler know it
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    cx.gw = (int64_t)blockIdx.x * kStreamWavesPerBlock + wave;
+    const int64_t T = args.total, G = args.nwaves;
+    cx.a = cx.gw * T / G;
+    cx.b = (cx.gw + 1) * T / G;
+    if (cx.gw >= G || cx.a >= cx.b) return;
+    int j = 0;
+    while (cx.a >= cx.D[j].tile_end) j++;
+    // one segment per job the range touches
+    for (int64_t f = cx.a; f < cx.b; j++) {
+      const int64_t tb = cx.D[j].tile_begin;
+      const int64_t e = cx.D[j].tile_end < cx.b ? cx.D[j].tile_end : cx.b;
+      if (cx.D[j].bits == 4) segment<4>(cx, j, f - tb, e - tb, xs);
+      else segment<5>(cx, j, f - tb, e - tb, xs);
+      f = e;
     }
   }
 };
@@ -666,7 +741,7 @@ hipError_t launch_fill_zero(void* p, int64_t words, hipStream_t stream) {
 
 typedef void (*sweep_fn)(SweepArgs);
 
-// kind: 0 = stream GEMV (cls = rows 1, 2, 4, 8), 1 = stream MFMA (cls 16),
+// kind: 0 = stream GEMV (cls = rows 1, 2, 4, 8), 1 = stream MFMA (cls 1, 2, 4, 16),
 //       2 = group MFMA (cls = padded rows 32, 48, 64)
 static sweep_fn pick(int kind, int cls) {
   if (kind == 0) {
@@ -677,7 +752,12 @@ static sweep_fn pick(int kind, int cls) {
       case 8: return stream_kernel<false, 8>;
     }
   } else if (kind == 1) {
-    if (cls == 16) return stream_kernel<true, 16>;
+    switch (cls) {
+      case 1: return stream_kernel<true, 1>;
+      case 2: return stream_kernel<true, 2>;
+      case 4: return stream_kernel<true, 4>;
+      case 16: return stream_kernel<true, 16>;
+    }
   } else {
     switch (cls) {
       case 32: return group_kernel<32>;
