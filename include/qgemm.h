@@ -12,8 +12,10 @@
  * "Weights" item; group size 32 here).
  *
  * This header is the whole boundary: plain C, device pointers and sizes.
- * The library allocates nothing that outlives a call and keeps no mutable
- * global state; every buffer belongs to the caller.
+ * The library allocates nothing that outlives a call; every buffer belongs to
+ * the caller.  Its only global state is two small thread-safe caches of values
+ * that depend on shapes and the device alone (kernel occupancy, and the wave
+ * count chosen for a set of matrix shapes).
  *
  * ---------------------------------------------------------------------------
  * Quantizer (qgemm_pack).  W is logical [N][K] (N outputs, K inputs,

@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <vector>
 
@@ -101,11 +102,77 @@ int kind_of(int path, int M) {
 
 int class_of(int kind, int M) {
   if (kind == kStreamGemv) return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
-  if (kind == kStreamMfma) return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 16;
+  if (kind == kStreamMfma) return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
   return (M + 15) / 16 * 16;
 }
 
 int cu_count();
+
+// Wave range boundaries (w * T / W) that fall inside a row block: each one
+// costs a partial-sum exchange between two waves.
+int64_t cut_row_blocks(const std::vector<JobDesc>& descs, int64_t T, int64_t W) {
+  int64_t cuts = 0;
+  size_t j = 0;
+  for (int64_t w = 1; w < W; w++) {
+    const int64_t f = w * T / W;
+    while (f >= descs[j].tile_end) j++;
+    if ((f - descs[j].tile_begin) % descs[j].nkt != 0) cuts++;
+  }
+  return cuts;
+}
+
+// Waves of a stream launch.  Every wave must get a non-empty tile range
+// (contributor counts rely on it), so W <= T.  Otherwise W is chosen in
+// [kStreamMinWaves, kStreamWaves] -- enough to fill the chip -- among a few
+// candidates, by the fewest cut row blocks, then the most waves.  Candidates
+// include the counts that give every wave a whole number of one job's row
+// blocks (T / (k * NKT)).  Depends on the shapes only, never on M.
+int64_t stream_waves_uncached(const std::vector<JobDesc>& descs, int64_t T) {
+  if (T <= qg::kStreamMinWaves) return T;
+  std::vector<int64_t> cand = {qg::kStreamMinWaves, 3072, qg::kStreamWaves};
+  for (const auto& d : descs)
+    for (int64_t k = 1; k <= 8; k++) {
+      const int64_t per = k * d.nkt;
+      if (T % per == 0) cand.push_back(T / per);
+    }
+  int64_t best = -1, best_cuts = 0;
+  for (int64_t W : cand) {
+    if (W < qg::kStreamMinWaves || W > qg::kStreamWaves || W > T) continue;
+    const int64_t cuts = cut_row_blocks(descs, T, W);
+    if (best < 0 || cuts < best_cuts || (cuts == best_cuts && W > best)) {
+      best = W;
+      best_cuts = cuts;
+    }
+  }
+  return best < 0 ? std::min<int64_t>(T, qg::kStreamWaves) : best;
+}
+
+// The choice above walks up to kStreamWaves boundaries per candidate, which
+// is too slow to repeat on every sweep call; it is a pure function of the
+// launch's row-block shapes, so it is memoized per shape signature (a bounded
+// cache; shapes only, never pointers or M).
+int64_t stream_waves(const std::vector<JobDesc>& descs, int64_t T) {
+  if (T <= qg::kStreamMinWaves) return T;
+  std::vector<int64_t> key;
+  key.reserve(2 * descs.size() + 1);
+  key.push_back(T);
+  for (const auto& d : descs) {
+    key.push_back(d.nkt);
+    key.push_back(d.nrb);
+  }
+  static std::mutex mu;
+  static std::map<std::vector<int64_t>, int64_t> cache;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  const int64_t W = stream_waves_uncached(descs, T);
+  std::lock_guard<std::mutex> g(mu);
+  if (cache.size() >= 256) cache.clear();
+  cache.emplace(std::move(key), W);
+  return W;
+}
 
 Plan make_plan(const qgemm_job* jobs, int njobs, int path) {
   Plan P;
@@ -157,8 +224,7 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path) {
       off = round_up(off + l.descs.size() * sizeof(JobDesc), 256);
     }
     if (l.kind != kGroupMfma) {
-      // every wave gets a non-empty tile range (contributor counts rely on it)
-      l.nwaves = (int)std::min<int64_t>(qg::kStreamWaves, l.total);
+      l.nwaves = (int)stream_waves(l.descs, l.total);
       l.counters_off = off;
       off = round_up(off + (size_t)l.rbs * sizeof(int), 256);
       l.slots_off = off;
@@ -247,9 +313,11 @@ qgemm_status qgemm_validate(const qgemm_job* jobs, int njobs, int path, void* wo
 
 qgemm_status qgemm_sweep_path(const qgemm_job* jobs, int njobs, int path, void* workspace,
                               size_t ws_bytes, void* stream) {
-  qgemm_status st = qgemm_validate(jobs, njobs, path, workspace, ws_bytes);
+  qgemm_status st = validate(jobs, njobs, path);
   if (st != QGEMM_OK) return st;
+  if (!workspace || !aligned(workspace, 256)) return QGEMM_ERR_INVALID_ARG;
   Plan P = make_plan(jobs, njobs, path);
+  if (ws_bytes < P.total) return QGEMM_ERR_INVALID_ARG;
   uint8_t* ws = (uint8_t*)workspace;
   hipStream_t s = (hipStream_t)stream;
   const int cus = cu_count();

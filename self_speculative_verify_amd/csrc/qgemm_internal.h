@@ -17,10 +17,12 @@ constexpr int kTile5 = 1408;
 constexpr int kMaxInline = 12;       // jobs passed by value in the kernel arguments
 constexpr int kXRowBytes = 272;      // LDS row stride of a staged X chunk (256 + 16 pad)
 
-// stream kernel (panels of at most 16 rows): waves per workgroup, and waves in
-// the grid -- a constant (16 per CU of a 256-CU MI355X), so that the K split of
-// every row block, and with it every output bit, is the same on any device
+// stream kernel (panels of at most 16 rows): waves per workgroup, and the
+// range of waves in the grid (8 to 16 per CU of a 256-CU MI355X).  The count
+// is chosen from the shapes alone -- never from the device or M -- so the K
+// split of every row block, and with it every output bit, is reproducible.
 constexpr int kStreamWavesPerBlock = 4;
+constexpr int kStreamMinWaves = 2048;
 constexpr int kStreamWaves = 4096;
 // group kernel (17..64 rows): waves per workgroup, one 16-row block each
 constexpr int kGroupWaves = 8;

@@ -298,15 +298,23 @@ __device__ __forceinline__ void mfma1_tile(f4_t& acc, const WRegs& w, const uint
   const h2_t s01 = scale_pair(w.ws.x), s23 = scale_pair(w.ws.y);
   const _Float16 sh[4] = {s01.x, s01.y, s23.x, s23.y};
   const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+  // all four groups' MFMAs are issued before any of their results is read,
+  // so the MFMA latency overlaps with independent work instead of stalling
+  f4_t p[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     if (!kRagged || j < gleft) {
       const h8_t q = unpack_chunk<BITS>(w.wc[j], w.wh, j);
       const h8_t a = lds_h8(xs + r * kXRowBytes + 64 * j + 16 * c);
-      const f4_t p = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, q, zero, 0, 0, 0);
+      p[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, q, zero, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    if (!kRagged || j < gleft) {
       const float sj = (float)sh[j];
 #pragma unroll
-      for (int i = 0; i < NF; i++) acc[i] = __builtin_fmaf(sj, p[i], acc[i]);
+      for (int i = 0; i < NF; i++) acc[i] = __builtin_fmaf(sj, p[j][i], acc[i]);
     }
   }
 }
@@ -359,8 +367,9 @@ struct Stream {
   static constexpr int kLoadRows = kCap;                          // X rows loaded per tile
   static constexpr int kPieces = (kLoadRows * 16 + 63) / 64;      // 16-byte X pieces per lane
   static constexpr int kNF = kCap < 4 ? kCap : 4;                 // MFMA accumulator rows kept
-  // tiles in flight per wave (fewer where the panel's registers need room)
-  static constexpr int kDepth = kCap == 16 ? 3 : (!kMfma && kCap == 8) ? 2 : 4;
+  // tiles in flight per wave (fewer where the panel's registers need room);
+  // 2048..4096 waves x depth x 1.15 KB keeps >= ~16 MB of reads in flight
+  static constexpr int kDepth = kCap <= 2 ? 8 : kCap == 4 ? 6 : kCap == 8 ? (kMfma ? 4 : 2) : 3;
 
   struct Regs {
     WRegs w;
@@ -392,10 +401,16 @@ struct Stream {
     int slot_rows;
     int64_t gw, a, b;
     int lane;
+    // split row blocks whose partial this wave stored (kind 0 / kind 1)
+    int pend_j0, pend_rb0, pend_j1, pend_rb1;
   };
 
-  // Write the finished (or partial) sums of row block rb of job j.
-  static __device__ __forceinline__ void flush(Acc acc, const Ctx& cx, int j, int rb) {
+  // Write the finished sums of row block rb of job j to Y, or, for a row
+  // block cut by this wave's range, store this wave's partial into its slot
+  // (kind 0: the range's first row block, kind 1: its last) and note it; the
+  // arrival is counted once, at the end of the range (see arrive), so the
+  // stream never stalls on it.
+  static __device__ __forceinline__ void flush(Acc acc, Ctx& cx, int j, int rb) {
     const QG_CONST JobDesc* D = cx.D;
     const int lane = cx.lane;
     const int M = D[j].M, N = D[j].N, nkt = D[j].nkt;
@@ -430,7 +445,6 @@ struct Stream {
       }
       return;
     }
-    const int64_t T = cx.T, G = cx.G;
     const int slot_floats = cx.slot_rows * kTileRows;
     const int kind = cx.a >= first ? 0 : 1;
     float* mine = cx.slots + (cx.gw * 2 + kind) * slot_floats;
@@ -447,10 +461,28 @@ struct Stream {
         if (m < M)
           __hip_atomic_store(mine + m * kTileRows + nn, acc.gv[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
-    // the slot stores must be complete before this wave's arrival is counted
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (kind == 0) {
+      cx.pend_j0 = j;
+      cx.pend_rb0 = rb;
+    } else {
+      cx.pend_j1 = j;
+      cx.pend_rb1 = rb;
+    }
+  }
+
+  // Count this wave's arrival at split row block rb of job j (its partial is
+  // already stored and complete); the last of its contributors adds all
+  // partials in wave order -- k order -- writes Y and resets the counter.
+  static __device__ __forceinline__ void arrive(const Ctx& cx, int j, int rb) {
+    const QG_CONST JobDesc* D = cx.D;
+    const int lane = cx.lane;
+    const int M = D[j].M, N = D[j].N, nkt = D[j].nkt;
+    const int64_t ldy = D[j].ldy;
+    QG_GLOBAL float* Y = (QG_GLOBAL float*)D[j].Y;
+    const int64_t first = D[j].tile_begin + (int64_t)rb * nkt;
+    const int64_t last = first + nkt - 1;
+    const int64_t T = cx.T, G = cx.G;
+    const int slot_floats = cx.slot_rows * kTileRows;
     const int64_t wf = wave_of(first, T, G), wl = wave_of(last, T, G);
     const int contributors = (int)(wl - wf + 1);
     int* ctr = cx.counters + D[j].rb_begin + rb;
@@ -504,7 +536,7 @@ struct Stream {
 
   // Tiles [s0, s1) of job j (local indices rb * NKT + kt), BITS fixed.
   template <int BITS>
-  static __device__ __forceinline__ void segment(const Ctx& cx, int j, int64_t s0, int64_t s1, uint8_t* xs) {
+  static __device__ __forceinline__ void segment(Ctx& cx, int j, int64_t s0, int64_t s1, uint8_t* xs) {
     const QG_CONST JobDesc* D = cx.D;
     const int lane = cx.lane;
     constexpr int TB = BITS == 4 ? kTile4 : kTile5;
@@ -581,6 +613,8 @@ struct Stream {
     cx.a = cx.gw * T / G;
     cx.b = (cx.gw + 1) * T / G;
     if (cx.gw >= G || cx.a >= cx.b) return;
+    cx.pend_j0 = cx.pend_j1 = -1;
+    cx.pend_rb0 = cx.pend_rb1 = 0;
     int j = 0;
     while (cx.a >= cx.D[j].tile_end) j++;
     // one segment per job the range touches
@@ -591,11 +625,21 @@ struct Stream {
       else segment<5>(cx, j, f - tb, e - tb, xs);
       f = e;
     }
+    if (cx.pend_j0 >= 0 || cx.pend_j1 >= 0) {
+      // every slot store of this wave must be complete before any arrival
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (cx.pend_j0 >= 0) arrive(cx, cx.pend_j0, cx.pend_rb0);
+      if (cx.pend_j1 >= 0) arrive(cx, cx.pend_j1, cx.pend_rb1);
+    }
   }
 };
 
+// At least 4 waves per SIMD: 16 per CU keep every wave of the grid resident.
 template <bool kMfma, int kCap>
-__global__ void __launch_bounds__(64 * kStreamWavesPerBlock) stream_kernel(SweepArgs args) {
+__global__ void __launch_bounds__(64 * kStreamWavesPerBlock) __attribute__((amdgpu_waves_per_eu(4)))
+stream_kernel(SweepArgs args) {
   using S = Stream<kMfma, kCap>;
   __shared__ __attribute__((aligned(16))) uint8_t xs[kStreamWavesPerBlock][S::kRows * kXRowBytes];
   S::run(args, xs[threadIdx.x >> 6]);
@@ -741,7 +785,7 @@ hipError_t launch_fill_zero(void* p, int64_t words, hipStream_t stream) {
 
 typedef void (*sweep_fn)(SweepArgs);
 
-// kind: 0 = stream GEMV (cls = rows 1, 2, 4, 8), 1 = stream MFMA (cls 1, 2, 4, 16),
+// kind: 0 = stream GEMV (cls = rows 1, 2, 4, 8), 1 = stream MFMA (cls 1, 2, 4, 8, 16),
 //       2 = group MFMA (cls = padded rows 32, 48, 64)
 static sweep_fn pick(int kind, int cls) {
   if (kind == 0) {
@@ -756,6 +800,7 @@ static sweep_fn pick(int kind, int cls) {
       case 1: return stream_kernel<true, 1>;
       case 2: return stream_kernel<true, 2>;
       case 4: return stream_kernel<true, 4>;
+      case 8: return stream_kernel<true, 8>;
       case 16: return stream_kernel<true, 16>;
     }
   } else {
