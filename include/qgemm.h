@@ -25,14 +25,14 @@
  *     q    = 0 if s == 0, else clamp(RNE((double)W[n,k] / (double)s), +-Qmax)
  *     u    = q + 2^(bits-1)                 (stored offset-binary code)
  *
- * Packed layout "QG32 tiled v0".  Tiles of 16 rows x 128 k; tile (rb, kt) is
+ * Packed layout "QG32 tiled v1".  Tiles of 16 rows x 128 k; tile (rb, kt) is
  * at byte (rb * NKT + kt) * TB, NKT = ceil(K/128), TB = 1152 (4-bit) or 1408
  * (5-bit).  For element (n, k) let r = n mod 16, j = (k mod 128) / 32,
  * c = (k mod 32) / 8, e = k mod 8:
  *     low 4 bits of u  -> little-endian 32-bit word at byte 16*(r + 16c) + 4j,
  *                         bit 4*(e >> 1) + 16*(e & 1)
  *     bit 4 of u       -> 32-bit word at byte 1152 + 4*(r + 16c),
- *                         bit (4 + 16*(e & 1) + 4j + (e >> 1)) mod 32  (5-bit)
+ *                         bit (4 + 16*(e & 1) + 4*(e >> 1) + j) mod 32 (5-bit)
  *     s(n, 4kt + j)    -> IEEE binary16 at byte 1024 + 8r + 2j
  * Rows n >= N and groups beyond K/32 are padding (u = 2^(bits-1), s = +0).
  * Lane l = r + 16c of a 64-wide wave thus reads the 16 bytes at 16*l: chunk c
@@ -83,8 +83,8 @@ typedef enum {
 /* One matrix of a sweep.  Pointers are device pointers.
  *   packed : QG32 tiled buffer from qgemm_pack, 256-byte aligned, read-only
  *   bits   : 4 or 5, as packed
- *   N, K   : N >= 1; K >= 32 and K % 32 == 0
- *   X      : binary16 [M][ldx], 16-byte aligned, ldx % 8 == 0, ldx >= K
+ *   N, K   : 1 <= N <= 2^30; 32 <= K <= 2^24 and K % 32 == 0
+ *   X      : binary16 [M][ldx], 16-byte aligned, ldx % 8 == 0, K <= ldx <= 2^24
  *   Y      : fp32 [M][ldy], 16-byte aligned, ldy % 4 == 0, ldy >= N
  *   M      : 1 .. QGEMM_MAX_M
  * Y must not overlap X, any packed buffer or another job's Y. */

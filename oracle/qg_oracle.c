@@ -16,13 +16,13 @@
  *   Dequant:  w_hat = (double)q * (double)s       (exact in fp64)
  *   Sweep:    Y[m,n] = sum_{k ascending} (double)X[m,k] * w_hat[n,k]   (fp64)
  *
- * Tiled group-32 layout ("QG32", our own: the pages do not publish q4s/q5f):
+ * Tiled group-32 layout ("QG32 tiled v1", our own: the pages do not publish q4s/q5f):
  *   16 rows x 128 k per tile; tile (rb, kt) at byte (rb*NKT + kt)*TB with
  *   NKT = ceil(K/128), TB = 1152 (4-bit) or 1408 (5-bit).  For element (n, k):
  *   r = n mod 16, j = (k mod 128)/32, c = (k mod 32)/8, e = k mod 8.
  *     low 4 bits of u : LE word at byte 16*(r+16c) + 4j, bit 4*(e>>1) + 16*(e&1)
  *     bit 4 of u      : LE word at byte 1152 + 4*(r+16c),
- *                       bit (4 + 16*(e&1) + 4j + (e>>1)) mod 32     (5-bit only)
+ *                       bit (4 + 16*(e&1) + 4*(e>>1) + j) mod 32   (5-bit only)
  *     scale s(n, 4kt+j): binary16 at byte 1024 + 8r + 2j
  *   Rows n >= N and groups g >= K/32 are padding: u = 2^(bits-1), s = +0.
  *
@@ -113,7 +113,7 @@ static loc_t locate(int64_t n, int64_t k, int64_t NKT, int bits) {
   L.code_word = base + 16 * (r + 16 * c) + 4 * j;
   L.code_bit = 4 * (e >> 1) + 16 * (e & 1);
   L.hi_word = base + 1152 + 4 * (r + 16 * c);
-  L.hi_bit = (4 + 16 * (e & 1) + 4 * j + (e >> 1)) % 32;
+  L.hi_bit = (4 + 16 * (e & 1) + 4 * (e >> 1) + j) % 32;
   L.scale = base + 1024 + 8 * r + 2 * j;
   return L;
 }

@@ -26,7 +26,8 @@ namespace {
 
 using qg::JobDesc;
 
-constexpr int64_t kMaxDim = (int64_t)1 << 30;  // N, K limits (32-bit tile math)
+constexpr int64_t kMaxN = (int64_t)1 << 30;    // keeps row-block math in 32 bits
+constexpr int64_t kMaxK = (int64_t)1 << 24;    // keeps row-group and X byte offsets in 32 bits
 constexpr int kAutoGemvMaxM = 4;               // AUTO: GEMV for M <= 4, MFMA above
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -37,7 +38,7 @@ int64_t nkt_of(int64_t K) { return (K + qg::kTileK - 1) / qg::kTileK; }
 int64_t nrb_of(int64_t N) { return (N + qg::kTileRows - 1) / qg::kTileRows; }
 
 bool valid_shape(int bits, int64_t N, int64_t K) {
-  return (bits == 4 || bits == 5) && N >= 1 && N <= kMaxDim && K >= qg::kGroup && K <= kMaxDim &&
+  return (bits == 4 || bits == 5) && N >= 1 && N <= kMaxN && K >= qg::kGroup && K <= kMaxK &&
          K % qg::kGroup == 0;
 }
 
@@ -56,7 +57,7 @@ qgemm_status validate(const qgemm_job* jobs, int njobs, int path) {
     if (j.M < 1 || j.M > QGEMM_MAX_M) return QGEMM_ERR_INVALID_ARG;
     if (!j.packed || !j.X || !j.Y) return QGEMM_ERR_INVALID_ARG;
     if (!aligned(j.packed, 256) || !aligned(j.X, 16) || !aligned(j.Y, 16)) return QGEMM_ERR_INVALID_ARG;
-    if (j.ldx < j.K || j.ldx % 8 != 0) return QGEMM_ERR_INVALID_ARG;
+    if (j.ldx < j.K || j.ldx % 8 != 0 || j.ldx > kMaxK) return QGEMM_ERR_INVALID_ARG;
     if (j.ldy < j.N || j.ldy % 4 != 0) return QGEMM_ERR_INVALID_ARG;
     if (path == QGEMM_PATH_GEMV && j.M > QGEMM_GEMV_MAX_M) return QGEMM_ERR_INVALID_ARG;
     // Y must not overlap X or the packed weights of this job
@@ -83,15 +84,21 @@ struct Launch {
   int kind;
   int cls;
   std::vector<JobDesc> descs;
-  int64_t total = 0;          // stream: flat tiles; group: units
-  int64_t rbs = 0;            // stream: row blocks (arrival counters)
+  int64_t total = 0;          // stream: flat units; group: row-block groups
+  int64_t rgs = 0;            // stream: row groups (arrival counters)
   size_t table_off = 0, counters_off = 0, slots_off = 0;
   int nwaves = 0;
+  int bshift = 0;             // stream with a table: log2 of the units per bucket
+  std::vector<int32_t> index; // stream with a table: uend per job, first job per bucket
 };
+
+// Flat units and row-block groups are 32-bit in the kernels.
+constexpr int64_t kMaxSteps = ((int64_t)1 << 31) - 1;
 
 struct Plan {
   std::vector<Launch> launches;
   size_t total = 0;
+  bool ok = true;             // false: a launch exceeds the 32-bit unit range
 };
 
 int kind_of(int path, int M) {
@@ -108,57 +115,63 @@ int class_of(int kind, int M) {
 
 int cu_count();
 
-// Wave range boundaries (w * T / W) that fall inside a row block: each one
-// costs a partial-sum exchange between two waves.
-int64_t cut_row_blocks(const std::vector<JobDesc>& descs, int64_t T, int64_t W) {
+// Wave range boundaries that fall inside a row group (after its first step
+// and at or before its last): each one costs a partial-sum exchange.
+int64_t cut_row_groups(const std::vector<JobDesc>& descs, int64_t T, int64_t W) {
+  const int64_t q = T / W, rem = T % W;
   int64_t cuts = 0;
   size_t j = 0;
   for (int64_t w = 1; w < W; w++) {
-    const int64_t f = w * T / W;
-    while (f >= descs[j].tile_end) j++;
-    if ((f - descs[j].tile_begin) % descs[j].nkt != 0) cuts++;
+    const int64_t f = w * q + std::min(w, rem);  // start of wave w (as in the kernel)
+    while (f >= descs[j].uend) j++;
+    const int64_t wt = qg::unit_weight(descs[j].bits), span = (int64_t)descs[j].nkt * wt;
+    const int64_t r = (f - descs[j].ubeg) % span;
+    if (r > 0 && r <= span - wt) cuts++;
   }
   return cuts;
 }
 
-// Waves of a stream launch.  Every wave must get a non-empty tile range
-// (contributor counts rely on it), so W <= T.  Otherwise W is chosen in
-// [kStreamMinWaves, kStreamWaves] -- enough to fill the chip -- among a few
-// candidates, by the fewest cut row blocks, then the most waves.  Candidates
-// include the counts that give every wave a whole number of one job's row
-// blocks (T / (k * NKT)).  Depends on the shapes only, never on M.
+// Waves of a stream launch.  Every wave must hold at least one step
+// (contributor counts rely on it), which kMaxUnitWeight units per wave
+// guarantee, so W <= T / kMaxUnitWeight.  Otherwise W is kStreamWaves
+// (enough to fill the chip), unless a count in [kStreamMinWaves,
+// kStreamWaves] that gives every wave a whole number of one job's row groups
+// cuts fewer row groups; ties go to the most waves.  Depends on the shapes
+// only, never on M.
 int64_t stream_waves_uncached(const std::vector<JobDesc>& descs, int64_t T) {
-  if (T <= qg::kStreamMinWaves) return T;
-  std::vector<int64_t> cand = {qg::kStreamMinWaves, 3072, qg::kStreamWaves};
+  const int64_t wmax = std::max<int64_t>(1, T / qg::kMaxUnitWeight);
+  if (wmax <= qg::kStreamMinWaves) return wmax;
+  std::vector<int64_t> cand = {std::min<int64_t>(qg::kStreamWaves, wmax)};
   for (const auto& d : descs)
     for (int64_t k = 1; k <= 8; k++) {
-      const int64_t per = k * d.nkt;
+      const int64_t per = k * d.nkt * qg::unit_weight(d.bits);
       if (T % per == 0) cand.push_back(T / per);
     }
   int64_t best = -1, best_cuts = 0;
   for (int64_t W : cand) {
-    if (W < qg::kStreamMinWaves || W > qg::kStreamWaves || W > T) continue;
-    const int64_t cuts = cut_row_blocks(descs, T, W);
+    if (W < qg::kStreamMinWaves || W > qg::kStreamWaves || W > wmax) continue;
+    const int64_t cuts = cut_row_groups(descs, T, W);
     if (best < 0 || cuts < best_cuts || (cuts == best_cuts && W > best)) {
       best = W;
       best_cuts = cuts;
     }
   }
-  return best < 0 ? std::min<int64_t>(T, qg::kStreamWaves) : best;
+  return best < 0 ? std::min<int64_t>(wmax, qg::kStreamWaves) : best;
 }
 
 // The choice above walks up to kStreamWaves boundaries per candidate, which
 // is too slow to repeat on every sweep call; it is a pure function of the
-// launch's row-block shapes, so it is memoized per shape signature (a bounded
+// launch's row-group shapes, so it is memoized per shape signature (a bounded
 // cache; shapes only, never pointers or M).
 int64_t stream_waves(const std::vector<JobDesc>& descs, int64_t T) {
-  if (T <= qg::kStreamMinWaves) return T;
+  if (T / qg::kMaxUnitWeight <= qg::kStreamMinWaves) return std::max<int64_t>(1, T / qg::kMaxUnitWeight);
   std::vector<int64_t> key;
   key.reserve(2 * descs.size() + 1);
   key.push_back(T);
   for (const auto& d : descs) {
     key.push_back(d.nkt);
-    key.push_back(d.nrb);
+    key.push_back(d.nrg);
+    key.push_back(d.bits);
   }
   static std::mutex mu;
   static std::map<std::vector<int64_t>, int64_t> cache;
@@ -204,32 +217,52 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path) {
     d.ngroups = (int32_t)(j.K / qg::kGroup);
     d.nrb = (int32_t)nrb_of(j.N);
     if (kind == kGroupMfma) {
-      const int64_t units = (d.nrb + qg::kGroupWaves - 1) / qg::kGroupWaves;
-      d.unit_begin = (int32_t)dst->total;
-      dst->total += units;
-      d.unit_end = (int32_t)dst->total;
+      const int64_t groups = (d.nrb + qg::kGroupWaves - 1) / qg::kGroupWaves;
+      d.grp_begin = (int32_t)dst->total;
+      dst->total += groups;
+      d.grp_end = (int32_t)std::min(dst->total, kMaxSteps);
     } else {
-      d.tile_begin = dst->total;
-      dst->total += (int64_t)d.nrb * d.nkt;
-      d.tile_end = dst->total;
-      d.rb_begin = (int32_t)dst->rbs;
-      dst->rbs += d.nrb;
+      const int R = qg::stream_rows(kind, cls);
+      d.nrg = (d.nrb + R - 1) / R;
+      d.ubeg = (int32_t)std::min(dst->total, kMaxSteps);
+      dst->total += (int64_t)d.nrg * d.nkt * qg::unit_weight(d.bits);
+      d.uend = (int32_t)std::min(dst->total, kMaxSteps);
+      d.rg_begin = (int32_t)dst->rgs;
+      dst->rgs += d.nrg;
     }
     dst->descs.push_back(d);
   }
   size_t off = 0;
   for (auto& l : P.launches) {
+    if (l.total > kMaxSteps) {
+      P.ok = false;
+      return P;
+    }
     if ((int)l.descs.size() > qg::kMaxInline) {
+      if (l.kind != kGroupMfma) {
+        // uend of every job, then for bucket b (units [b << bshift, ...))
+        // the job holding its first unit
+        while ((l.total >> l.bshift) > 1024) l.bshift++;
+        const int64_t nb = (l.total >> l.bshift) + 1;
+        l.index.reserve(l.descs.size() + nb);
+        for (const auto& d : l.descs) l.index.push_back(d.uend);
+        size_t j = 0;
+        for (int64_t b = 0; b < nb; b++) {
+          const int64_t f = std::min(b << l.bshift, l.total - 1);
+          while (f >= l.descs[j].uend) j++;
+          l.index.push_back((int32_t)j);
+        }
+      }
       l.table_off = off;
-      off = round_up(off + l.descs.size() * sizeof(JobDesc), 256);
+      off = round_up(off + l.descs.size() * sizeof(JobDesc) + l.index.size() * sizeof(int32_t), 256);
     }
     if (l.kind != kGroupMfma) {
       l.nwaves = (int)stream_waves(l.descs, l.total);
       l.counters_off = off;
-      off = round_up(off + (size_t)l.rbs * sizeof(int), 256);
+      off = round_up(off + (size_t)l.rgs * sizeof(int), 256);
       l.slots_off = off;
-      const int rows = l.cls;
-      off = round_up(off + (size_t)2 * l.nwaves * rows * qg::kTileRows * sizeof(float), 256);
+      const size_t slot_floats = (size_t)l.cls * qg::stream_rows(l.kind, l.cls) * qg::kTileRows;
+      off = round_up(off + (size_t)2 * l.nwaves * slot_floats * sizeof(float), 256);
     }
   }
   P.total = off ? off : 256;
@@ -292,7 +325,8 @@ qgemm_status qgemm_pack(const float* W, int64_t ldw, int64_t N, int64_t K, int b
 
 size_t qgemm_workspace_bytes(const qgemm_job* jobs, int njobs, int path) {
   if (validate(jobs, njobs, path) != QGEMM_OK) return 0;
-  return make_plan(jobs, njobs, path).total;
+  const Plan P = make_plan(jobs, njobs, path);
+  return P.ok ? P.total : 0;
 }
 
 qgemm_status qgemm_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
@@ -307,7 +341,9 @@ qgemm_status qgemm_validate(const qgemm_job* jobs, int njobs, int path, void* wo
   qgemm_status st = validate(jobs, njobs, path);
   if (st != QGEMM_OK) return st;
   if (!workspace || !aligned(workspace, 256)) return QGEMM_ERR_INVALID_ARG;
-  if (ws_bytes < make_plan(jobs, njobs, path).total) return QGEMM_ERR_INVALID_ARG;
+  const Plan P = make_plan(jobs, njobs, path);
+  if (!P.ok) return QGEMM_ERR_UNSUPPORTED;
+  if (ws_bytes < P.total) return QGEMM_ERR_INVALID_ARG;
   return QGEMM_OK;
 }
 
@@ -317,6 +353,7 @@ qgemm_status qgemm_sweep_path(const qgemm_job* jobs, int njobs, int path, void* 
   if (st != QGEMM_OK) return st;
   if (!workspace || !aligned(workspace, 256)) return QGEMM_ERR_INVALID_ARG;
   Plan P = make_plan(jobs, njobs, path);
+  if (!P.ok) return QGEMM_ERR_UNSUPPORTED;
   if (ws_bytes < P.total) return QGEMM_ERR_INVALID_ARG;
   uint8_t* ws = (uint8_t*)workspace;
   hipStream_t s = (hipStream_t)stream;
@@ -325,16 +362,23 @@ qgemm_status qgemm_sweep_path(const qgemm_job* jobs, int njobs, int path, void* 
     qg::SweepArgs args;
     std::memset(&args, 0, sizeof(args));
     args.njobs = (int32_t)l.descs.size();
-    args.total = l.total;
+    args.total = (int32_t)l.total;
     if ((int)l.descs.size() > qg::kMaxInline) {
-      JobDesc* table = (JobDesc*)(ws + l.table_off);
-      if (hipMemcpyAsync(table, l.descs.data(), l.descs.size() * sizeof(JobDesc), hipMemcpyHostToDevice,
-                         s) != hipSuccess)
+      // one copy: the job table, then the stream kernel's job index
+      uint8_t* table = ws + l.table_off;
+      const size_t tb = l.descs.size() * sizeof(JobDesc);
+      std::vector<uint8_t> host(tb + l.index.size() * sizeof(int32_t));
+      std::memcpy(host.data(), l.descs.data(), tb);
+      if (!l.index.empty()) std::memcpy(host.data() + tb, l.index.data(), l.index.size() * sizeof(int32_t));
+      if (hipMemcpyAsync(table, host.data(), host.size(), hipMemcpyHostToDevice, s) != hipSuccess)
         return QGEMM_ERR_HIP;
-      args.table = table;
+      args.table = (const JobDesc*)table;
+      args.index = l.index.empty() ? nullptr : (const int32_t*)(table + tb);
+      args.bshift = l.bshift;
     } else {
       for (size_t i = 0; i < l.descs.size(); i++) args.inl[i] = l.descs[i];
       args.table = nullptr;
+      args.index = nullptr;
     }
     int grid;
     if (l.kind == kGroupMfma) {
@@ -343,6 +387,8 @@ qgemm_status qgemm_sweep_path(const qgemm_job* jobs, int njobs, int path, void* 
       args.counters = (int*)(ws + l.counters_off);
       args.slots = (float*)(ws + l.slots_off);
       args.nwaves = l.nwaves;
+      args.q = (int32_t)(l.total / l.nwaves);
+      args.rem = (int32_t)(l.total % l.nwaves);
       args.slot_rows = l.cls;
       grid = (l.nwaves + qg::kStreamWavesPerBlock - 1) / qg::kStreamWavesPerBlock;
     }

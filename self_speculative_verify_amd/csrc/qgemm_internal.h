@@ -18,16 +18,28 @@ constexpr int kMaxInline = 12;       // jobs passed by value in the kernel argum
 constexpr int kXRowBytes = 272;      // LDS row stride of a staged X chunk (256 + 16 pad)
 
 // stream kernel (panels of at most 16 rows): waves per workgroup, and the
-// range of waves in the grid (8 to 16 per CU of a 256-CU MI355X).  The count
-// is chosen from the shapes alone -- never from the device or M -- so the K
-// split of every row block, and with it every output bit, is reproducible.
+// range of waves in the grid.  The count is chosen from the shapes alone --
+// never from the device or M -- so the K split of every row group, and with it
+// every output bit, is reproducible.
 constexpr int kStreamWavesPerBlock = 4;
-constexpr int kStreamMinWaves = 2048;
-constexpr int kStreamWaves = 4096;
+constexpr int kStreamMinWaves = 1024;
+constexpr int kStreamWaves = 1024;
 // group kernel (17..64 rows): waves per workgroup, one 16-row block each
 constexpr int kGroupWaves = 8;
 
+// Stream kernels walk "steps": one k tile of a row group of kStreamRows
+// consecutive 16-row blocks.  The same for every class of a path, so the K
+// split of a row -- and with it every output bit -- does not depend on M.
+constexpr int kStreamRows = 4;
+constexpr int stream_rows(int kind, int cls) { return (void)kind, (void)cls, kStreamRows; }
+
 inline __host__ __device__ int tile_bytes(int bits) { return bits == 4 ? kTile4 : kTile5; }
+
+// Stream kernels split work by weight bytes: a step of a 4-bit job weighs 9
+// units, of a 5-bit job 11 (tile bytes / 128), and every wave gets at least
+// kMaxUnitWeight units, so every wave holds at least one step.
+inline __host__ __device__ int unit_weight(int bits) { return tile_bytes(bits) / kTileK; }
+constexpr int kMaxUnitWeight = kTile5 / kTileK;
 
 // One job as the kernels see it.  All sizes are derived on the host.
 struct JobDesc {
@@ -36,27 +48,31 @@ struct JobDesc {
   float* Y;
   int64_t ldx;
   int64_t ldy;
-  int64_t tile_begin;    // stream kernel: first flat tile of this job
-  int64_t tile_end;
+  int32_t ubeg;          // stream kernel: units [ubeg, uend) of this job's steps
+  int32_t uend;          //   (a step weighs unit_weight(bits) units)
   int32_t N, K;
   int32_t M, bits;
   int32_t nkt;           // ceil(K / 128)
   int32_t ngroups;       // K / 32
   int32_t nrb;           // ceil(N / 16)
-  int32_t rb_begin;      // stream kernel: first arrival counter of this job
-  int32_t unit_begin;    // group kernel: first unit (row-block group) of this job
-  int32_t unit_end;
+  int32_t nrg;           // stream kernel: row groups, ceil(nrb / stream_rows)
+  int32_t rg_begin;      // stream kernel: first arrival counter of this job
+  int32_t grp_begin;     // group kernel: first row-block group of this job
+  int32_t grp_end;
 };
 
 struct SweepArgs {
-  const JobDesc* table;  // device copy of all jobs (when njobs > kMaxInline), else null
-  int* counters;         // stream kernel: arrival counter per row block (zero between calls)
-  float* slots;          // stream kernel: two partial-sum slots per wave
-  int64_t total;         // stream kernel: flat tiles; group kernel: units
-  int32_t njobs;
+  int32_t total;         // stream kernel: flat units; group kernel: row-block groups (< 2^31)
   int32_t nwaves;        // stream kernel: waves in the grid (fixes the K split)
-  int32_t slot_rows;     // stream kernel: rows per slot
+  int32_t q, rem;        // stream kernel: wave w takes q units, one more if w < rem
+  int32_t njobs;
+  int32_t slot_rows;     // stream kernel: rows m per slot (the class)
+  int32_t bshift;        // stream kernel with a table: log2 of the units per bucket
   int32_t pad_;
+  const JobDesc* table;  // device copy of all jobs (when njobs > kMaxInline), else null
+  const int32_t* index;  // with a table: uend of every job, then the first job of every bucket
+  int* counters;         // stream kernel: arrival counter per row group (zero between calls)
+  float* slots;          // stream kernel: two partial-sum slots per wave
   JobDesc inl[kMaxInline];
 };
 

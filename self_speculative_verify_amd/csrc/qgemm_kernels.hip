@@ -25,6 +25,7 @@ typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+typedef float f2_t __attribute__((ext_vector_type(2)));
 
 // --------------------------------------------------------------------------
 // pack
@@ -116,7 +117,7 @@ __global__ void __launch_bounds__(256) pack_kernel(const float* __restrict__ W, 
       for (int e = 0; e < 8; e++) {
         const int uu = u[8 * c + e];
         word |= (uint32_t)(uu & 15) << (4 * (e >> 1) + 16 * (e & 1));
-        if (BITS == 5) hi[c] |= (uint32_t)((uu >> 4) & 1) << ((4 + 16 * (e & 1) + 4 * j + (e >> 1)) & 31);
+        if (BITS == 5) hi[c] |= (uint32_t)((uu >> 4) & 1) << ((4 + 16 * (e & 1) + 4 * (e >> 1) + j) & 31);
       }
       code[c][j] = word;
     }
@@ -146,31 +147,79 @@ __global__ void __launch_bounds__(256) pack_kernel(const float* __restrict__ W, 
 #define QG_CONST
 #endif
 
+// Split-K partial sums are exchanged through raw buffer accesses with the
+// system-coherent cache policy (sc0 sc1: written through to and read from
+// memory, as system-scope atomics are), which also vectorize.  kBufWord3 is
+// word 3 of a raw (untyped) gfx9 buffer descriptor.
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kCoherent = 1 | 16;
+
 template <typename T>
 __device__ __forceinline__ const QG_GLOBAL T* gload_ptr(const void* p) {
   return (const QG_GLOBAL T*)p;
 }
 
-// Eight codes of one group chunk -> four fp16 pairs holding the exact q.
+// Eight codes of one group chunk (code word w of group J, high word h) ->
+// four fp16 pairs holding the exact q; pair i holds elements (2i, 2i+1).
+// Pair i's low nibbles sit at bits (4i, 16+4i) of w.  OR-ing 0x6400 into an
+// fp16 sets its exponent field to 25 (value 1024, unit spacing), so
+//   pair 0: (w & 0x000F000F) | 0x64006400 = 1024 + u     -> q = t - (1024 + bias)
+//   pair 1: (w & 0x00F000F0) | 0x64006400 = 1024 + 16u   -> q = t / 16 - (64 + bias)
+// and pairs 2, 3 the same from w >> 8.  Both forms are exact: one packed fp16
+// add or fma whose operands and result are exactly representable.  5-bit:
+// bit 4 of the pair-i codes of group J sits at bits (4 + 4i + J, 20 + 4i + J)
+// mod 32 of h, so rotr(h, J) places pairs 0 and 1 at (4, 20) and (8, 24) --
+// bit 4 of u in the first form, of 16u in the second -- and rotr(h, J + 8)
+// does the same for pairs 2 and 3.
+// v_and_or_b32 (a & m) | o in one instruction.  Written out because with two
+// literal operands the compiler splits it into v_and + v_or (a VOP3 encoding
+// holds no literal on this target); here the constants live in registers.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
+}
+
 template <int BITS>
-__device__ __forceinline__ h8_t unpack_chunk(uint32_t w, uint32_t hi, int j) {
-  constexpr uint32_t kMagic = 0x64006400u;                       // (1024.0, 1024.0)
-  constexpr _Float16 kOff = (_Float16)(1024 + (1 << (BITS - 1)));
-  const h2_t off = {kOff, kOff};
-  h8_t out;
+__device__ __forceinline__ void unpack8(uint32_t w, uint32_t h, int J, h2_t (&q)[4]) {
+  constexpr uint32_t kMagic = 0x64006400u;
+  constexpr _Float16 kOff0 = (_Float16)(-1024 - (1 << (BITS - 1)));
+  constexpr _Float16 kOff1 = (_Float16)(-64 - (1 << (BITS - 1)));
+  const h2_t off0 = {kOff0, kOff0}, off1 = {kOff1, kOff1};
+  const h2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const uint32_t w2 = w >> 8;
+  uint32_t t0 = and_or(w, 0x000F000Fu, kMagic), t1 = and_or(w, 0x00F000F0u, kMagic);
+  uint32_t t2 = and_or(w2, 0x000F000Fu, kMagic), t3 = and_or(w2, 0x00F000F0u, kMagic);
+  if constexpr (BITS == 5) {
+    const uint32_t h0 = __builtin_amdgcn_alignbit(h, h, J);
+    const uint32_t h2 = __builtin_amdgcn_alignbit(h, h, J + 8);
+    t0 = and_or(h0, 0x00100010u, t0);
+    t1 = and_or(h0, 0x01000100u, t1);
+    t2 = and_or(h2, 0x00100010u, t2);
+    t3 = and_or(h2, 0x01000100u, t3);
+  }
+  q[0] = __builtin_bit_cast(h2_t, t0) + off0;
+  q[1] = __builtin_elementwise_fma(__builtin_bit_cast(h2_t, t1), sixteenth, off1);
+  q[2] = __builtin_bit_cast(h2_t, t2) + off0;
+  q[3] = __builtin_elementwise_fma(__builtin_bit_cast(h2_t, t3), sixteenth, off1);
+}
+
+__device__ __forceinline__ h8_t cat8(const h2_t (&q)[4]) {
+  h8_t o;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    uint32_t t = ((w >> (4 * i)) & 0x000F000Fu) | kMagic;
-    if (BITS == 5) {
-      const int s = 4 * j + i;  // rotate right: bits (4+s, 20+s) of hi -> bits (4, 20)
-      const uint32_t rot = (hi >> s) | (hi << ((32 - s) & 31));
-      t |= rot & 0x00100010u;
-    }
-    const h2_t q = __builtin_bit_cast(h2_t, t) - off;
-    out[2 * i] = q.x;
-    out[2 * i + 1] = q.y;
+    o[2 * i] = q[i].x;
+    o[2 * i + 1] = q[i].y;
   }
-  return out;
+  return o;
+}
+
+// (J is a constant after unrolling, so the rotations take immediates.)
+template <int BITS>
+__device__ __forceinline__ h8_t unpack_chunk(uint32_t w, uint32_t hi, int J) {
+  h2_t q[4];
+  unpack8<BITS>(w, hi, J, q);
+  return cat8(q);
 }
 
 // The weight part of one k tile as seen by lane l = r + 16c: its 16 code
@@ -239,178 +288,113 @@ __device__ __forceinline__ void mfma_tile(f4_t (&acc)[MB], const WRegs& w, const
   }
 }
 
-// GEMV: per lane and row m, four v_dot2_f32_f16 over the lane's 8 codes of a
-// group, scaled by the group's scale; the four k chunks of a row (lanes r,
-// r+16, r+32, r+48) are summed when the row block is flushed.
-template <int BITS, int GM>
-__device__ __forceinline__ void gemv_tile(float (&acc)[GM], const WRegs& w, const uint8_t* xs, int lane,
-                                          int gleft, int M) {
-  const int c = lane >> 4;
-  const h2_t s01 = scale_pair(w.ws.x), s23 = scale_pair(w.ws.y);
-  const float sc[4] = {(float)s01.x, (float)s01.y, (float)s23.x, (float)s23.y};
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    if (j < gleft) {
-      const h8_t q = unpack_chunk<BITS>(w.wc[j], w.wh, j);
-      const h2_t q0 = {q[0], q[1]}, q1 = {q[2], q[3]}, q2 = {q[4], q[5]}, q3 = {q[6], q[7]};
-#pragma unroll
-      for (int m = 0; m < GM; m++) {
-        if (m < M) {
-          const h8_t x = lds_h8(xs + m * kXRowBytes + 64 * j + 16 * c);
-          const h2_t x0 = {x[0], x[1]}, x1 = {x[2], x[3]}, x2 = {x[4], x[5]}, x3 = {x[6], x[7]};
-          float d = __builtin_amdgcn_fdot2(q0, x0, 0.f, false);
-          d = __builtin_amdgcn_fdot2(q1, x1, d, false);
-          d = __builtin_amdgcn_fdot2(q2, x2, d, false);
-          d = __builtin_amdgcn_fdot2(q3, x3, d, false);
-          acc[m] = __builtin_fmaf(sc[j], d, acc[m]);
-        }
-      }
-    }
-  }
-}
-
 __device__ __forceinline__ const QG_CONST JobDesc* job_table(const SweepArgs& a) {
   return a.table ? (const QG_CONST JobDesc*)a.table : (const QG_CONST JobDesc*)&a.inl[0];
 }
 
 // --------------------------------------------------------------------------
-// stream kernel: panels of at most 16 rows (GEMV, or MFMA with one m block)
+// stream kernels: panels of at most 16 rows (GEMV, or MFMA with one m block)
 // --------------------------------------------------------------------------
-// The flat sequence of (job, row block, k tile) tiles is cut into `nwaves`
-// equal contiguous ranges, one per wave, so every wave streams the same number
-// of tiles.  A wave accumulates one row block at a time; a row block whose
-// tiles all lie in one range is written to Y directly.  A row block cut by
-// range ends gets one partial sum per contributing wave, stored into that
-// wave's slot; the last contributor to arrive (per-row-block counter) adds the
-// partials in wave order -- k order -- writes Y and resets the counter to
-// zero.  Nothing waits on another wave.  The slots and counters are accessed
-// with system-scope atomics: the per-XCD L2 caches are not coherent with each
-// other, and system-scope accesses bypass them, so no cache-wide writeback or
-// invalidate is needed on either side of the exchange.
-
-// One k tile of the stream kernels.  kRagged: the tile may hold fewer than
-// four groups (the last tile of a row when K % 128 != 0).
-// MFMA: only the first NF of the lane's four accumulator rows are scaled and
-// kept (rows 4*(l/16)+i, i < NF); panels of at most 4 rows need NF = M.
-template <int BITS, int NF, bool kRagged>
-__device__ __forceinline__ void mfma1_tile(f4_t& acc, const WRegs& w, const uint8_t* xs, int lane, int gleft) {
-  const int r = lane & 15, c = lane >> 4;
-  const h2_t s01 = scale_pair(w.ws.x), s23 = scale_pair(w.ws.y);
-  const _Float16 sh[4] = {s01.x, s01.y, s23.x, s23.y};
-  const f4_t zero = {0.f, 0.f, 0.f, 0.f};
-  // all four groups' MFMAs are issued before any of their results is read,
-  // so the MFMA latency overlaps with independent work instead of stalling
-  f4_t p[4];
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    if (!kRagged || j < gleft) {
-      const h8_t q = unpack_chunk<BITS>(w.wc[j], w.wh, j);
-      const h8_t a = lds_h8(xs + r * kXRowBytes + 64 * j + 16 * c);
-      p[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, q, zero, 0, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    if (!kRagged || j < gleft) {
-      const float sj = (float)sh[j];
-#pragma unroll
-      for (int i = 0; i < NF; i++) acc[i] = __builtin_fmaf(sj, p[j][i], acc[i]);
-    }
-  }
-}
-
-template <int BITS, int GM, bool kRagged>
-__device__ __forceinline__ void gemv1_tile(float (&acc)[GM], const WRegs& w, const uint8_t* xs, int lane,
-                                           int gleft, int M) {
-  const int c = lane >> 4;
-  const h2_t s01 = scale_pair(w.ws.x), s23 = scale_pair(w.ws.y);
-  const _Float16 sh[4] = {s01.x, s01.y, s23.x, s23.y};
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    if (!kRagged || j < gleft) {
-      const h8_t q = unpack_chunk<BITS>(w.wc[j], w.wh, j);
-      const h2_t q0 = {q[0], q[1]}, q1 = {q[2], q[3]}, q2 = {q[4], q[5]}, q3 = {q[6], q[7]};
-      const float sj = (float)sh[j];
-#pragma unroll
-      for (int m = 0; m < GM; m++) {
-        if (m < M) {
-          const h8_t x = lds_h8(xs + m * kXRowBytes + 64 * j + 16 * c);
-          const h2_t x0 = {x[0], x[1]}, x1 = {x[2], x[3]}, x2 = {x[4], x[5]}, x3 = {x[6], x[7]};
-          float d = __builtin_amdgcn_fdot2(q0, x0, 0.f, false);
-          d = __builtin_amdgcn_fdot2(q1, x1, d, false);
-          d = __builtin_amdgcn_fdot2(q2, x2, d, false);
-          d = __builtin_amdgcn_fdot2(q3, x3, d, false);
-          acc[m] = __builtin_fmaf(sj, d, acc[m]);
-        }
-      }
-    }
-  }
-}
-
-// --------------------------------------------------------------------------
-// stream kernel: panels of at most 16 rows (GEMV, or MFMA with one m block)
-// --------------------------------------------------------------------------
-// The flat sequence of (job, row block, k tile) tiles is cut into `nwaves`
-// equal contiguous ranges, one per wave, so every wave streams the same number
-// of tiles.  Within one job a wave's tiles are contiguous in memory (tile
-// index rb * NKT + kt), so the weight pointer simply advances.  A wave
-// accumulates one row block at a time; a row block whose tiles all lie in one
-// range is written to Y directly.  A row block cut by range ends gets one
+// Work is a flat sequence of steps (job, row group, k tile); a row group is
+// kR consecutive 16-row blocks, and one step reads the kR tiles of its row
+// group at one k tile.  The sequence is cut into `nwaves` equal contiguous
+// ranges, one per wave, so every wave streams the same number of steps.
+// Within one job a row group's steps are consecutive tiles in memory per row
+// block (tile index rb * NKT + kt), so the weight pointers simply advance.  A
+// wave accumulates one row group at a time; a row group whose steps all lie in
+// one range is written to Y directly.  A row group cut by range ends gets one
 // partial sum per contributing wave, stored into that wave's slot; the last
-// contributor to arrive (per-row-block counter) adds the partials in wave
+// contributor to arrive (per-row-group counter) adds the partials in wave
 // order -- k order -- writes Y and resets the counter to zero.  Nothing waits
 // on another wave.  The slots and counters are accessed with system-scope
 // atomics, which bypass the per-XCD L2 caches (not coherent with each other).
+//
+// MFMA: v_mfma_f32_16x16x32_f16 with A = X (16 rows m x 32 k of one group)
+// and B = codes (32 k x 16 rows n): lane l supplies A row m = l%16 and B
+// column n = l%16, both for k chunk l/16 -- exactly the lane's 16 code bytes
+// -- and holds D for (m = 4(l/16) + i, n = l%16).  The group's scale (one per
+// lane) multiplies D before it is added to the accumulators; only the kA rows
+// that can hold m < M are kept.  X rows m >= M read row M-1 and feed only
+// output rows that are never stored (MFMA rows are independent).
+// GEMV: lane l = r + 16c forms, for row n = r and each m, four v_dot2_f32_f16
+// over its 8 codes of a group, scaled by the group's scale; the four k chunks
+// of a row (lanes r, r+16, r+32, r+48) are summed when the row group is
+// written.  X chunks go through a small wave-private LDS buffer.
+// Padding groups (beyond K) have codes q = 0 and scale +0, and their X reads
+// are clamped into the row, so they add exact zeros: no tile needs a branch.
 template <bool kMfma, int kCap>
 struct Stream {
-  static constexpr int kRows = kMfma ? 16 : kCap;                 // X rows staged in LDS
-  static constexpr int kLoadRows = kCap;                          // X rows loaded per tile
-  static constexpr int kPieces = (kLoadRows * 16 + 63) / 64;      // 16-byte X pieces per lane
-  static constexpr int kNF = kCap < 4 ? kCap : 4;                 // MFMA accumulator rows kept
-  // tiles in flight per wave (fewer where the panel's registers need room);
-  // 2048..4096 waves x depth x 1.15 KB keeps >= ~16 MB of reads in flight
-  static constexpr int kDepth = kCap <= 2 ? 8 : kCap == 4 ? 6 : kCap == 8 ? (kMfma ? 4 : 2) : 3;
+  static constexpr int kR = stream_rows(kMfma ? 1 : 0, kCap);        // row blocks per step
+  static constexpr int kA = kMfma ? (kCap < 4 ? kCap : 4) : kCap;    // accumulators per row block
+  static constexpr int kXP = kMfma ? 4 : (kCap * 16 + 63) / 64;      // X loads per lane per step
+  // steps in flight per wave: about 8 tiles (9-11 KB) per wave
+  static constexpr int kDepth = 4;
 
-  struct Regs {
-    WRegs w;
-    u4_t x[kPieces];
+  template <int BITS>
+  struct Step {
+    u4_t c[kR];
+    u2_t s[kR];
+    uint32_t h[BITS == 5 ? kR : 1];
+    u4_t x[kXP];
   };
 
-  struct Acc {
-    f4_t mf;
-    float gv[kCap];
+  // Position of a step cursor: wp points at tile (rg * kR, kt) of the job and
+  // the step's tile r sits roff[r] bytes further (blocks past the job's last
+  // read the last one again; their sums are never stored).  Offsets fit 32
+  // bits because K <= 2^24 (host check).
+  struct Cur {
+    const uint8_t* wp;
+    uint32_t roff[kR];
+    int kt, rg;
   };
 
-  static __device__ __forceinline__ void zero(Acc& a) {
-    a.mf = f4_t{0.f, 0.f, 0.f, 0.f};
+  static __device__ __forceinline__ void set_rows(Cur& c, int nrb, uint32_t rstride) {
+    const int left = nrb - 1 - c.rg * kR;  // >= 0
 #pragma unroll
-    for (int m = 0; m < kCap; m++) a.gv[m] = 0.f;
+    for (int r = 0; r < kR; r++) c.roff[r] = (uint32_t)(r < left ? r : left) * rstride;
   }
 
-  static __device__ __forceinline__ int64_t wave_of(int64_t f, int64_t T, int64_t G) {
-    const int64_t w = ((f + 1) * G - 1) / T;
-    return w < G - 1 ? w : G - 1;
+  static __device__ __forceinline__ void advance(Cur& c, int nkt, int nrb, uint32_t rstride, uint32_t tb) {
+    c.wp += tb;
+    if (++c.kt == nkt) {
+      c.kt = 0;
+      c.rg++;
+      c.wp += (uint64_t)(kR - 1) * rstride;
+      set_rows(c, nrb, rstride);
+    }
   }
 
-  // Everything a wave needs to place one row block's sums.
+  // Wave w streams the steps whose first unit lies in [start(w), start(w + 1)):
+  // q units each, one more for the first rem waves.
+  static __device__ __forceinline__ int start_of(int w, int q, int rem) { return w * q + (w < rem ? w : rem); }
+  static __device__ __forceinline__ int wave_of(int f, int q, int rem) {
+    const int edge = rem * (q + 1);
+    return f < edge ? f / (q + 1) : rem + (f - edge) / q;
+  }
+
+  // Everything a wave needs to place one row group's sums.
+  struct Ctx;
+  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const Ctx& cx) {
+    const int bytes = 2 * cx.G * cx.slot_rows * kR * kTileRows * 4;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)cx.slots, (short)0, bytes, kBufWord3);
+  }
   struct Ctx {
     const QG_CONST JobDesc* D;
     int* counters;
     float* slots;
-    int64_t T, G;          // flat tiles, waves
+    int q, rem, G;         // partition of the flat steps over G waves
     int slot_rows;
-    int64_t gw, a, b;
+    int gw, a, b;
     int lane;
-    // split row blocks whose partial this wave stored (kind 0 / kind 1)
-    int pend_j0, pend_rb0, pend_j1, pend_rb1;
+    // split row groups whose partial this wave stored (kind 0 / kind 1)
+    int pend_j0, pend_rg0, pend_j1, pend_rg1;
   };
 
-  // Write the finished sums of row block rb of job j to Y, or, for a row
-  // block cut by this wave's range, store this wave's partial into its slot
-  // (kind 0: the range's first row block, kind 1: its last) and note it; the
-  // arrival is counted once, at the end of the range (see arrive), so the
-  // stream never stalls on it.
-  static __device__ __forceinline__ void flush(Acc acc, Ctx& cx, int j, int rb) {
+  // Write the finished sums of row group rg of job j to Y, or, for a row
+  // group cut by this wave's range, store this wave's partial into its slot
+  // (kind 0: the range's first row group, kind 1: its last) and note it; the
+  // arrival is counted once, at the end of the range (see arrive).
+  static __device__ __forceinline__ void flush(float (&acc)[kR][kA], Ctx& cx, int j, int rg) {
     const QG_CONST JobDesc* D = cx.D;
     const int lane = cx.lane;
     const int M = D[j].M, N = D[j].N, nkt = D[j].nkt;
@@ -418,181 +402,367 @@ struct Stream {
     QG_GLOBAL float* Y = (QG_GLOBAL float*)D[j].Y;
     if constexpr (!kMfma) {
 #pragma unroll
-      for (int m = 0; m < kCap; m++) {
-        float v = acc.gv[m];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        acc.gv[m] = v;
-      }
+      for (int r = 0; r < kR; r++)
+#pragma unroll
+        for (int m = 0; m < kCap; m++) {
+          float v = acc[r][m];
+          v += __shfl_xor(v, 16);
+          v += __shfl_xor(v, 32);
+          acc[r][m] = v;
+        }
     }
-    const int64_t first = D[j].tile_begin + (int64_t)rb * nkt;
-    const int64_t last = first + nkt - 1;
+    const int wt = unit_weight(D[j].bits);
+    const int first = D[j].ubeg + rg * nkt * wt;   // first unit of the row group's first step
+    const int last = first + (nkt - 1) * wt;       // ... and of its last step
     const int nn = lane & 15;
-    const int n = rb * kTileRows + nn;
+    // row m held by this lane in accumulator i (MFMA), or m = i (GEMV, lanes < 16)
+    auto row_of = [&](int i) { return kMfma ? 4 * (lane >> 4) + i : i; };
+    const bool holder = kMfma || lane < 16;
     if (first >= cx.a && last < cx.b) {
-      if (n < N) {
-        if constexpr (kMfma) {
 #pragma unroll
-          for (int i = 0; i < kNF; i++) {
-            const int m = 4 * (lane >> 4) + i;
-            if (m < M) Y[(int64_t)m * ldy + n] = acc.mf[i];
+      for (int r = 0; r < kR; r++) {
+        const int n = (rg * kR + r) * kTileRows + nn;
+        if (holder && n < N) {
+#pragma unroll
+          for (int i = 0; i < kA; i++) {
+            const int m = row_of(i);
+            if (m < M) Y[(int64_t)m * ldy + n] = acc[r][i];
           }
-        } else if (lane < 16) {
-#pragma unroll
-          for (int m = 0; m < kCap; m++)
-            if (m < M) Y[(int64_t)m * ldy + n] = acc.gv[m];
         }
       }
       return;
     }
-    const int slot_floats = cx.slot_rows * kTileRows;
-    const int kind = cx.a >= first ? 0 : 1;
-    float* mine = cx.slots + (cx.gw * 2 + kind) * slot_floats;
+    // partial: slot of (wave, kind), laid out [column][slot_rows] so that each
+    // lane's rows are contiguous; written through to memory (system scope)
+    const int srows = cx.slot_rows;
+    // kind 0: the row group began before this range (its first row group);
+    // kind 1: it begins inside and runs past the range (its last)
+    const int kind = cx.a > first ? 0 : 1;
+    const uint32_t sbase = (uint32_t)((cx.gw * 2 + kind) * srows * kR * kTileRows) * 4u;
+    const __amdgpu_buffer_rsrc_t sr = slot_rsrc(cx);
     if constexpr (kMfma) {
+      const int m0 = 4 * (lane >> 4);
+      if (m0 < srows) {
 #pragma unroll
-      for (int i = 0; i < kNF; i++) {
-        const int m = 4 * (lane >> 4) + i;
-        if (m < M) __hip_atomic_store(mine + m * kTileRows + nn, acc.mf[i], __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_SYSTEM);
+        for (int r = 0; r < kR; r++) {
+          const uint32_t o = sbase + (uint32_t)(((r * kTileRows + nn) * srows + m0) * 4);
+          if constexpr (kA == 4) {
+            const f4_t v = {acc[r][0], acc[r][1], acc[r][2], acc[r][3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, v), sr, o, 0, kCoherent);
+          } else if constexpr (kA == 2) {
+            const f2_t v = {acc[r][0], acc[r][1]};
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2_t, v), sr, o, 0, kCoherent);
+          } else {
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc[r][0]), sr, o, 0, kCoherent);
+          }
+        }
       }
     } else if (lane < 16) {
 #pragma unroll
-      for (int m = 0; m < kCap; m++)
-        if (m < M)
-          __hip_atomic_store(mine + m * kTileRows + nn, acc.gv[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      for (int r = 0; r < kR; r++) {
+        const uint32_t o = sbase + (uint32_t)((r * kTileRows + nn) * srows * 4);
+        if constexpr (kCap == 1) {
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc[r][0]), sr, o, 0, kCoherent);
+        } else if constexpr (kCap == 2) {
+          const f2_t v = {acc[r][0], acc[r][1]};
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2_t, v), sr, o, 0, kCoherent);
+        } else {
+#pragma unroll
+          for (int q = 0; q < kCap; q += 4) {
+            const f4_t v = {acc[r][q], acc[r][q + 1], acc[r][q + 2], acc[r][q + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, v), sr, o + 4u * q, 0, kCoherent);
+          }
+        }
+      }
     }
     if (kind == 0) {
       cx.pend_j0 = j;
-      cx.pend_rb0 = rb;
+      cx.pend_rg0 = rg;
     } else {
       cx.pend_j1 = j;
-      cx.pend_rb1 = rb;
+      cx.pend_rg1 = rg;
     }
   }
 
-  // Count this wave's arrival at split row block rb of job j (its partial is
-  // already stored and complete); the last of its contributors adds all
-  // partials in wave order -- k order -- writes Y and resets the counter.
-  static __device__ __forceinline__ void arrive(const Ctx& cx, int j, int rb) {
+  // A split row group's contributors are the waves wf..wl whose ranges hold
+  // its first and last steps; its arrival counter is at counters[rg_begin + rg].
+  static __device__ __forceinline__ void span(const Ctx& cx, int j, int rg, int& wf, int& wl) {
+    const QG_CONST JobDesc* D = cx.D;
+    const int wt = unit_weight(D[j].bits), nkt = D[j].nkt;
+    const int first = D[j].ubeg + rg * nkt * wt;
+    wf = wave_of(first, cx.q, cx.rem);
+    wl = wave_of(first + (nkt - 1) * wt, cx.q, cx.rem);
+  }
+
+  // Sums of split row groups.  The last contributor to arrive at a row group
+  // (every partial stored and complete) adds all partials in wave order -- k
+  // order -- writes Y and resets the arrival counter.  A wave can complete
+  // both of its split row groups; all their partial loads are issued before
+  // the first add, 4 floats per load.
+  // slots hold kCap rows (the class); 4-float chunks per lane, and partials
+  // loaded per batch (at least 8 loads in flight)
+  static constexpr int kChunksPerLane = (kCap * kR * kTileRows / 4 + 63) / 64;
+  static constexpr int kBatch = kChunksPerLane >= 8 ? 1 : 8 / kChunksPerLane;
+
+  static __device__ __forceinline__ void reduce2(const Ctx& cx, bool do0, bool do1) {
     const QG_CONST JobDesc* D = cx.D;
     const int lane = cx.lane;
-    const int M = D[j].M, N = D[j].N, nkt = D[j].nkt;
-    const int64_t ldy = D[j].ldy;
-    QG_GLOBAL float* Y = (QG_GLOBAL float*)D[j].Y;
-    const int64_t first = D[j].tile_begin + (int64_t)rb * nkt;
-    const int64_t last = first + nkt - 1;
-    const int64_t T = cx.T, G = cx.G;
-    const int slot_floats = cx.slot_rows * kTileRows;
-    const int64_t wf = wave_of(first, T, G), wl = wave_of(last, T, G);
-    const int contributors = (int)(wl - wf + 1);
-    int* ctr = cx.counters + D[j].rb_begin + rb;
-    int old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    old = __builtin_amdgcn_readfirstlane(old);
-    if (old != contributors - 1) return;
+    const int srows = cx.slot_rows, cols = kR * kTileRows;
+    const int slot_bytes = srows * cols * 4;
+    const int nchunks = srows * cols / 4;
+    const __amdgpu_buffer_rsrc_t sr = slot_rsrc(cx);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    for (int e = lane; e < M * kTileRows; e += 64) {
-      const int m = e / kTileRows, col = e % kTileRows;
-      float v = 0.f;
-      for (int64_t w = wf; w <= wl; w++) {
-        const int64_t aw = w * T / G;
-        const int kw = aw >= first ? 0 : 1;
-        v += __hip_atomic_load(cx.slots + (w * 2 + kw) * slot_floats + e, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_SYSTEM);
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      if (k == 0 ? !do0 : !do1) continue;
+      const int j = k == 0 ? cx.pend_j0 : cx.pend_j1, rg = k == 0 ? cx.pend_rg0 : cx.pend_rg1;
+      int wf, wl;
+      span(cx, j, rg, wf, wl);
+      const int M = D[j].M, N = D[j].N;
+      const int64_t ldy = D[j].ldy;
+      QG_GLOBAL float* Y = (QG_GLOBAL float*)D[j].Y;
+      // The first contributor holds the row group's first step (its kind-1
+      // slot); every later one began inside the row group (kind 0).
+      auto part = [&](int w, int q) {
+        const int kw = w == wf ? 1 : 0;
+        return __builtin_bit_cast(
+            f4_t, __builtin_amdgcn_raw_buffer_load_b128(sr, 16u * q, (uint32_t)((w * 2 + kw) * slot_bytes), kCoherent));
+      };
+      f4_t v[kChunksPerLane];
+#pragma unroll
+      for (int c = 0; c < kChunksPerLane; c++) v[c] = f4_t{0.f, 0.f, 0.f, 0.f};
+      for (int w = wf; w <= wl; w += kBatch) {
+        f4_t p[kBatch][kChunksPerLane];
+#pragma unroll
+        for (int t = 0; t < kBatch; t++)
+#pragma unroll
+          for (int c = 0; c < kChunksPerLane; c++) {
+            const int q = lane + 64 * c;
+            p[t][c] = (w + t <= wl && q < nchunks) ? part(w + t, q) : f4_t{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+        for (int t = 0; t < kBatch; t++)
+#pragma unroll
+          for (int c = 0; c < kChunksPerLane; c++)
+            if (w + t <= wl) v[c] += p[t][c];
       }
-      const int ncol = rb * kTileRows + col;
-      if (ncol < N) Y[(int64_t)m * ldy + ncol] = v;
-    }
-    if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  }
-
-  // xp points at X[0][kbase]; pieces with k = kbase + 8*col >= K or rows >= M
-  // read X[0][0] and are never used.
-  template <int BITS>
-  static __device__ __forceinline__ void load(Regs& t, const uint8_t* wp, const uint16_t* X, int kbase,
-                                              int lane, int M, int K, int64_t ldx) {
-    t.w.wc = __builtin_nontemporal_load(gload_ptr<u4_t>(wp + 16 * lane));
-    t.w.ws = __builtin_nontemporal_load(gload_ptr<u2_t>(wp + kScaleOff + 8 * (lane & 15)));
-    if constexpr (BITS == 5) t.w.wh = __builtin_nontemporal_load(gload_ptr<uint32_t>(wp + kHiOff + 4 * lane));
-    else t.w.wh = 0u;
 #pragma unroll
-    for (int p = 0; p < kPieces; p++) {
-      const int piece = lane + 64 * p;
-      const int row = piece >> 4, col = piece & 15;
-      const int k = kbase + 8 * col;
-      const bool ok = row < M && row < kLoadRows && k < K;
-      t.x[p] = *gload_ptr<u4_t>(X + (ok ? (int64_t)row * ldx + k : 0));
-    }
-  }
-
-  static __device__ __forceinline__ void stage(const Regs& t, uint8_t* xs, int lane) {
+      for (int c = 0; c < kChunksPerLane; c++) {
+        const int q = lane + 64 * c;
+        if (q >= nchunks) continue;
 #pragma unroll
-    for (int p = 0; p < kPieces; p++) {
-      const int piece = lane + 64 * p;
-      const int row = piece >> 4, col = piece & 15;
-      if (row < kLoadRows) *(u4_t*)(xs + row * kXRowBytes + 16 * col) = t.x[p];
+        for (int t = 0; t < 4; t++) {
+          const int e = 4 * q + t, col = e / srows, m = e - col * srows;
+          const int n = rg * cols + col;
+          if (m < M && n < N) Y[(int64_t)m * ldy + n] = v[c][t];
+        }
+      }
+      if (lane == 0)
+        __hip_atomic_store(cx.counters + D[j].rg_begin + rg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
 
-  // Tiles [s0, s1) of job j (local indices rb * NKT + kt), BITS fixed.
+  // Count this wave's arrivals at its split row groups (kind 0 and kind 1;
+  // both atomics issued before either result is used) and reduce those it
+  // completes.  Called once, at the end of the range, after every partial
+  // store of the wave has completed.
+  static __device__ __forceinline__ void arrive(const Ctx& cx) {
+    const QG_CONST JobDesc* D = cx.D;
+    const bool has0 = cx.pend_j0 >= 0, has1 = cx.pend_j1 >= 0;
+    int old0 = 0, old1 = 0;
+    if (cx.lane == 0) {
+      if (has0)
+        old0 = __hip_atomic_fetch_add(cx.counters + D[cx.pend_j0].rg_begin + cx.pend_rg0, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_SYSTEM);
+      if (has1)
+        old1 = __hip_atomic_fetch_add(cx.counters + D[cx.pend_j1].rg_begin + cx.pend_rg1, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    old0 = __builtin_amdgcn_readfirstlane(old0);
+    old1 = __builtin_amdgcn_readfirstlane(old1);
+    int wf, wl;
+    bool last0 = false, last1 = false;
+    if (has0) {
+      span(cx, cx.pend_j0, cx.pend_rg0, wf, wl);
+      last0 = old0 == wl - wf;
+    }
+    if (has1) {
+      span(cx, cx.pend_j1, cx.pend_rg1, wf, wl);
+      last1 = old1 == wl - wf;
+    }
+    if (last0 || last1) reduce2(cx, last0, last1);
+  }
+
+  // Issue the loads of the step at cursor c: kR weight tiles (non-temporal:
+  // streamed once) and the X chunk.  X reads outside [0, M) x [0, K) are
+  // clamped into the matrix (see above); xlane[p] is the lane's byte offset
+  // into X for k = 0.
   template <int BITS>
-  static __device__ __forceinline__ void segment(Ctx& cx, int j, int64_t s0, int64_t s1, uint8_t* xs) {
+  static __device__ __forceinline__ void load(Step<BITS>& t, const Cur& c, const uint16_t* X,
+                                              const uint32_t (&xlane)[kXP], int K, int lane) {
+#pragma unroll
+    for (int r = 0; r < kR; r++) {
+      const uint8_t* tp = c.wp + c.roff[r];
+      t.c[r] = __builtin_nontemporal_load(gload_ptr<u4_t>(tp + 16 * lane));
+      t.s[r] = __builtin_nontemporal_load(gload_ptr<u2_t>(tp + kScaleOff + 8 * (lane & 15)));
+      if constexpr (BITS == 5) t.h[r] = __builtin_nontemporal_load(gload_ptr<uint32_t>(tp + kHiOff + 4 * lane));
+    }
+    const uint8_t* xb = (const uint8_t*)X;
+    const int k0 = c.kt * kTileK;
+    if constexpr (kMfma) {
+      // group j of k tile kt: X[m][k0 + 32j + 8(l/16) ..]
+      if (k0 + kTileK <= K) {
+        const uint32_t o = xlane[0] + 2u * (uint32_t)k0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) t.x[j] = *gload_ptr<u4_t>(xb + (o + 64u * j));
+      } else {
+        const int kl = k0 + 8 * (lane >> 4);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int k = kl + 32 * j < K - 8 ? k0 + 32 * j : K - 8 - 8 * (lane >> 4);
+          t.x[j] = *gload_ptr<u4_t>(xb + (xlane[0] + 2u * (uint32_t)k));
+        }
+      }
+    } else {
+      // piece lane + 64p of the chunk: X[row][k0 + 8 col ..]
+      const int col = lane & 15;
+#pragma unroll
+      for (int p = 0; p < kXP; p++) {
+        if (k0 + kTileK <= K) {
+          t.x[p] = *gload_ptr<u4_t>(xb + (xlane[p] + 2u * (uint32_t)k0));
+        } else {
+          const int k = k0 + 8 * col < K - 8 ? k0 : K - 8 - 8 * col;
+          t.x[p] = *gload_ptr<u4_t>(xb + (xlane[p] + 2u * (uint32_t)k));
+        }
+      }
+    }
+  }
+
+  template <int BITS>
+  static __device__ __forceinline__ void compute(float (&acc)[kR][kA], const Step<BITS>& t, uint8_t* xs,
+                                                 int lane) {
+    if constexpr (kMfma) {
+      const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < kR; r++) {
+        f4_t p[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const h8_t q = unpack_chunk<BITS>(t.c[r][j], t.h[BITS == 5 ? r : 0], j);
+          p[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, t.x[j]), q, zero, 0, 0, 0);
+        }
+        const h2_t s01 = scale_pair(t.s[r].x), s23 = scale_pair(t.s[r].y);
+        const _Float16 sh[4] = {s01.x, s01.y, s23.x, s23.y};
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+          for (int i = 0; i < kA; i++) acc[r][i] = __builtin_fmaf((float)sh[j], p[j][i], acc[r][i]);
+      }
+    } else {
+      const int c = lane >> 4;
+#pragma unroll
+      for (int p = 0; p < kXP; p++) {
+        const int piece = lane + 64 * p;
+        const int row = piece >> 4, col = piece & 15;
+        if (row < kCap) *(u4_t*)(xs + row * kXRowBytes + 16 * col) = t.x[p];
+      }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);  // LDS writes stay before the reads
+#pragma unroll
+      for (int r = 0; r < kR; r++) {
+        const h2_t s01 = scale_pair(t.s[r].x), s23 = scale_pair(t.s[r].y);
+        const _Float16 sh[4] = {s01.x, s01.y, s23.x, s23.y};
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          h2_t q[4];
+          unpack8<BITS>(t.c[r][j], t.h[BITS == 5 ? r : 0], j, q);
+          const float sj = (float)sh[j];
+#pragma unroll
+          for (int m = 0; m < kCap; m++) {
+            const h8_t x = lds_h8(xs + m * kXRowBytes + 64 * j + 16 * c);
+            const h2_t x0 = {x[0], x[1]}, x1 = {x[2], x[3]}, x2 = {x[4], x[5]}, x3 = {x[6], x[7]};
+            float d = __builtin_amdgcn_fdot2(q[0], x0, 0.f, false);
+            d = __builtin_amdgcn_fdot2(q[1], x1, d, false);
+            d = __builtin_amdgcn_fdot2(q[2], x2, d, false);
+            d = __builtin_amdgcn_fdot2(q[3], x3, d, false);
+            acc[r][m] = __builtin_fmaf(sj, d, acc[r][m]);
+          }
+        }
+      }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the next step's writes stay after these reads
+    }
+  }
+
+  static __device__ __forceinline__ void zero(float (&acc)[kR][kA]) {
+#pragma unroll
+    for (int r = 0; r < kR; r++)
+#pragma unroll
+      for (int i = 0; i < kA; i++) acc[r][i] = 0.f;
+  }
+
+  // Steps [s0, s1) of job j (local step index rg * NKT + kt), BITS fixed.
+  template <int BITS>
+  static __device__ __forceinline__ void segment(Ctx& cx, int j, int s0, int s1, uint8_t* xs) {
     const QG_CONST JobDesc* D = cx.D;
     const int lane = cx.lane;
     constexpr int TB = BITS == 4 ? kTile4 : kTile5;
-    const int nkt = D[j].nkt, ngroups = D[j].ngroups, M = D[j].M, K = D[j].K;
+    const int nkt = D[j].nkt, nrb = D[j].nrb, M = D[j].M, K = D[j].K;
     const int64_t ldx = D[j].ldx;
-    const uint8_t* packed = D[j].packed;
     const uint16_t* X = D[j].X;
-    const bool ragged_k = (ngroups & 3) != 0;
-    // consume cursor
-    int rb = (int)(s0 / nkt);
-    int kt = (int)(s0 - (int64_t)rb * nkt);
-    // prefetch cursor: stops at the segment's last tile (later loads re-read it)
-    int64_t ps = s0;
-    int pkt = kt;
-    const uint8_t* pw = packed + s0 * TB;
-    auto pf_advance = [&]() {
-      if (ps < s1 - 1) {
-        ps++;
-        pw += TB;
-        if (++pkt == nkt) pkt = 0;
+    const uint32_t rstride = (uint32_t)nkt * TB;
+    // lane byte offsets into X (fit 32 bits: host check)
+    uint32_t xlane[kXP];
+    if constexpr (kMfma) {
+      const int m = (lane & 15) < M ? (lane & 15) : M - 1;
+      xlane[0] = 2u * (uint32_t)(m * ldx + 8 * (lane >> 4));
+    } else {
+#pragma unroll
+      for (int p = 0; p < kXP; p++) {
+        const int piece = lane + 64 * p;
+        const int row = piece >> 4, m = row < M ? row : M - 1;
+        xlane[p] = 2u * (uint32_t)(m * ldx + 8 * (piece & 15));
       }
-    };
-    Regs buf[kDepth];
+    }
+    // consume cursor
+    int rg = s0 / nkt;
+    int kt = s0 - rg * nkt;
+    // prefetch cursor: stops at the segment's last step (later loads re-read it)
+    Cur pc;
+    pc.rg = rg;
+    pc.kt = kt;
+    pc.wp = D[j].packed + ((int64_t)rg * kR * nkt + kt) * TB;
+    set_rows(pc, nrb, rstride);
+    int pleft = s1 - s0 - 1;
+    Step<BITS> buf[kDepth];
 #pragma unroll
     for (int p = 0; p < kDepth; p++) {
-      load<BITS>(buf[p], pw, X, pkt * kTileK, lane, M, K, ldx);
-      pf_advance();
+      load<BITS>(buf[p], pc, X, xlane, K, lane);
+      if (pleft > 0) {
+        advance(pc, nkt, nrb, rstride, TB);
+        pleft--;
+      }
     }
-    Acc acc;
+    float acc[kR][kA];
     zero(acc);
-    const int64_t n = s1 - s0;
-    for (int64_t f = 0; f < n; f += kDepth) {
+    const int n = s1 - s0;
+    for (int f = 0; f < n; f += kDepth) {
 #pragma unroll
       for (int p = 0; p < kDepth; p++) {
         if (f + p < n) {
-          stage(buf[p], xs, lane);
-          __atomic_signal_fence(__ATOMIC_SEQ_CST);  // LDS writes stay before the reads
-          const int gleft = ngroups - 4 * kt;
-          if (!ragged_k || gleft >= 4) {
-            if constexpr (kMfma) mfma1_tile<BITS, kNF, false>(acc.mf, buf[p].w, xs, lane, 4);
-            else gemv1_tile<BITS, kCap, false>(acc.gv, buf[p].w, xs, lane, 4, M);
-          } else {
-            if constexpr (kMfma) mfma1_tile<BITS, kNF, true>(acc.mf, buf[p].w, xs, lane, gleft);
-            else gemv1_tile<BITS, kCap, true>(acc.gv, buf[p].w, xs, lane, gleft, M);
-          }
+          compute<BITS>(acc, buf[p], xs, lane);
           if (kt == nkt - 1 || f + p == n - 1) {
-            flush(acc, cx, j, rb);
+            flush(acc, cx, j, rg);
             zero(acc);
           }
           if (++kt == nkt) {
             kt = 0;
-            rb++;
+            rg++;
           }
         }
-        load<BITS>(buf[p], pw, X, pkt * kTileK, lane, M, K, ldx);
-        pf_advance();
+        load<BITS>(buf[p], pc, X, xlane, K, lane);
+        if (pleft > 0) {
+          advance(pc, nkt, nrb, rstride, TB);
+          pleft--;
+        }
       }
     }
   }
@@ -602,46 +772,60 @@ struct Stream {
     cx.D = job_table(args);
     cx.counters = args.counters;
     cx.slots = args.slots;
-    cx.T = args.total;
+    cx.q = args.q;
+    cx.rem = args.rem;
     cx.G = args.nwaves;
     cx.slot_rows = args.slot_rows;
     cx.lane = threadIdx.x & 63;
     // wave-uniform by construction; readfirstlane lets the compiler know it
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    cx.gw = (int64_t)blockIdx.x * kStreamWavesPerBlock + wave;
-    const int64_t T = args.total, G = args.nwaves;
-    cx.a = cx.gw * T / G;
-    cx.b = (cx.gw + 1) * T / G;
-    if (cx.gw >= G || cx.a >= cx.b) return;
+    cx.gw = (int)blockIdx.x * kStreamWavesPerBlock + wave;
+    if (cx.gw >= cx.G) return;
+    cx.a = start_of(cx.gw, cx.q, cx.rem);
+    cx.b = cx.a + cx.q + (cx.gw < cx.rem ? 1 : 0);
     cx.pend_j0 = cx.pend_j1 = -1;
-    cx.pend_rb0 = cx.pend_rb1 = 0;
+    cx.pend_rg0 = cx.pend_rg1 = 0;
+    // first job of the range: a bucket index into the uend list when the jobs
+    // come from a table, else a scan of the (at most 12) inline jobs
     int j = 0;
-    while (cx.a >= cx.D[j].tile_end) j++;
+    if (args.index) {
+      const QG_CONST int32_t* ends = (const QG_CONST int32_t*)args.index;
+      j = ends[args.njobs + (cx.a >> args.bshift)];
+      while (cx.a >= ends[j]) j++;
+    } else {
+      while (cx.a >= cx.D[j].uend) j++;
+    }
     // one segment per job the range touches
-    for (int64_t f = cx.a; f < cx.b; j++) {
-      const int64_t tb = cx.D[j].tile_begin;
-      const int64_t e = cx.D[j].tile_end < cx.b ? cx.D[j].tile_end : cx.b;
-      if (cx.D[j].bits == 4) segment<4>(cx, j, f - tb, e - tb, xs);
-      else segment<5>(cx, j, f - tb, e - tb, xs);
+    // one segment per job the range touches: the job's steps whose first
+    // unit lies in the range
+    for (int f = cx.a; f < cx.b; j++) {
+      const int ub = cx.D[j].ubeg;
+    static_assert(kTile4 / kTileK == 9 && kTile5 / kTileK == 11, "unit weights");
+      const int e = cx.D[j].uend < cx.b ? cx.D[j].uend : cx.b;
+      if (cx.D[j].bits == 4) {
+        const int s0 = (f - ub + 8) / 9, s1 = (e - ub + 8) / 9;
+        if (s0 < s1) segment<4>(cx, j, s0, s1, xs);
+      } else {
+        const int s0 = (f - ub + 10) / 11, s1 = (e - ub + 10) / 11;
+        if (s0 < s1) segment<5>(cx, j, s0, s1, xs);
+      }
       f = e;
     }
     if (cx.pend_j0 >= 0 || cx.pend_j1 >= 0) {
-      // every slot store of this wave must be complete before any arrival
+      // every slot store of this wave must be complete before any arrival;
+      // both arrivals are counted before either result is waited for
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_s_waitcnt(0);
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      if (cx.pend_j0 >= 0) arrive(cx, cx.pend_j0, cx.pend_rb0);
-      if (cx.pend_j1 >= 0) arrive(cx, cx.pend_j1, cx.pend_rb1);
+      arrive(cx);
     }
   }
 };
 
-// At least 4 waves per SIMD: 16 per CU keep every wave of the grid resident.
 template <bool kMfma, int kCap>
-__global__ void __launch_bounds__(64 * kStreamWavesPerBlock) __attribute__((amdgpu_waves_per_eu(4)))
-stream_kernel(SweepArgs args) {
+__global__ void __launch_bounds__(64 * kStreamWavesPerBlock) stream_kernel(SweepArgs args) {
   using S = Stream<kMfma, kCap>;
-  __shared__ __attribute__((aligned(16))) uint8_t xs[kStreamWavesPerBlock][S::kRows * kXRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kStreamWavesPerBlock][kMfma ? 16 : kCap * kXRowBytes];
   S::run(args, xs[threadIdx.x >> 6]);
 }
 
@@ -728,10 +912,10 @@ __global__ void __launch_bounds__(64 * kGroupWaves) group_kernel(SweepArgs args)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int j = 0;
-  for (int64_t u = blockIdx.x; u < args.total; u += gridDim.x) {
-    while (u >= D[j].unit_end) j++;
+  for (int u = blockIdx.x; u < args.total; u += gridDim.x) {
+    while (u >= D[j].grp_end) j++;
     const JobDesc d = D[j];
-    const int rb = (int)(u - d.unit_begin) * kGroupWaves + wave;
+    const int rb = (u - d.grp_begin) * kGroupWaves + wave;
     f4_t acc[S::kMb];
 #pragma unroll
     for (int mb = 0; mb < S::kMb; mb++) acc[mb] = f4_t{0.f, 0.f, 0.f, 0.f};
