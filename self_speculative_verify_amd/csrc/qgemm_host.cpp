@@ -189,7 +189,17 @@ int64_t stream_waves(const std::vector<JobDesc>& descs, int64_t T) {
 
 Plan make_plan(const qgemm_job* jobs, int njobs, int path) {
   Plan P;
-  for (int i = 0; i < njobs; i++) {
+  // Jobs of the group kernel go longest K first (their units are whole-K,
+  // so the long ones are dealt out before the short ones fill the gaps);
+  // stream jobs keep the caller's order.
+  std::vector<int> order(njobs);
+  for (int i = 0; i < njobs; i++) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+    const bool ga = kind_of(path, jobs[a].M) == kGroupMfma, gb = kind_of(path, jobs[b].M) == kGroupMfma;
+    if (ga != gb) return gb;  // stream jobs first, in order
+    return ga && jobs[a].K > jobs[b].K;
+  });
+  for (int i : order) {
     const qgemm_job& j = jobs[i];
     const int kind = kind_of(path, j.M);
     const int cls = class_of(kind, j.M);
@@ -217,7 +227,8 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path) {
     d.ngroups = (int32_t)(j.K / qg::kGroup);
     d.nrb = (int32_t)nrb_of(j.N);
     if (kind == kGroupMfma) {
-      const int64_t groups = (d.nrb + qg::kGroupWaves - 1) / qg::kGroupWaves;
+      const int64_t per = (int64_t)qg::group_waves(cls) * qg::kGroupRows;
+      const int64_t groups = (d.nrb + per - 1) / per;
       d.grp_begin = (int32_t)dst->total;
       dst->total += groups;
       d.grp_end = (int32_t)std::min(dst->total, kMaxSteps);

@@ -24,8 +24,10 @@ constexpr int kXRowBytes = 272;      // LDS row stride of a staged X chunk (256 
 constexpr int kStreamWavesPerBlock = 4;
 constexpr int kStreamMinWaves = 1024;
 constexpr int kStreamWaves = 1024;
-// group kernel (17..64 rows): waves per workgroup, one 16-row block each
-constexpr int kGroupWaves = 8;
+// group kernel (17..64 rows): waves per workgroup (three per SIMD where the
+// registers allow it: padded rows 32 and 48), 16-row blocks per wave
+constexpr int group_waves(int mpad) { return mpad >= 64 ? 8 : 12; }
+constexpr int kGroupRows = 2;
 
 // Stream kernels walk "steps": one k tile of a row group of kStreamRows
 // consecutive 16-row blocks.  The same for every class of a path, so the K

@@ -222,35 +222,6 @@ __device__ __forceinline__ h8_t unpack_chunk(uint32_t w, uint32_t hi, int J) {
   return cat8(q);
 }
 
-// The weight part of one k tile as seen by lane l = r + 16c: its 16 code
-// bytes (chunk c of the tile's four groups of row r), the four fp16 scales of
-// row r, and (5-bit) the 32 high bits of its codes.
-struct WRegs {
-  u4_t wc;
-  u2_t ws;
-  uint32_t wh;
-};
-
-// Every tile issues the same three loads whatever its bit width (a 4-bit tile
-// re-reads a word of its own scale block in place of the high bits), so the
-// compiler can count outstanding loads exactly and never has to drain them.
-__device__ __forceinline__ void load_w(WRegs& t, const uint8_t* tile, int bits, int lane) {
-  t.wc = __builtin_nontemporal_load(gload_ptr<u4_t>(tile + 16 * lane));
-  t.ws = __builtin_nontemporal_load(gload_ptr<u2_t>(tile + kScaleOff + 8 * (lane & 15)));
-  const int hoff = bits == 5 ? kHiOff + 4 * lane : kScaleOff + 4 * (lane & 31);
-  t.wh = __builtin_nontemporal_load(gload_ptr<uint32_t>(tile + hoff));  // unused when 4-bit
-}
-
-// One 16-byte piece of an X chunk.  Outside [0,M) x [0,K) it reads row 0, k 0
-// (always valid) and the value is never used: rows m >= M only feed output
-// rows that are not stored (MFMA rows are independent) and k >= K lies in
-// groups the tile loop skips.  No select on the loaded value, so the load
-// need not complete before the next ones are issued.
-__device__ __forceinline__ u4_t load_x_piece(const uint16_t* X, int64_t ldx, int row, int k, int M, int K) {
-  const bool ok = row < M && k < K;
-  return *gload_ptr<u4_t>(X + (ok ? (int64_t)row * ldx + k : 0));
-}
-
 // X chunks are written to and read from LDS as the same 16-byte integer
 // vector type (then bit-cast), so type-based alias analysis can never move a
 // read above the write that produced it.
@@ -260,33 +231,6 @@ __device__ __forceinline__ h8_t lds_h8(const uint8_t* p) { return __builtin_bit_
 // bit_cast applied directly to an element of a vector register type was
 // compiled to an undefined value (only element 0 survived).
 __device__ __forceinline__ h2_t scale_pair(uint32_t word) { return __builtin_bit_cast(h2_t, word); }
-
-// MFMA:  v_mfma_f32_16x16x32_f16, A = X (16 rows m x 32 k of one group),
-//        B = codes (32 k x 16 rows n).  Lane l holds for A row m = l%16 and for
-//        B row n = l%16, both k chunk l/16 of the same group; D lane l holds
-//        (n = l%16, m = 4*(l/16) + i).  The group's fp32 scale multiplies the
-//        16x16 partial before it is added to the accumulator.
-template <int BITS, int MB>
-__device__ __forceinline__ void mfma_tile(f4_t (&acc)[MB], const WRegs& w, const uint8_t* xs, int lane,
-                                          int gleft) {
-  const int r = lane & 15, c = lane >> 4;
-  const h2_t s01 = scale_pair(w.ws.x), s23 = scale_pair(w.ws.y);
-  const float sc[4] = {(float)s01.x, (float)s01.y, (float)s23.x, (float)s23.y};
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    if (j < gleft) {
-      const h8_t q = unpack_chunk<BITS>(w.wc[j], w.wh, j);
-      const f4_t zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int mb = 0; mb < MB; mb++) {
-        const h8_t a = lds_h8(xs + (16 * mb + r) * kXRowBytes + 64 * j + 16 * c);
-        const f4_t p = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, q, zero, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; i++) acc[mb][i] = __builtin_fmaf(sc[j], p[i], acc[mb][i]);
-      }
-    }
-  }
-}
 
 __device__ __forceinline__ const QG_CONST JobDesc* job_table(const SweepArgs& a) {
   return a.table ? (const QG_CONST JobDesc*)a.table : (const QG_CONST JobDesc*)&a.inl[0];
@@ -832,106 +776,163 @@ __global__ void __launch_bounds__(64 * kStreamWavesPerBlock) stream_kernel(Sweep
 // --------------------------------------------------------------------------
 // group kernel: panels of 17..64 rows (MFMA, 2..4 m blocks)
 // --------------------------------------------------------------------------
-// One workgroup of kGroupWaves waves per unit = (job, kGroupWaves row blocks),
-// whole K.  Wave w owns row block kGroupWaves*g + w; the X chunk of each k tile
-// is staged once in LDS for all waves (double buffered) and loaded kDepth tiles
-// ahead together with the weight tiles.
+// One workgroup of kW waves per unit = (job, kW * kRG row
+// blocks), whole K: no K split, so no partial sums cross waves.  The waves
+// walk the k tiles in lockstep.  The X chunk of a k tile (kMPad rows x 128 k)
+// is staged once in LDS for the workgroup (double buffered, one barrier per
+// k tile); each wave reads its MFMA A fragments for the tile once and applies
+// them to its kRG row blocks, so LDS traffic per weight byte falls kRG-fold.
+// Weight tiles are loaded kDepth k tiles ahead.  Units are handed out in job
+// order with a stride of the grid; the host orders jobs longest K first.
 template <int kMPad>
 struct Group {
+  static constexpr int kW = group_waves(kMPad);
   static constexpr int kMb = kMPad / 16;
-  static constexpr int kThreads = 64 * kGroupWaves;
-  static constexpr int kPieces = (kMPad * 16 + kThreads - 1) / kThreads;
-  static constexpr int kDepth = 3;
+  static constexpr int kThreads = 64 * kW;
+  static constexpr int kRG = kGroupRows;                             // row blocks per wave
+  static constexpr int kXP = (kMPad * 16 + kThreads - 1) / kThreads;  // 16-byte X pieces per thread
+  static constexpr int kDepth = 4;
 
-  struct Regs {
-    WRegs w;
-    u4_t x[kPieces];
+  template <int BITS>
+  struct Tiles {
+    u4_t c[kRG];
+    u2_t s[kRG];
+    uint32_t h[BITS == 5 ? kRG : 1];
   };
 
-  // Waves whose row block lies past N read row block 0 and discard it, so
-  // every wave issues the same loads.
-  static __device__ __forceinline__ void load(Regs& t, const JobDesc& d, const uint8_t* wtile, int kt, int tid) {
-    const int lane = tid & 63;
-    load_w(t.w, wtile, d.bits, lane);
+  // X piece p of thread tid for k tile kt: row min(row, M-1), k clamped into
+  // the row (padding groups then add exact zeros: their codes are 0).
+  static __device__ __forceinline__ void load_x(u4_t (&x)[kXP], const JobDesc& d, int kt, int tid) {
 #pragma unroll
-    for (int p = 0; p < kPieces; p++) {
+    for (int p = 0; p < kXP; p++) {
       const int piece = tid + kThreads * p;
       const int row = piece >> 4, col = piece & 15;
-      t.x[p] = load_x_piece(d.X, d.ldx, row, kt * kTileK + 8 * col, d.M, d.K);
+      const int m = row < d.M ? row : d.M - 1;
+      const int kk = kt * kTileK + 8 * col;
+      const int k = kk < d.K - 8 ? kk : d.K - 8;
+      x[p] = *gload_ptr<u4_t>(d.X + (int64_t)m * d.ldx + k);
     }
   }
 
-  static __device__ __forceinline__ void stage(const Regs& t, uint8_t* xs, int tid) {
+  static __device__ __forceinline__ void store_x(const u4_t (&x)[kXP], uint8_t* xs, int tid) {
 #pragma unroll
-    for (int p = 0; p < kPieces; p++) {
+    for (int p = 0; p < kXP; p++) {
       const int piece = tid + kThreads * p;
       const int row = piece >> 4, col = piece & 15;
-      if (row < kMPad) *(u4_t*)(xs + row * kXRowBytes + 16 * col) = t.x[p];
+      if (row < kMPad) *(u4_t*)(xs + row * kXRowBytes + 16 * col) = x[p];
     }
   }
 
   template <int BITS>
-  static __device__ void run_unit(f4_t (&acc)[kMb], const JobDesc& d, int rb,
-                                  uint8_t (*xs)[kMPad * kXRowBytes], int tid) {
-    const bool rb_ok = rb < d.nrb;
-    constexpr int tb = BITS == 4 ? kTile4 : kTile5;
-    const uint8_t* wbase = d.packed + (int64_t)(rb_ok ? rb : 0) * d.nkt * tb;
-    const int nkt = d.nkt;
-    // prefetch runs kDepth tiles ahead and re-reads the last tile at the end
-    Regs buf[kDepth];
+  static __device__ __forceinline__ void load_w(Tiles<BITS>& t, const uint8_t* w0, int64_t rstride,
+                                                int nrows, int lane) {
 #pragma unroll
-    for (int p = 0; p < kDepth; p++) {
-      const int lt = p < nkt ? p : nkt - 1;
-      load(buf[p], d, wbase + (int64_t)lt * tb, lt, tid);
+    for (int r = 0; r < kRG; r++) {
+      const uint8_t* tp = w0 + (int64_t)(r < nrows ? r : nrows - 1) * rstride;
+      t.c[r] = __builtin_nontemporal_load(gload_ptr<u4_t>(tp + 16 * lane));
+      t.s[r] = __builtin_nontemporal_load(gload_ptr<u2_t>(tp + kScaleOff + 8 * (lane & 15)));
+      if constexpr (BITS == 5) t.h[r] = __builtin_nontemporal_load(gload_ptr<uint32_t>(tp + kHiOff + 4 * lane));
     }
-    int parity = 0;
-    for (int kt = 0; kt < nkt; kt += kDepth) {
+  }
+
+  // One unit: row blocks rb0 + kRG * wave + r (r < kRG) of job d, all k tiles.
+  template <int BITS>
+  static __device__ void run_unit(const JobDesc& d, int rb0, uint8_t (*xs)[kMPad * kXRowBytes], int tid) {
+    constexpr int TB = BITS == 4 ? kTile4 : kTile5;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int nkt = d.nkt;
+    const int64_t rstride = (int64_t)nkt * TB;
+    const int rbw = rb0 + kRG * wave;                  // this wave's first row block
+    const int nrows = d.nrb - rbw;                     // valid row blocks (may be <= 0)
+    const int rbl = nrows > 0 ? rbw : d.nrb - 1;       // waves past the job re-read its last block
+    const int nr = nrows > 0 ? nrows : 1;
+    const uint8_t* wbase = d.packed + (int64_t)rbl * rstride;
+    // prologue: X chunks 0 (to LDS) and 1 (staged), weights of k tiles 0..kDepth-1
+    u4_t xst[kXP];
+    load_x(xst, d, 0, tid);
+    store_x(xst, xs[0], tid);
+    load_x(xst, d, nkt > 1 ? 1 : 0, tid);
+    Tiles<BITS> buf[kDepth];
+#pragma unroll
+    for (int p = 0; p < kDepth; p++) load_w<BITS>(buf[p], wbase + (int64_t)(p < nkt ? p : nkt - 1) * TB, rstride, nr, lane);
+    f4_t acc[kRG][kMb];
+#pragma unroll
+    for (int r = 0; r < kRG; r++)
+#pragma unroll
+      for (int mb = 0; mb < kMb; mb++) acc[r][mb] = f4_t{0.f, 0.f, 0.f, 0.f};
+    const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+    const int mr = lane & 15, c = lane >> 4;
+    for (int kt0 = 0; kt0 < nkt; kt0 += kDepth) {
 #pragma unroll
       for (int p = 0; p < kDepth; p++) {
-        const int t = kt + p;
-        if (t < nkt) {
-          uint8_t* xb = xs[parity];
-          stage(buf[p], xb, tid);
+        const int kt = kt0 + p;
+        if (kt < nkt) {
+          // chunk kt is in xs[kt & 1]; every wave is done with xs[(kt + 1) & 1]
           __syncthreads();
-          if (rb_ok) mfma_tile<BITS, kMb>(acc, buf[p].w, xb, tid & 63, d.ngroups - 4 * t);
-          parity ^= 1;
+          store_x(xst, xs[(kt + 1) & 1], tid);
+          load_x(xst, d, kt + 2 < nkt ? kt + 2 : nkt - 1, tid);
+          const uint8_t* xb = xs[kt & 1];
+          // group by group: the A fragments of group j serve all kRG row blocks
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            h8_t a[kMb];
+#pragma unroll
+            for (int mb = 0; mb < kMb; mb++) a[mb] = lds_h8(xb + (16 * mb + mr) * kXRowBytes + 64 * j + 16 * c);
+            // every MFMA of the group is issued before the first of its
+            // results is scaled, so the matrix-core latency overlaps
+            f4_t pr[kRG][kMb];
+#pragma unroll
+            for (int r = 0; r < kRG; r++) {
+              const h8_t q = unpack_chunk<BITS>(buf[p].c[r][j], buf[p].h[BITS == 5 ? r : 0], j);
+#pragma unroll
+              for (int mb = 0; mb < kMb; mb++) pr[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb], q, zero, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < kRG; r++) {
+              const float sj = (float)scale_pair(j < 2 ? buf[p].s[r].x : buf[p].s[r].y)[j & 1];
+#pragma unroll
+              for (int mb = 0; mb < kMb; mb++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) acc[r][mb][i] = __builtin_fmaf(sj, pr[r][mb][i], acc[r][mb][i]);
+            }
+          }
         }
-        const int lt = t + kDepth < nkt ? t + kDepth : nkt - 1;
-        load(buf[p], d, wbase + (int64_t)lt * tb, lt, tid);
+        const int lt = kt + kDepth < nkt ? kt + kDepth : nkt - 1;
+        load_w<BITS>(buf[p], wbase + (int64_t)lt * TB, rstride, nr, lane);
       }
     }
     __syncthreads();  // both X buffers are free again
+    if (nrows <= 0) return;
+    QG_GLOBAL float* Y = (QG_GLOBAL float*)d.Y;
+#pragma unroll
+    for (int r = 0; r < kRG; r++) {
+      const int n = (rbw + r) * kTileRows + mr;
+      if (r < nrows && n < d.N) {
+#pragma unroll
+        for (int mb = 0; mb < kMb; mb++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int m = 16 * mb + 4 * c + i;
+            if (m < d.M) Y[(int64_t)m * d.ldy + n] = acc[r][mb][i];
+          }
+      }
+    }
   }
 };
 
 template <int kMPad>
-__global__ void __launch_bounds__(64 * kGroupWaves) group_kernel(SweepArgs args) {
+__global__ void __launch_bounds__(64 * group_waves(kMPad)) group_kernel(SweepArgs args) {
   using S = Group<kMPad>;
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][kMPad * kXRowBytes];
   const QG_CONST JobDesc* D = job_table(args);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tid = threadIdx.x;
   int j = 0;
   for (int u = blockIdx.x; u < args.total; u += gridDim.x) {
     while (u >= D[j].grp_end) j++;
     const JobDesc d = D[j];
-    const int rb = (u - d.grp_begin) * kGroupWaves + wave;
-    f4_t acc[S::kMb];
-#pragma unroll
-    for (int mb = 0; mb < S::kMb; mb++) acc[mb] = f4_t{0.f, 0.f, 0.f, 0.f};
-    if (d.bits == 4) S::template run_unit<4>(acc, d, rb, xs, tid);
-    else S::template run_unit<5>(acc, d, rb, xs, tid);
-    const int n = rb * kTileRows + (lane & 15);
-    if (rb < d.nrb && n < d.N) {
-      QG_GLOBAL float* Y = (QG_GLOBAL float*)d.Y;
-#pragma unroll
-      for (int mb = 0; mb < S::kMb; mb++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const int m = 16 * mb + 4 * (lane >> 4) + i;
-          if (m < d.M) Y[(int64_t)m * d.ldy + n] = acc[mb][i];
-        }
-    }
+    const int rb0 = (u - d.grp_begin) * S::kW * kGroupRows;
+    if (d.bits == 4) S::template run_unit<4>(d, rb0, xs, tid);
+    else S::template run_unit<5>(d, rb0, xs, tid);
   }
 }
 
@@ -997,13 +998,13 @@ static sweep_fn pick(int kind, int cls) {
   return nullptr;
 }
 
-int sweep_threads(int kind) { return kind == 2 ? 64 * kGroupWaves : 64 * kStreamWavesPerBlock; }
+int sweep_threads(int kind, int cls) { return kind == 2 ? 64 * group_waves(cls) : 64 * kStreamWavesPerBlock; }
 
 int sweep_blocks_per_cu(int kind, int cls) {
   sweep_fn f = pick(kind, cls);
   if (!f) return 0;
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void*)f, sweep_threads(kind), 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void*)f, sweep_threads(kind, cls), 0) != hipSuccess)
     return 0;
   return nb;
 }
@@ -1011,7 +1012,7 @@ int sweep_blocks_per_cu(int kind, int cls) {
 hipError_t launch_sweep(int kind, int cls, const SweepArgs& args, int grid, hipStream_t stream) {
   sweep_fn f = pick(kind, cls);
   if (!f) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(f, dim3(grid), dim3(sweep_threads(kind)), 0, stream, args);
+  hipLaunchKernelGGL(f, dim3(grid), dim3(sweep_threads(kind, cls)), 0, stream, args);
   return hipGetLastError();
 }
 
