@@ -14,6 +14,8 @@ streams its weights from HBM.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only 2|3|4]
        [--no-cpu] [--stack-layers L]
+       python bench.py --copy-calib MIB   (a plain device copy of MIB MiB, the
+       reference for scaling the HBM byte counters)
 """
 from __future__ import annotations
 
@@ -27,6 +29,27 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+
+# HBM bytes per launch of the headline sweep kernel, from rocprofv3 FETCH_SIZE
+# and WRITE_SIZE runs scaled by the same counters on a plain copy (profiles/
+# has the commands and raw figures).  Valid only for the kernel sources they
+# were taken on: keyed by the SHA-256 of those sources, else reported as null.
+TRAFFIC = {
+    "2cb8c0b5c22649bd": {"workload": "gate+up 5120->34816 4-bit M=1", "bytes": 105898581},
+}
+KERNEL_SOURCES = ("self_speculative_verify_amd/csrc/qgemm_kernels.hip",
+                  "self_speculative_verify_amd/csrc/qgemm_internal.h",
+                  "self_speculative_verify_amd/csrc/qgemm_host.cpp")
+
+
+def kernel_sha():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 METRIC = "weight GB/s (% of HBM peak) + verify tokens/s per sweep at M=1,6,48"
 
 
@@ -157,6 +180,7 @@ def main():
     ap.add_argument("--only", type=int, default=0, help="time one workload (2, 3 or 4) only")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--stack-layers", type=int, default=64)
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the sweep shards "
@@ -171,6 +195,18 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+
+    if args.copy_calib:
+        # one device-to-device copy kernel per step: reads and writes exactly
+        # n bytes each, the yardstick for the byte counters
+        n = args.copy_calib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
+        return
 
     results = {}
     order = [args.only] if args.only else [2, 3, 4]
@@ -197,6 +233,9 @@ def main():
         "frac": round(head["alg_GBps"] / HBM_PEAK_GBPS, 4),
         "traffic": None,
     }
+    tr = TRAFFIC.get(kernel_sha())
+    if tr and head["workload"] == tr["workload"]:
+        roof["traffic"] = tr["bytes"]
     line = {
         "metric": METRIC,
         "value": head["weight_GBps"],

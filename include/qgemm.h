@@ -49,6 +49,9 @@
  * matrices in a sweep it is bitwise the same for any other rows and any M of
  * one panel class -- GEMV M <= 8; MFMA M <= 16; MFMA 17 <= M <= 64 -- and
  * within the tolerance above across classes.  Repeated calls are bitwise equal.
+ * A non-finite X entry makes its row's outputs non-finite (Inf or NaN is not
+ * specified).  A sweep whose work exceeds the kernels' 32-bit ranges (about
+ * 2^31 / 9 k tiles of 16-row blocks per launch) returns QGEMM_ERR_UNSUPPORTED.
  * ---------------------------------------------------------------------------
  */
 #ifndef QGEMM_H
@@ -69,8 +72,10 @@ typedef enum {
   QGEMM_ERR_HIP = 4           /* a HIP runtime call or launch failed */
 } qgemm_status;
 
-/* Which contraction a sweep uses.  AUTO picks by M (GEMV for small M, MFMA
- * otherwise).  GEMV accepts M <= QGEMM_GEMV_MAX_M; MFMA accepts any M. */
+/* Which contraction a sweep uses.  AUTO takes MFMA at every M: on gfx950 it
+ * is as fast as GEMV at M = 1 and faster above, and it keeps an M = 1 row
+ * bitwise equal to the same row in any panel of up to 16 rows.  GEMV (per-lane
+ * dot products) accepts M <= QGEMM_GEMV_MAX_M; MFMA accepts any M. */
 typedef enum {
   QGEMM_PATH_AUTO = 0,
   QGEMM_PATH_GEMV = 1,

@@ -46,8 +46,7 @@ def test_packed_bytes_agrees_with_oracle():
 
 def test_auto_path_table():
     for M in range(1, 65):
-        want = qgemm.PATH_GEMV if M <= 4 else qgemm.PATH_MFMA
-        assert qgemm.auto_path(M) == want
+        assert qgemm.auto_path(M) == qgemm.PATH_MFMA
     assert qgemm.auto_path(0) == -1 and qgemm.auto_path(65) == -1
 
 
