@@ -232,6 +232,18 @@ __device__ __forceinline__ h8_t lds_h8(const uint8_t* p) { return __builtin_bit_
 // compiled to an undefined value (only element 0 survived).
 __device__ __forceinline__ h2_t scale_pair(uint32_t word) { return __builtin_bit_cast(h2_t, word); }
 
+// One fp16 scale of a packed pair to fp32 as an instruction of its own, so the
+// scale products that follow are two-operand fp32 FMAs; left to itself the
+// compiler fuses the conversion into mixed-precision FMAs, which issue more
+// slowly on gfx950.
+template <int HI>
+__device__ __forceinline__ float scale_f32(uint32_t pair) {
+  float f;
+  if constexpr (HI) asm("v_cvt_f32_f16_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1" : "=v"(f) : "v"(pair));
+  else asm("v_cvt_f32_f16_e32 %0, %1" : "=v"(f) : "v"(pair));
+  return f;
+}
+
 __device__ __forceinline__ const QG_CONST JobDesc* job_table(const SweepArgs& a) {
   return a.table ? (const QG_CONST JobDesc*)a.table : (const QG_CONST JobDesc*)&a.inl[0];
 }
@@ -296,6 +308,14 @@ struct Stream {
     const int left = nrb - 1 - c.rg * kR;  // >= 0
 #pragma unroll
     for (int r = 0; r < kR; r++) c.roff[r] = (uint32_t)(r < left ? r : left) * rstride;
+  }
+
+  // Redirect a finished prefetch cursor to base (its loads are never used).
+  static __device__ __forceinline__ void spill_to(Cur& c, const uint8_t* base) {
+    if (base == nullptr) return;
+    c.wp = base;
+#pragma unroll
+    for (int r = 0; r < kR; r++) c.roff[r] = 0;
   }
 
   static __device__ __forceinline__ void advance(Cur& c, int nkt, int nrb, uint32_t rstride, uint32_t tb) {
@@ -676,6 +696,11 @@ struct Stream {
     pc.wp = D[j].packed + ((int64_t)rg * kR * nkt + kt) * TB;
     set_rows(pc, nrb, rstride);
     int pleft = s1 - s0 - 1;
+    // Past the segment's last step the prefetch keeps issuing its fixed
+    // number of loads (so the compiler's wait counts stay exact) but points
+    // them at X, which every wave keeps reading and so stays cached, instead
+    // of fetching weights again; X smaller than a tile: the last step.
+    const uint8_t* xover = 2 * ((int64_t)(M - 1) * ldx + K) >= kTile5 ? (const uint8_t*)X : nullptr;
     Step<BITS> buf[kDepth];
 #pragma unroll
     for (int p = 0; p < kDepth; p++) {
@@ -683,6 +708,8 @@ struct Stream {
       if (pleft > 0) {
         advance(pc, nkt, nrb, rstride, TB);
         pleft--;
+      } else {
+        spill_to(pc, xover);
       }
     }
     float acc[kR][kA];
@@ -706,6 +733,8 @@ struct Stream {
         if (pleft > 0) {
           advance(pc, nkt, nrb, rstride, TB);
           pleft--;
+        } else {
+          spill_to(pc, xover);
         }
       }
     }
@@ -776,50 +805,84 @@ __global__ void __launch_bounds__(64 * kStreamWavesPerBlock) stream_kernel(Sweep
 // --------------------------------------------------------------------------
 // group kernel: panels of 17..64 rows (MFMA, 2..4 m blocks)
 // --------------------------------------------------------------------------
-// One workgroup of kW waves per unit = (job, kW * kRG row
-// blocks), whole K: no K split, so no partial sums cross waves.  The waves
-// walk the k tiles in lockstep.  The X chunk of a k tile (kMPad rows x 128 k)
-// is staged once in LDS for the workgroup (double buffered, one barrier per
-// k tile); each wave reads its MFMA A fragments for the tile once and applies
-// them to its kRG row blocks, so LDS traffic per weight byte falls kRG-fold.
-// Weight tiles are loaded kDepth k tiles ahead.  Units are handed out in job
-// order with a stride of the grid; the host orders jobs longest K first.
+// One workgroup of kW waves per unit = (job, kW * kRG row blocks), whole K:
+// no K split, so no partial sums cross waves.  The waves walk the k tiles in
+// lockstep, one barrier per k tile.  The X chunk of a k tile (kMPad rows x 128
+// k) is copied once per workgroup straight from memory into LDS (direct-to-LDS
+// loads, no registers), into a ring of kDepth + 1 buffers; each wave reads its
+// MFMA A fragments for the tile once and applies them to its kRG row blocks,
+// so LDS traffic per weight byte falls kRG-fold.  The X copy of tile t is
+// issued just before the weight loads of tile t, kDepth tiles ahead, so
+// waiting for it never waits on a younger weight load.  Units are handed out
+// in job order with a stride of the grid; the host orders jobs longest K first.
+//
+// LDS layout of one buffer: 16-byte slot s (X chunk col' of row s / 16,
+// col' = s mod 16) holds X[row][8 col .. 8 col + 7] of the k tile with col =
+// col' XOR (row mod 16), so the 16 rows an A-fragment read touches fall on
+// distinct banks.  Slots past kMPad rows are a landing area for the copies of
+// waves with no rows left (every wave issues the same number of copies, which
+// keeps the wait counts exact).
+// Global memory straight into LDS: 16 (or 4) bytes per lane at dst + 16 *
+// lane (dst + 4 * lane); dst is wave-uniform and goes to M0.  Written as
+// assembly so the compiler neither tracks nor waits for these copies: the
+// group kernel covers them with its own explicit waits (a copy issued before a
+// load has completed once that load has).  The compiler's wait counts for its
+// own loads are then only ever too strict.  The nop covers the M0-write hazard
+// of LDS-direct loads.
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(dst)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy4(const void* src, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off nt" ::"v"(src), "s"(dst)
+               : "memory", "m0");
+}
+
 template <int kMPad>
 struct Group {
   static constexpr int kW = group_waves(kMPad);
   static constexpr int kMb = kMPad / 16;
   static constexpr int kThreads = 64 * kW;
   static constexpr int kRG = kGroupRows;                             // row blocks per wave
-  static constexpr int kXP = (kMPad * 16 + kThreads - 1) / kThreads;  // 16-byte X pieces per thread
-  static constexpr int kDepth = 4;
+  static_assert(kRG == 2, "one 64-lane scale copy holds the scales of two row blocks");
+  static constexpr int kDepth = 4;                                    // code prefetch distance, k tiles
+  static constexpr int kBufs = kDepth;                                // ring of k-tile buffers in LDS:
+                                                                      // X and scales go kDepth - 1 ahead
+  static constexpr int kND = (kMPad * 16 + kThreads - 1) / kThreads;  // X copies per wave and k tile
+  static constexpr int kXBytes = kND * kThreads * 16;                 // X area of a buffer
+  static constexpr int kBufBytes = kXBytes + kW * 256;                // then 256 scale bytes per wave
+  static constexpr int kYRow = kRG * kTileRows;                       // outputs n of a wave
+  static_assert(kND * kThreads >= kMPad * 16, "X copies cover the panel");
+  static constexpr int kYBytes = kW * kMPad * kYRow * 4;             // output staging (reuses the ring)
+  static constexpr int kLdsBytes = kBufs * kBufBytes > kYBytes ? kBufs * kBufBytes : kYBytes;
 
   template <int BITS>
   struct Tiles {
     u4_t c[kRG];
-    u2_t s[kRG];
     uint32_t h[BITS == 5 ? kRG : 1];
   };
+  // vector memory instructions of one k tile per wave: X copies, the scale
+  // copy, then the weight loads
+  template <int BITS>
+  static constexpr int kLoadsW = kRG * (BITS == 5 ? 2 : 1);
+  template <int BITS>
+  static constexpr int kLoadsTile = kND + 1 + kLoadsW<BITS>;
 
-  // X piece p of thread tid for k tile kt: row min(row, M-1), k clamped into
-  // the row (padding groups then add exact zeros: their codes are 0).
-  static __device__ __forceinline__ void load_x(u4_t (&x)[kXP], const JobDesc& d, int kt, int tid) {
+  // Direct-to-LDS copy of this wave's X slots of k tile kt (clamped to the
+  // last) into the buffer at LDS address buf.  Slot rows past M repeat row
+  // M-1 and k is clamped into the row (padding groups then add exact zeros:
+  // their codes are 0).
+  static __device__ __forceinline__ void copy_x(const JobDesc& d, int kt, uint32_t buf, int wave, int lane) {
+    kt = kt < d.nkt ? kt : d.nkt - 1;
 #pragma unroll
-    for (int p = 0; p < kXP; p++) {
-      const int piece = tid + kThreads * p;
-      const int row = piece >> 4, col = piece & 15;
+    for (int i = 0; i < kND; i++) {
+      const int s = 64 * (wave * kND + i) + lane;
+      const int row = s >> 4;
+      const int col = (s & 15) ^ (row & 15);
       const int m = row < d.M ? row : d.M - 1;
       const int kk = kt * kTileK + 8 * col;
       const int k = kk < d.K - 8 ? kk : d.K - 8;
-      x[p] = *gload_ptr<u4_t>(d.X + (int64_t)m * d.ldx + k);
-    }
-  }
-
-  static __device__ __forceinline__ void store_x(const u4_t (&x)[kXP], uint8_t* xs, int tid) {
-#pragma unroll
-    for (int p = 0; p < kXP; p++) {
-      const int piece = tid + kThreads * p;
-      const int row = piece >> 4, col = piece & 15;
-      if (row < kMPad) *(u4_t*)(xs + row * kXRowBytes + 16 * col) = x[p];
+      lds_copy16(d.X + (int64_t)m * d.ldx + k, buf + 1024u * (uint32_t)(wave * kND + i));
     }
   }
 
@@ -830,16 +893,45 @@ struct Group {
     for (int r = 0; r < kRG; r++) {
       const uint8_t* tp = w0 + (int64_t)(r < nrows ? r : nrows - 1) * rstride;
       t.c[r] = __builtin_nontemporal_load(gload_ptr<u4_t>(tp + 16 * lane));
-      t.s[r] = __builtin_nontemporal_load(gload_ptr<u2_t>(tp + kScaleOff + 8 * (lane & 15)));
       if constexpr (BITS == 5) t.h[r] = __builtin_nontemporal_load(gload_ptr<uint32_t>(tp + kHiOff + 4 * lane));
     }
   }
 
+  // Copies of k tile kx (clamped to the last) into ring buffer slot, then
+  // the code loads of k tile kw into t, in the order the wait counts assume
+  // (the scheduling barriers keep it): X, this wave's scales, codes.  The
+  // scale copy puts row r's four scales of both row blocks side by side (16
+  // bytes per row): lane l copies word l & 1 of row l >> 2, row block
+  // (l >> 1) & 1, whose offset from the tile is soff.
+  template <int BITS>
+  static __device__ __forceinline__ void copies(const JobDesc& d, int kx, uint32_t buf, const uint8_t* wbase,
+                                                uint32_t soff, int wave, int lane) {
+    constexpr int TB = BITS == 4 ? kTile4 : kTile5;
+    const uint8_t* tile = wbase + (int64_t)(kx < d.nkt ? kx : d.nkt - 1) * TB;
+    copy_x(d, kx, buf, wave, lane);
+    lds_copy4(tile + soff, buf + (uint32_t)(kXBytes + 256 * wave));
+  }
+  template <int BITS>
+  static __device__ __forceinline__ void codes(const JobDesc& d, int kw, Tiles<BITS>& t, const uint8_t* wbase,
+                                               int64_t rstride, int nrows, int lane) {
+    constexpr int TB = BITS == 4 ? kTile4 : kTile5;
+    load_w<BITS>(t, wbase + (int64_t)(kw < d.nkt ? kw : d.nkt - 1) * TB, rstride, nrows, lane);
+  }
+
   // One unit: row blocks rb0 + kRG * wave + r (r < kRG) of job d, all k tiles.
   template <int BITS>
-  static __device__ void run_unit(const JobDesc& d, int rb0, uint8_t (*xs)[kMPad * kXRowBytes], int tid) {
+  static __device__ void run_unit(const JobDesc& d, int rb0, uint8_t* xs, uint32_t xs_lds, int tid) {
     constexpr int TB = BITS == 4 ? kTile4 : kTile5;
-    const int lane = tid & 63, wave = tid >> 6;
+    // Issue order: codes of tile 0, then per tile t (the prologue for
+    // t < kDepth - 1, else the end of tile t - kDepth + 1): copies of tile t,
+    // codes of tile t + 1.  The copies of tile kt are therefore complete once
+    // at most this many younger loads of this wave are outstanding: the codes
+    // of tile kt + 1 and kDepth - 2 whole tiles.
+    constexpr int kXWait = kLoadsW<BITS> + (kDepth - 2) * kLoadsTile<BITS>;
+    static_assert(kXWait < 64, "vmcnt range");
+    // s_waitcnt encoding (gfx9): vmcnt low 4 bits, expcnt 7, lgkmcnt 15, vmcnt high 2 bits
+    constexpr int kXWaitImm = (kXWait & 15) | (7 << 4) | (15 << 8) | ((kXWait >> 4) << 14);
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nkt = d.nkt;
     const int64_t rstride = (int64_t)nkt * TB;
     const int rbw = rb0 + kRG * wave;                  // this wave's first row block
@@ -847,37 +939,52 @@ struct Group {
     const int rbl = nrows > 0 ? rbw : d.nrb - 1;       // waves past the job re-read its last block
     const int nr = nrows > 0 ? nrows : 1;
     const uint8_t* wbase = d.packed + (int64_t)rbl * rstride;
-    // prologue: X chunks 0 (to LDS) and 1 (staged), weights of k tiles 0..kDepth-1
-    u4_t xst[kXP];
-    load_x(xst, d, 0, tid);
-    store_x(xst, xs[0], tid);
-    load_x(xst, d, nkt > 1 ? 1 : 0, tid);
+    const int srb = ((lane >> 1) & 1) < nr ? (lane >> 1) & 1 : nr - 1;
+    const uint32_t soff = (uint32_t)(srb * rstride) + (uint32_t)(kScaleOff + 8 * (lane >> 2) + 4 * (lane & 1));
     Tiles<BITS> buf[kDepth];
+    __builtin_amdgcn_sched_barrier(0);
+    codes<BITS>(d, 0, buf[0], wbase, rstride, nr, lane);
 #pragma unroll
-    for (int p = 0; p < kDepth; p++) load_w<BITS>(buf[p], wbase + (int64_t)(p < nkt ? p : nkt - 1) * TB, rstride, nr, lane);
+    for (int p = 0; p < kDepth - 1; p++) {
+      __builtin_amdgcn_sched_barrier(0);
+      copies<BITS>(d, p, xs_lds + (uint32_t)(p * kBufBytes), wbase, soff, wave, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      codes<BITS>(d, p + 1, buf[p + 1], wbase, rstride, nr, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     f4_t acc[kRG][kMb];
 #pragma unroll
     for (int r = 0; r < kRG; r++)
 #pragma unroll
       for (int mb = 0; mb < kMb; mb++) acc[r][mb] = f4_t{0.f, 0.f, 0.f, 0.f};
     const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+    // A fragment of group j, m block mb: row 16 mb + (lane mod 16), chunk
+    // 4 j + lane / 16, at its swizzled slot
     const int mr = lane & 15, c = lane >> 4;
+    uint32_t aoff[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) aoff[j] = (uint32_t)(256 * mr + 16 * ((4 * j + c) ^ mr));
+    const uint32_t sread = (uint32_t)(kXBytes + 256 * wave + 16 * mr);
     for (int kt0 = 0; kt0 < nkt; kt0 += kDepth) {
 #pragma unroll
       for (int p = 0; p < kDepth; p++) {
         const int kt = kt0 + p;
         if (kt < nkt) {
-          // chunk kt is in xs[kt & 1]; every wave is done with xs[(kt + 1) & 1]
-          __syncthreads();
-          store_x(xst, xs[(kt + 1) & 1], tid);
-          load_x(xst, d, kt + 2 < nkt ? kt + 2 : nkt - 1, tid);
-          const uint8_t* xb = xs[kt & 1];
+          // this wave's copies of tile kt have landed; after the barrier every
+          // wave's have, and every wave is done with tile kt - 1
+          __builtin_amdgcn_s_waitcnt(kXWaitImm);
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          __builtin_amdgcn_s_barrier();
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          const uint8_t* xb = xs + p * kBufBytes;
+          // scales of row mr: words 0, 1 of row block 0, then of row block 1
+          const u4_t sc = *(const u4_t*)(xb + sread);
           // group by group: the A fragments of group j serve all kRG row blocks
 #pragma unroll
           for (int j = 0; j < 4; j++) {
             h8_t a[kMb];
 #pragma unroll
-            for (int mb = 0; mb < kMb; mb++) a[mb] = lds_h8(xb + (16 * mb + mr) * kXRowBytes + 64 * j + 16 * c);
+            for (int mb = 0; mb < kMb; mb++) a[mb] = lds_h8(xb + aoff[j] + 4096 * mb);
             // every MFMA of the group is issued before the first of its
             // results is scaled, so the matrix-core latency overlaps
             f4_t pr[kRG][kMb];
@@ -889,7 +996,8 @@ struct Group {
             }
 #pragma unroll
             for (int r = 0; r < kRG; r++) {
-              const float sj = (float)scale_pair(j < 2 ? buf[p].s[r].x : buf[p].s[r].y)[j & 1];
+              const uint32_t sp = sc[2 * r + (j >> 1)];
+              const float sj = (j & 1) ? scale_f32<1>(sp) : scale_f32<0>(sp);
 #pragma unroll
               for (int mb = 0; mb < kMb; mb++)
 #pragma unroll
@@ -897,33 +1005,69 @@ struct Group {
             }
           }
         }
-        const int lt = kt + kDepth < nkt ? kt + kDepth : nkt - 1;
-        load_w<BITS>(buf[p], wbase + (int64_t)lt * TB, rstride, nr, lane);
+        // copies of tile kt + kDepth - 1 into the buffer of tile kt - 1 (every
+        // wave is past it), codes of tile kt + kDepth.  Past the last k tile
+        // they (kept for exact wait counts) re-read the last tile into
+        // buffers no wave reads again.
+        __builtin_amdgcn_sched_barrier(0);
+        copies<BITS>(d, kt + kDepth - 1, xs_lds + (uint32_t)(((p + kDepth - 1) % kBufs) * kBufBytes), wbase, soff,
+                     wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        codes<BITS>(d, kt + kDepth, buf[p], wbase, rstride, nr, lane);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __syncthreads();  // both X buffers are free again
-    if (nrows <= 0) return;
+    // every copy has landed and every wave is done with the ring
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    __syncthreads();
+    if (nrows > 0) store_y(d, acc, rbw, xs + kMPad * kYRow * 4 * wave, lane);
+    // the ring is free for the next unit's copies
+    __syncthreads();
+  }
+
+  // The wave's outputs (rows m < kMPad, n = 16 rbw .. 16 rbw + 31) go through
+  // its slice of the LDS ring, row-major with 16-byte chunks swizzled by
+  // m mod 8, and leave as whole 128-byte row segments: lane L of store t
+  // writes row 8 t + L / 8, outputs 4 (L mod 8) .. + 3.
+  static __device__ __forceinline__ void store_y(const JobDesc& d, const f4_t (&acc)[kRG][kMb], int rbw,
+                                                 uint8_t* st, int lane) {
+    const int mr = lane & 15, c = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < kRG; r++)
+#pragma unroll
+      for (int mb = 0; mb < kMb; mb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int m = 16 * mb + 4 * c + i, n = 16 * r + mr;
+          *(float*)(st + 128 * m + 16 * ((n >> 2) ^ (m & 7)) + 4 * (n & 3)) = acc[r][mb][i];
+        }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     QG_GLOBAL float* Y = (QG_GLOBAL float*)d.Y;
+    const int n0 = kTileRows * rbw + 4 * (lane & 7);
 #pragma unroll
-    for (int r = 0; r < kRG; r++) {
-      const int n = (rbw + r) * kTileRows + mr;
-      if (r < nrows && n < d.N) {
+    for (int t = 0; t < kMPad / 8; t++) {
+      const int m = 8 * t + (lane >> 3);
+      const f4_t v = *(const f4_t*)(st + 128 * m + 16 * ((lane & 7) ^ (m & 7)));
+      if (m < d.M) {
+        QG_GLOBAL float* y = Y + (int64_t)m * d.ldy + n0;
+        if (n0 + 3 < d.N) {
+          *(QG_GLOBAL f4_t*)y = v;
+        } else {
 #pragma unroll
-        for (int mb = 0; mb < kMb; mb++)
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const int m = 16 * mb + 4 * c + i;
-            if (m < d.M) Y[(int64_t)m * d.ldy + n] = acc[r][mb][i];
-          }
+          for (int e = 0; e < 4; e++)
+            if (n0 + e < d.N) y[e] = v[e];
+        }
       }
     }
   }
 };
 
 template <int kMPad>
-__global__ void __launch_bounds__(64 * group_waves(kMPad)) group_kernel(SweepArgs args) {
+__global__ void __launch_bounds__(64 * group_waves(kMPad)) __attribute__((amdgpu_waves_per_eu(kMPad >= 64 ? 2 : 3)))
+group_kernel(SweepArgs args) {
   using S = Group<kMPad>;
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][kMPad * kXRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[S::kLdsBytes];
+  const uint32_t xs_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)xs;
   const QG_CONST JobDesc* D = job_table(args);
   const int tid = threadIdx.x;
   int j = 0;
@@ -931,8 +1075,8 @@ __global__ void __launch_bounds__(64 * group_waves(kMPad)) group_kernel(SweepArg
     while (u >= D[j].grp_end) j++;
     const JobDesc d = D[j];
     const int rb0 = (u - d.grp_begin) * S::kW * kGroupRows;
-    if (d.bits == 4) S::template run_unit<4>(d, rb0, xs, tid);
-    else S::template run_unit<5>(d, rb0, xs, tid);
+    if (d.bits == 4) S::template run_unit<4>(d, rb0, xs, xs_lds, tid);
+    else S::template run_unit<5>(d, rb0, xs, xs_lds, tid);
   }
 }
 
