@@ -12,7 +12,7 @@ tokens/s per sweep is M / step time.  The workloads that fit in the 256 MB
 last-level cache rotate over enough packed copies (>= 1 GB) that every step
 streams its weights from HBM.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only 2|3|4]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only 2|3|4|5]
        [--no-cpu] [--stack-layers L]
        python bench.py --copy-calib MIB   (a plain device copy of MIB MiB, the
        reference for scaling the HBM byte counters)
@@ -35,7 +35,7 @@ HBM_PEAK_GBPS = 8000.0
 # has the commands and raw figures).  Valid only for the kernel sources they
 # were taken on: keyed by the SHA-256 of those sources, else reported as null.
 TRAFFIC = {
-    "2cb8c0b5c22649bd": {"workload": "gate+up 5120->34816 4-bit M=1", "bytes": 105898581},
+    "c635a57367ac41af": {"workload": "gate+up 5120->34816 4-bit M=1", "bytes": 101696653},
 }
 KERNEL_SOURCES = ("self_speculative_verify_amd/csrc/qgemm_kernels.hip",
                   "self_speculative_verify_amd/csrc/qgemm_internal.h",
@@ -58,7 +58,7 @@ def log(msg):
 
 
 class Bench:
-    def __init__(self, cfg, layers=None, rotate_bytes=1 << 30):
+    def __init__(self, cfg, layers=None, rotate_bytes=1 << 30, M=None):
         import torch
 
         from self_speculative_verify_amd import qgemm
@@ -66,7 +66,7 @@ class Bench:
 
         self.qgemm = qgemm
         self.wl = workloads.workload(cfg, layers) if layers else workloads.workload(cfg)
-        self.M = self.wl.Ms[0]
+        self.M = M if M is not None else self.wl.Ms[0]
         dev = torch.device("cuda:0")
         stream = torch.cuda.current_stream()
         maxel = max(m.N * m.K for m in self.wl.matrices)
@@ -97,6 +97,27 @@ class Bench:
         self.ws = qgemm.Workspace(ws, device=dev)
         # the job arrays are marshalled once; each step is one C call
         self.arrays = [qgemm.job_array(js) for js in self.jobsets]
+        self.xbytes = sum(2 * M * K for K in self.wl.distinct_K)
+        self.ybytes = sum(4 * M * m.N for m in self.wl.matrices)
+        torch.cuda.synchronize()
+
+    def set_M(self, M):
+        """Re-point every job at fresh X / Y panels of M rows (same weights)."""
+        import torch
+
+        from synth import synth
+
+        q = self.qgemm
+        dev = torch.device("cuda:0")
+        self.M = M
+        self.X = {K: torch.from_numpy(synth.x_fp16(self.wl.x_seed(K), M, K)).to(dev)
+                  for K in self.wl.distinct_K}
+        self.Y = [torch.empty((M, m.N), dtype=torch.float32, device=dev) for m in self.wl.matrices]
+        self.jobsets = [[q.make_job(p, m.bits, m.N, m.K, self.X[m.K], y, M)
+                         for p, m, y in zip(cp, self.wl.matrices, self.Y)] for cp in self.copies]
+        ws = max(q.workspace_bytes(js) for js in self.jobsets)
+        self.ws = q.Workspace(ws, device=dev)
+        self.arrays = [q.job_array(js) for js in self.jobsets]
         self.xbytes = sum(2 * M * K for K in self.wl.distinct_K)
         self.ybytes = sum(4 * M * m.N for m in self.wl.matrices)
         torch.cuda.synchronize()
@@ -177,7 +198,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", type=int, default=0, help="time one workload (2, 3 or 4) only")
+    ap.add_argument("--only", type=int, default=0,
+                    help="time one workload (2, 3 or 4) only; 5 times the 5-bit stack at every M of its sweep")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--stack-layers", type=int, default=64)
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB")
@@ -206,6 +228,18 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
+        return
+
+    if args.only == 5:
+        # the 5-bit stack at each M of its sweep (same weights, fresh panels);
+        # one JSON line per M, no headline
+        b = Bench(5, layers=args.stack_layers)
+        for M in b.wl.Ms:
+            b.set_M(M)
+            ms, wall = b.run(args.steps, args.warmup)
+            r = b.report(ms)
+            r["wall_s"] = round(wall, 4)
+            print(json.dumps(r), flush=True)
         return
 
     results = {}

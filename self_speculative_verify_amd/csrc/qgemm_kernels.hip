@@ -809,12 +809,13 @@ __global__ void __launch_bounds__(64 * kStreamWavesPerBlock) stream_kernel(Sweep
 // no K split, so no partial sums cross waves.  The waves walk the k tiles in
 // lockstep, one barrier per k tile.  The X chunk of a k tile (kMPad rows x 128
 // k) is copied once per workgroup straight from memory into LDS (direct-to-LDS
-// loads, no registers), into a ring of kDepth + 1 buffers; each wave reads its
+// loads, no registers), into a ring of kDepth buffers; each wave reads its
 // MFMA A fragments for the tile once and applies them to its kRG row blocks,
 // so LDS traffic per weight byte falls kRG-fold.  The X copy of tile t is
 // issued just before the weight loads of tile t, kDepth tiles ahead, so
 // waiting for it never waits on a younger weight load.  Units are handed out
-// in job order with a stride of the grid; the host orders jobs longest K first.
+// in job order, one round of the grid at a time in alternating directions;
+// the host orders jobs longest K first.
 //
 // LDS layout of one buffer: 16-byte slot s (X chunk col' of row s / 16,
 // col' = s mod 16) holds X[row][8 col .. 8 col + 7] of the k tile with col =
@@ -1071,7 +1072,12 @@ group_kernel(SweepArgs args) {
   const QG_CONST JobDesc* D = job_table(args);
   const int tid = threadIdx.x;
   int j = 0;
-  for (int u = blockIdx.x; u < args.total; u += gridDim.x) {
+  // round i of the grid takes units [i G, (i + 1) G) in alternating
+  // directions, so the longest-first order evens out across workgroups
+  const int G = (int)gridDim.x, b = (int)blockIdx.x;
+  for (int i = 0;; i++) {
+    const int u = i * G + ((i & 1) ? G - 1 - b : b);
+    if (u >= args.total) break;
     while (u >= D[j].grp_end) j++;
     const JobDesc d = D[j];
     const int rb0 = (u - d.grp_begin) * S::kW * kGroupRows;
