@@ -12,7 +12,7 @@ tokens/s per sweep is M / step time.  The workloads that fit in the 256 MB
 last-level cache rotate over enough packed copies (>= 1 GB) that every step
 streams its weights from HBM.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only 2|3|4|5]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only 2|3|4|5|6]
        [--no-cpu] [--stack-layers L]
        python bench.py --copy-calib MIB   (a plain device copy of MIB MiB, the
        reference for scaling the HBM byte counters)
@@ -122,8 +122,36 @@ class Bench:
         self.ybytes = sum(4 * M * m.N for m in self.wl.matrices)
         torch.cuda.synchronize()
 
+    def set_verify(self, M):
+        """Time the verify head instead: the single matrix swept with the
+        argmax epilogue (no logits written) and M / 6 slots of five drafts."""
+        import torch
+
+        q = self.qgemm
+        dev = torch.device("cuda:0")
+        self.set_M(M)
+        m = self.wl.matrices[0]
+        self.heads = [q.make_head_job(cp[0], m.bits, m.N, m.K, self.X[m.K], M) for cp in self.copies]
+        self.vslots = q.slot_array([(6 * i, 5) for i in range(M // 6)])
+        self.drafts = torch.zeros(M, dtype=torch.int32, device=dev)
+        self.am = torch.empty(M, dtype=torch.int32, device=dev)
+        self.acc = torch.empty(len(self.vslots), dtype=torch.int32, device=dev)
+        self.ws = q.Workspace(q.verify_workspace_bytes(self.heads[0]), device=dev)
+        self.ybytes = 0
+        self.verify = True
+        torch.cuda.synchronize()
+
     def step(self, i):
         q = self.qgemm
+        if getattr(self, "verify", False):
+            import ctypes
+
+            st = q.lib().qgemm_verify_head(ctypes.byref(self.heads[i % len(self.heads)]), self.drafts.data_ptr(),
+                                           self.vslots, len(self.vslots), self.am.data_ptr(), None,
+                                           self.acc.data_ptr(), self.ws.ptr, self.ws.nbytes, self.stream)
+            if st != q.OK:
+                raise q.QgemmError(st, "qgemm_verify_head")
+            return
         arr = self.arrays[i % len(self.arrays)]
         st = q.lib().qgemm_sweep(arr, len(arr), self.ws.ptr, self.ws.nbytes, self.stream)
         if st != q.OK:
@@ -199,7 +227,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", type=int, default=0,
-                    help="time one workload (2, 3 or 4) only; 5 times the 5-bit stack at every M of its sweep")
+                    help="time one workload (2, 3 or 4) only; 5 times the 5-bit stack at every M of its "
+                         "sweep; 6 times the verify head")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--stack-layers", type=int, default=64)
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB")
@@ -228,6 +257,24 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
+        return
+
+    if args.only == 6:
+        # the verify head (lm_head-class sweep + argmax + acceptance) at each
+        # M of workload 6; one JSON line per M, no headline
+        b = Bench(6)
+        for M in b.wl.Ms:
+            b.verify = False
+            b.set_M(M)
+            ms_sweep, _ = b.run(args.steps, args.warmup)     # the same matrix, logits written
+            b.set_verify(M)
+            ms, wall = b.run(args.steps, args.warmup)
+            r = b.report(ms)
+            r["wall_s"] = round(wall, 4)
+            r["slots"] = M // 6
+            r["rounds_per_s"] = round(1e3 / ms, 1)
+            r["plain_sweep_ms"] = round(ms_sweep, 5)
+            print(json.dumps(r), flush=True)
         return
 
     if args.only == 5:

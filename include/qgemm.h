@@ -144,6 +144,49 @@ qgemm_status qgemm_sweep(const qgemm_job* jobs, int njobs, void* workspace, size
 qgemm_status qgemm_sweep_path(const qgemm_job* jobs, int njobs, int path, void* workspace,
                               size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Verify head (greedy acceptance).  In a self-speculative decode round the
+ * panel holds, per slot, the hidden states after the accepted context and
+ * after each of its d drafted tokens (1 + d rows).  Greedy speculative
+ * decoding must leave the greedy output unchanged (Quasar/q27 wiki, opening
+ * notes: greedy spec decode by default, greedy output bitwise unchanged), so
+ * draft i + 1 stands only if it equals the model's argmax at row i, and the
+ * round yields the longest such prefix plus the argmax at the first row that
+ * disagrees.  The per-round payoff is the accepted count per weight read
+ * (same page, intro bullets).  The head is the lm_head-class matrix
+ * (vocabulary rows N).  One call sweeps it with a per-row argmax epilogue
+ * (the logits are reduced in the kernel, not written unless Y is given) and
+ * then scores every slot.
+ *
+ *   head     : one job as for qgemm_sweep; head->Y may be NULL (no logits
+ *              written) or a logits buffer obeying the sweep's rules
+ *   drafts   : device int32 [M]; drafts[r] is the draft token that row r's
+ *              argmax is checked against (unused for each slot's last row);
+ *              may be NULL when no slot has drafts
+ *   slots    : host array of nslots (1 .. 64) slots: rows row0 .. row0 + ndraft
+ *              of the panel, ndraft >= 0, row0 + ndraft < M
+ *   argmax   : device int32 [M]: per row, the column of the largest logit,
+ *              the lowest column among equal values
+ *   maxlogit : device fp32 [M] (may be NULL): that largest logit
+ *   accepted : device int32 [nslots]: per slot, the number L of leading rows
+ *              i < ndraft with argmax[row0 + i] == drafts[row0 + i]; the round
+ *              emits drafts[row0 .. row0 + L - 1] and then argmax[row0 + L]
+ * The logits (and so the argmax) are exactly those qgemm_sweep computes for
+ * the same job.  Rows whose X is not finite get an unspecified column in
+ * 0 .. N - 1.  The workspace (qgemm_verify_workspace_bytes, zero-filled
+ * before first use like a sweep's) ends with the argmax keys, which the call leaves at
+ * zero.  Two kernel launches on `stream`; asynchronous like qgemm_sweep. */
+typedef struct {
+  int32_t row0;
+  int32_t ndraft;
+} qgemm_slot;
+
+size_t qgemm_verify_workspace_bytes(const qgemm_job* head);
+
+qgemm_status qgemm_verify_head(const qgemm_job* head, const int32_t* drafts, const qgemm_slot* slots, int nslots,
+                               int32_t* argmax, float* maxlogit, int32_t* accepted, void* workspace,
+                               size_t ws_bytes, void* stream);
+
 /* The argument checks of qgemm_sweep_path alone (host only, no HIP call). */
 qgemm_status qgemm_validate(const qgemm_job* jobs, int njobs, int path, void* workspace,
                             size_t ws_bytes);

@@ -17,6 +17,14 @@ dequantized inside the weight-streaming product; group 32 and 4/5 bits):
   ascending k, decoded from the packed bytes.
 * ``compare``: the acceptance test -- relative L2 over a job's Y at most 1e-4
   and, per row m, ``max_n |Y - Yref| <= 1e-3 * ||X[m, :]||_2 * max(s)``.
+* ``verify_head``: the greedy verify step after a sweep of an lm_head-class
+  matrix.  Greedy speculative decoding leaves greedy output unchanged (Quasar/q27
+  wiki, opening notes: greedy spec decode by default, greedy bitwise
+  unchanged), so with a slot's panel rows r0 .. r0 + d (the states after the
+  context and after each of its d drafted tokens), draft i + 1 stands only if
+  it equals the argmax of row r0 + i; the accepted count is the longest such
+  prefix, and the round's next token is the argmax of the first row that
+  disagrees.  ``argmax_rows`` takes the lowest column among equal maxima.
 """
 from __future__ import annotations
 
@@ -186,3 +194,38 @@ def compare(Y: np.ndarray, Yref: np.ndarray, X: np.ndarray, smax: float) -> dict
 def max_scale(packed: np.ndarray, N: int, K: int, bits: int) -> float:
     _, s = unpack(packed, N, K, bits)
     return float(np.abs(f16_bits_to_f64(s)).max())
+
+
+def argmax_rows(Y: np.ndarray) -> np.ndarray:
+    """Per row, the column of the largest value, the lowest one among equal
+    values (numpy's argmax returns the first occurrence)."""
+    return np.argmax(np.asarray(Y), axis=1).astype(np.int64)
+
+
+def accept(argmax, drafts, slots) -> list:
+    """Accepted draft count per slot (row0, ndraft): leading rows i < ndraft
+    with argmax[row0 + i] == drafts[row0 + i], counted until the first that
+    differs."""
+    out = []
+    for row0, nd in slots:
+        L = 0
+        while L < nd and int(argmax[row0 + L]) == int(drafts[row0 + L]):
+            L += 1
+        out.append(L)
+    return out
+
+
+def verify_head(packed: np.ndarray, N: int, K: int, bits: int, X: np.ndarray, drafts, slots,
+                nthreads: int | None = None):
+    """(argmax [M], max logit [M], accepted per slot, logits [M, N]) in fp64."""
+    Y = sweep(packed, N, K, bits, X, nthreads=nthreads)
+    am = argmax_rows(Y)
+    mx = Y[np.arange(Y.shape[0]), am]
+    return am, mx, accept(am, drafts, slots), Y
+
+
+def top2_gap(Y: np.ndarray) -> np.ndarray:
+    """Per row, the largest value minus the second largest (0 on a tie)."""
+    Y = np.asarray(Y, dtype=np.float64)
+    part = np.partition(Y, Y.shape[1] - 2, axis=1)
+    return part[:, -1] - part[:, -2]

@@ -20,6 +20,8 @@ hipError_t launch_pack(const float* W, int64_t ldw, int N, int K, int bits, void
 hipError_t launch_fill_zero(void* p, int64_t words, hipStream_t stream);
 int sweep_blocks_per_cu(int kind, int cls);
 hipError_t launch_sweep(int kind, int cls, const SweepArgs& args, int grid, hipStream_t stream);
+hipError_t launch_accept(const AcceptArgs& a, unsigned long long* keys, const int32_t* drafts, int32_t* argmax,
+                         float* maxval, int32_t* accepted, hipStream_t stream);
 }  // namespace qg
 
 namespace {
@@ -48,7 +50,8 @@ int path_of(int path, int M) {
   return path;
 }
 
-qgemm_status validate(const qgemm_job* jobs, int njobs, int path) {
+// y_optional: the verify head, whose Y may be null (no outputs written)
+qgemm_status validate(const qgemm_job* jobs, int njobs, int path, bool y_optional = false) {
   if (njobs < 1 || jobs == nullptr) return QGEMM_ERR_INVALID_ARG;
   if (path != QGEMM_PATH_AUTO && path != QGEMM_PATH_GEMV && path != QGEMM_PATH_MFMA)
     return QGEMM_ERR_INVALID_ARG;
@@ -56,11 +59,16 @@ qgemm_status validate(const qgemm_job* jobs, int njobs, int path) {
     const qgemm_job& j = jobs[i];
     if (!valid_shape(j.bits, j.N, j.K)) return QGEMM_ERR_INVALID_ARG;
     if (j.M < 1 || j.M > QGEMM_MAX_M) return QGEMM_ERR_INVALID_ARG;
-    if (!j.packed || !j.X || !j.Y) return QGEMM_ERR_INVALID_ARG;
-    if (!aligned(j.packed, 256) || !aligned(j.X, 16) || !aligned(j.Y, 16)) return QGEMM_ERR_INVALID_ARG;
+    if (!j.packed || !j.X) return QGEMM_ERR_INVALID_ARG;
+    if (!aligned(j.packed, 256) || !aligned(j.X, 16)) return QGEMM_ERR_INVALID_ARG;
     if (j.ldx < j.K || j.ldx % 8 != 0 || j.ldx > kMaxK) return QGEMM_ERR_INVALID_ARG;
-    if (j.ldy < j.N || j.ldy % 4 != 0) return QGEMM_ERR_INVALID_ARG;
     if (path == QGEMM_PATH_GEMV && j.M > QGEMM_GEMV_MAX_M) return QGEMM_ERR_INVALID_ARG;
+    if (!j.Y) {
+      if (y_optional) continue;
+      return QGEMM_ERR_INVALID_ARG;
+    }
+    if (!aligned(j.Y, 16)) return QGEMM_ERR_INVALID_ARG;
+    if (j.ldy < j.N || j.ldy % 4 != 0) return QGEMM_ERR_INVALID_ARG;
     // Y must not overlap X or the packed weights of this job
     const uintptr_t y0 = (uintptr_t)j.Y;
     const uintptr_t y1 = y0 + (uintptr_t)(((j.M - 1) * j.ldy + j.N) * sizeof(float));
@@ -188,7 +196,7 @@ int64_t stream_waves(const std::vector<JobDesc>& descs, int64_t T) {
   return W;
 }
 
-Plan make_plan(const qgemm_job* jobs, int njobs, int path) {
+Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* keys = nullptr) {
   Plan P;
   // Jobs of the group kernel go longest K first (their units are whole-K,
   // so the long ones are dealt out before the short ones fill the gaps);
@@ -218,6 +226,7 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path) {
     d.packed = (const uint8_t*)j.packed;
     d.X = j.X;
     d.Y = j.Y;
+    d.keys = keys;
     d.ldx = j.ldx;
     d.ldy = j.ldy;
     d.N = (int32_t)j.N;
@@ -305,6 +314,8 @@ int cu_count() {
   return cus;
 }
 
+qgemm_status run_plan(Plan& P, void* workspace, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -367,6 +378,58 @@ qgemm_status qgemm_sweep_path(const qgemm_job* jobs, int njobs, int path, void* 
   Plan P = make_plan(jobs, njobs, path);
   if (!P.ok) return QGEMM_ERR_UNSUPPORTED;
   if (ws_bytes < P.total) return QGEMM_ERR_INVALID_ARG;
+  return run_plan(P, workspace, stream);
+}
+
+// verify head workspace: the sweep's, then one argmax key per row
+static size_t verify_keys_off(const Plan& P) { return round_up(P.total, 256); }
+static size_t verify_total(const Plan& P) {
+  return verify_keys_off(P) + (size_t)qg::kKeyCopies * qg::kKeyRows * sizeof(unsigned long long);
+}
+
+size_t qgemm_verify_workspace_bytes(const qgemm_job* head) {
+  if (validate(head, 1, QGEMM_PATH_AUTO, true) != QGEMM_OK) return 0;
+  const Plan P = make_plan(head, 1, QGEMM_PATH_AUTO);
+  return P.ok ? verify_total(P) : 0;
+}
+
+qgemm_status qgemm_verify_head(const qgemm_job* head, const int32_t* drafts, const qgemm_slot* slots, int nslots,
+                               int32_t* argmax, float* maxlogit, int32_t* accepted, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  qgemm_status st = validate(head, 1, QGEMM_PATH_AUTO, true);
+  if (st != QGEMM_OK) return st;
+  if (!workspace || !aligned(workspace, 256) || !argmax || !accepted) return QGEMM_ERR_INVALID_ARG;
+  if (!slots || nslots < 1 || nslots > qg::kMaxSlots) return QGEMM_ERR_INVALID_ARG;
+  qg::AcceptArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.nslots = nslots;
+  a.M = head->M;
+  bool any_draft = false;
+  for (int i = 0; i < nslots; i++) {
+    const qgemm_slot& sl = slots[i];
+    if (sl.row0 < 0 || sl.ndraft < 0 || (int64_t)sl.row0 + sl.ndraft >= head->M) return QGEMM_ERR_INVALID_ARG;
+    any_draft = any_draft || sl.ndraft > 0;
+    a.row0[i] = sl.row0;
+    a.ndraft[i] = sl.ndraft;
+  }
+  if (any_draft && !drafts) return QGEMM_ERR_INVALID_ARG;
+  const Plan P0 = make_plan(head, 1, QGEMM_PATH_AUTO);
+  if (!P0.ok) return QGEMM_ERR_UNSUPPORTED;
+  if (ws_bytes < verify_total(P0)) return QGEMM_ERR_INVALID_ARG;
+  unsigned long long* keys = (unsigned long long*)((uint8_t*)workspace + verify_keys_off(P0));
+  Plan P = make_plan(head, 1, QGEMM_PATH_AUTO, keys);
+  st = run_plan(P, workspace, stream);
+  if (st != QGEMM_OK) return st;
+  return qg::launch_accept(a, keys, drafts, argmax, maxlogit, accepted, (hipStream_t)stream) == hipSuccess
+             ? QGEMM_OK
+             : QGEMM_ERR_HIP;
+}
+
+}  // extern "C"
+
+namespace {
+
+qgemm_status run_plan(Plan& P, void* workspace, void* stream) {
   uint8_t* ws = (uint8_t*)workspace;
   hipStream_t s = (hipStream_t)stream;
   const int cus = cu_count();
@@ -408,6 +471,10 @@ qgemm_status qgemm_sweep_path(const qgemm_job* jobs, int njobs, int path, void* 
   }
   return QGEMM_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 qgemm_status qgemm_sweep(const qgemm_job* jobs, int njobs, void* workspace, size_t ws_bytes, void* stream) {
   return qgemm_sweep_path(jobs, njobs, QGEMM_PATH_AUTO, workspace, ws_bytes, stream);

@@ -47,7 +47,8 @@ constexpr int kMaxUnitWeight = kTile5 / kTileK;
 struct JobDesc {
   const uint8_t* packed;
   const uint16_t* X;
-  float* Y;
+  float* Y;              // null: outputs not written (verify head)
+  unsigned long long* keys;  // null, or kKeyCopies x kKeyRows argmax keys (verify head)
   int64_t ldx;
   int64_t ldy;
   int32_t ubeg;          // stream kernel: units [ubeg, uend) of this job's steps
@@ -61,6 +62,35 @@ struct JobDesc {
   int32_t rg_begin;      // stream kernel: first arrival counter of this job
   int32_t grp_begin;     // group kernel: first row-block group of this job
   int32_t grp_end;
+};
+
+// Argmax key of output value v in column n: the value's bits mapped to an
+// order-preserving unsigned integer in the high word, the complement of n in
+// the low word, so the maximum key is the largest value and, among equal
+// values, the lowest column.  0 is below every key.
+inline __host__ __device__ unsigned long long logit_key(float v, int n) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)o << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)n);
+}
+inline __host__ __device__ float key_value(unsigned long long k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+inline __host__ __device__ int key_column(unsigned long long k) {
+  return (int)(0xFFFFFFFFu - (uint32_t)k);
+}
+
+constexpr int kMaxSlots = 64;  // verify head: slots per call (at most one per row)
+// verify head: argmax keys are kept in kKeyCopies copies of the per-row
+// array (copy = wave or workgroup index mod kKeyCopies), so that the atomics
+// of the many waves finishing together spread over that many addresses per row
+constexpr int kKeyCopies = 16;
+constexpr int kKeyRows = 64;
+struct AcceptArgs {
+  int32_t nslots, M;
+  int32_t row0[kMaxSlots];
+  int32_t ndraft[kMaxSlots];
 };
 
 struct SweepArgs {

@@ -244,6 +244,21 @@ __device__ __forceinline__ float scale_f32(uint32_t pair) {
   return f;
 }
 
+__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
+  return a > b ? a : b;
+}
+// maximum of a 64-bit key over the lanes l ^ mask for mask < span (a power
+// of two), bit by bit
+template <int kFrom, int kSpan>
+__device__ __forceinline__ unsigned long long lanes_max(unsigned long long k) {
+#pragma unroll
+  for (int m = kFrom; m < kSpan; m <<= 1) k = umax64(k, __shfl_xor(k, m));
+  return k;
+}
+__device__ __forceinline__ void key_max(unsigned long long* p, unsigned long long k) {
+  __hip_atomic_fetch_max(p, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ const QG_CONST JobDesc* job_table(const SweepArgs& a) {
   return a.table ? (const QG_CONST JobDesc*)a.table : (const QG_CONST JobDesc*)&a.inl[0];
 }
@@ -352,6 +367,9 @@ struct Stream {
     int lane;
     // split row groups whose partial this wave stored (kind 0 / kind 1)
     int pend_j0, pend_rg0, pend_j1, pend_rg1;
+    // verify head: best argmax key of this lane's rows over the columns it
+    // finished (accumulator i's row), published at the end of a segment
+    unsigned long long best[kA];
   };
 
   // Write the finished sums of row group rg of job j to Y, or, for a row
@@ -383,6 +401,7 @@ struct Stream {
     auto row_of = [&](int i) { return kMfma ? 4 * (lane >> 4) + i : i; };
     const bool holder = kMfma || lane < 16;
     if (first >= cx.a && last < cx.b) {
+      const bool keys = D[j].keys != nullptr;
 #pragma unroll
       for (int r = 0; r < kR; r++) {
         const int n = (rg * kR + r) * kTileRows + nn;
@@ -390,7 +409,10 @@ struct Stream {
 #pragma unroll
           for (int i = 0; i < kA; i++) {
             const int m = row_of(i);
-            if (m < M) Y[(int64_t)m * ldy + n] = acc[r][i];
+            if (m < M) {
+              if (Y) Y[(int64_t)m * ldy + n] = acc[r][i];
+              if (keys) cx.best[i] = umax64(cx.best[i], logit_key(acc[r][i], n));
+            }
           }
         }
       }
@@ -510,6 +532,10 @@ struct Stream {
           for (int c = 0; c < kChunksPerLane; c++)
             if (w + t <= wl) v[c] += p[t][c];
       }
+      // verify head: element t of every chunk of this lane is row
+      // (4 lane + t) mod srows (64 chunks of 4 elements span whole columns)
+      unsigned long long kb[4] = {0ull, 0ull, 0ull, 0ull};
+      const bool keys = D[j].keys != nullptr;
 #pragma unroll
       for (int c = 0; c < kChunksPerLane; c++) {
         const int q = lane + 64 * c;
@@ -518,7 +544,21 @@ struct Stream {
         for (int t = 0; t < 4; t++) {
           const int e = 4 * q + t, col = e / srows, m = e - col * srows;
           const int n = rg * cols + col;
-          if (m < M && n < N) Y[(int64_t)m * ldy + n] = v[c][t];
+          if (m < M && n < N) {
+            if (Y) Y[(int64_t)m * ldy + n] = v[c][t];
+            if (keys) kb[t] = umax64(kb[t], logit_key(v[c][t], n));
+          }
+        }
+      }
+      if (keys) {
+        // lanes l and l' hold the same rows when l = l' mod max(srows / 4, 1)
+        const int per = srows >= 4 ? srows / 4 : 1;
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          unsigned long long k = kb[t];
+          for (int msk = per; msk < 64; msk <<= 1) k = umax64(k, __shfl_xor(k, msk));
+          const int m = (4 * lane + t) % srows;
+          if (lane < per && m < M && k != 0ull) key_max(D[j].keys + (cx.gw % kKeyCopies) * kKeyRows + m, k);
         }
       }
       if (lane == 0)
@@ -738,9 +778,26 @@ struct Stream {
         }
       }
     }
+    if (D[j].keys) publish(cx, D[j].keys + (cx.gw % kKeyCopies) * kKeyRows, M);
   }
 
-  static __device__ void run(const SweepArgs& args, uint8_t* xs) {
+  // Verify head: the segment's best key per row, over the 16 lanes holding
+  // the row's columns, into the job's keys (one atomic per row and wave).
+  static __device__ __forceinline__ void publish(Ctx& cx, unsigned long long* keys, int M) {
+    const int lane = cx.lane;
+#pragma unroll
+    for (int i = 0; i < kA; i++) {
+      const unsigned long long k = lanes_max<1, 16>(cx.best[i]);
+      const int m = kMfma ? 4 * (lane >> 4) + i : i;
+      if ((lane & 15) == 0 && (kMfma || lane == 0) && m < M && k != 0ull) key_max(keys + m, k);
+      cx.best[i] = 0ull;
+    }
+  }
+
+  // Inlined into the kernel on purpose: the job table pointer below is the
+  // address of the kernel argument in the constant (kernarg) address space,
+  // which a by-reference copy on the stack would not be.
+  static __device__ __forceinline__ void run(const SweepArgs& args, uint8_t* xs) {
     Ctx cx;
     cx.D = job_table(args);
     cx.counters = args.counters;
@@ -758,6 +815,8 @@ struct Stream {
     cx.b = cx.a + cx.q + (cx.gw < cx.rem ? 1 : 0);
     cx.pend_j0 = cx.pend_j1 = -1;
     cx.pend_rg0 = cx.pend_rg1 = 0;
+#pragma unroll
+    for (int i = 0; i < kA; i++) cx.best[i] = 0ull;
     // first job of the range: a bucket index into the uend list when the jobs
     // come from a table, else a scan of the (at most 12) inline jobs
     int j = 0;
@@ -829,14 +888,23 @@ __global__ void __launch_bounds__(64 * kStreamWavesPerBlock) stream_kernel(Sweep
 // group kernel covers them with its own explicit waits (a copy issued before a
 // load has completed once that load has).  The compiler's wait counts for its
 // own loads are then only ever too strict.  The nop covers the M0-write hazard
-// of LDS-direct loads.
+// of LDS-direct loads.  M0 is a register the compiler reserves, so the
+// sequence saves and restores it.
 __device__ __forceinline__ void lds_copy16(const void* src, uint32_t dst) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(dst)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(dst)
+      : "memory");
 }
 __device__ __forceinline__ void lds_copy4(const void* src, uint32_t dst) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off nt" ::"v"(src), "s"(dst)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off nt\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(dst)
+      : "memory");
 }
 
 template <int kMPad>
@@ -855,7 +923,8 @@ struct Group {
   static constexpr int kYRow = kRG * kTileRows;                       // outputs n of a wave
   static_assert(kND * kThreads >= kMPad * 16, "X copies cover the panel");
   static constexpr int kYBytes = kW * kMPad * kYRow * 4;             // output staging (reuses the ring)
-  static constexpr int kLdsBytes = kBufs * kBufBytes > kYBytes ? kBufs * kBufBytes : kYBytes;
+  static constexpr int kRingBytes = kBufs * kBufBytes > kYBytes ? kBufs * kBufBytes : kYBytes;
+  static constexpr int kLdsBytes = kRingBytes + kMPad * 8;           // then one argmax key per row
 
   template <int BITS>
   struct Tiles {
@@ -1021,9 +1090,16 @@ struct Group {
     // every copy has landed and every wave is done with the ring
     __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
     __syncthreads();
-    if (nrows > 0) store_y(d, acc, rbw, xs + kMPad * kYRow * 4 * wave, lane);
-    // the ring is free for the next unit's copies
+    unsigned long long* best = (unsigned long long*)(xs + kRingBytes);
+    if (nrows > 0) store_y(d, acc, rbw, xs + kMPad * kYRow * 4 * wave, best, lane);
+    // the ring is free for the next unit's copies; the unit's argmax keys are
+    // complete and go to the job's keys
     __syncthreads();
+    if (d.keys && tid < d.M) {
+      const unsigned long long k = best[tid];
+      if (k != 0ull) key_max(d.keys + (blockIdx.x % kKeyCopies) * kKeyRows + tid, k);
+      best[tid] = 0ull;
+    }
   }
 
   // The wave's outputs (rows m < kMPad, n = 16 rbw .. 16 rbw + 31) go through
@@ -1031,7 +1107,7 @@ struct Group {
   // m mod 8, and leave as whole 128-byte row segments: lane L of store t
   // writes row 8 t + L / 8, outputs 4 (L mod 8) .. + 3.
   static __device__ __forceinline__ void store_y(const JobDesc& d, const f4_t (&acc)[kRG][kMb], int rbw,
-                                                 uint8_t* st, int lane) {
+                                                 uint8_t* st, unsigned long long* best, int lane) {
     const int mr = lane & 15, c = lane >> 4;
 #pragma unroll
     for (int r = 0; r < kRG; r++)
@@ -1049,7 +1125,7 @@ struct Group {
     for (int t = 0; t < kMPad / 8; t++) {
       const int m = 8 * t + (lane >> 3);
       const f4_t v = *(const f4_t*)(st + 128 * m + 16 * ((lane & 7) ^ (m & 7)));
-      if (m < d.M) {
+      if (m < d.M && Y) {
         QG_GLOBAL float* y = Y + (int64_t)m * d.ldy + n0;
         if (n0 + 3 < d.N) {
           *(QG_GLOBAL f4_t*)y = v;
@@ -1058,6 +1134,17 @@ struct Group {
           for (int e = 0; e < 4; e++)
             if (n0 + e < d.N) y[e] = v[e];
         }
+      }
+      if (d.keys) {
+        // verify head: the best of the row's 32 outputs (8 lanes), into the
+        // workgroup's key of row m
+        unsigned long long k = 0ull;
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+          if (n0 + e < d.N) k = umax64(k, logit_key(v[e], n0 + e));
+        k = lanes_max<1, 8>(k);
+        if ((lane & 7) == 0 && m < d.M && k != 0ull)
+          __hip_atomic_fetch_max(best + m, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
   }
@@ -1071,6 +1158,9 @@ group_kernel(SweepArgs args) {
   const uint32_t xs_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)xs;
   const QG_CONST JobDesc* D = job_table(args);
   const int tid = threadIdx.x;
+  // argmax keys of the verify head start at 0 (the first unit's barriers
+  // order this before any use)
+  if (tid < kMPad) ((unsigned long long*)(xs + S::kRingBytes))[tid] = 0ull;
   int j = 0;
   // round i of the grid takes units [i G, (i + 1) G) in alternating
   // directions, so the longest-first order evens out across workgroups
@@ -1084,6 +1174,39 @@ group_kernel(SweepArgs args) {
     if (d.bits == 4) S::template run_unit<4>(d, rb0, xs, xs_lds, tid);
     else S::template run_unit<5>(d, rb0, xs, xs_lds, tid);
   }
+}
+
+// Verify head, after the sweep: each row's key (the largest of its copies)
+// becomes its argmax column and maximum; each slot accepts its drafts up to
+// the first row whose argmax is not the next draft token.  The keys are reset
+// for the next call.
+__global__ void __launch_bounds__(64) accept_kernel(AcceptArgs a, unsigned long long* keys, const int32_t* drafts,
+                                                    int32_t* argmax, float* maxval, int32_t* accepted) {
+  __shared__ int32_t am[64];
+  const int t = threadIdx.x;
+  if (t < a.M) {
+    unsigned long long k = 0ull;
+    for (int c = 0; c < kKeyCopies; c++) {
+      k = umax64(k, keys[c * kKeyRows + t]);
+      keys[c * kKeyRows + t] = 0ull;
+    }
+    am[t] = key_column(k);
+    argmax[t] = am[t];
+    if (maxval) maxval[t] = key_value(k);
+  }
+  __syncthreads();
+  if (t < a.nslots) {
+    const int r0 = a.row0[t], nd = a.ndraft[t];
+    int L = 0;
+    while (L < nd && am[r0 + L] == drafts[r0 + L]) L++;
+    accepted[t] = L;
+  }
+}
+
+hipError_t launch_accept(const AcceptArgs& a, unsigned long long* keys, const int32_t* drafts, int32_t* argmax,
+                         float* maxval, int32_t* accepted, hipStream_t stream) {
+  hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64), 0, stream, a, keys, drafts, argmax, maxval, accepted);
+  return hipGetLastError();
 }
 
 // zero fill for workspaces (no memset node, safe under capture)

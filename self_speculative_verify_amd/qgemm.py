@@ -22,8 +22,9 @@ GEMV_MAX_M = 8
 EXPORTS = (
     "qgemm_packed_bytes", "qgemm_pack", "qgemm_workspace_bytes", "qgemm_workspace_init",
     "qgemm_sweep", "qgemm_sweep_path", "qgemm_validate", "qgemm_auto_path",
-    "qgemm_status_string",
+    "qgemm_status_string", "qgemm_verify_workspace_bytes", "qgemm_verify_head",
 )
+MAX_SLOTS = 64
 
 
 class QgemmError(RuntimeError):
@@ -45,6 +46,11 @@ class Job(ctypes.Structure):
         ("M", ctypes.c_int32),
         ("bits", ctypes.c_int32),
     ]
+
+
+class Slot(ctypes.Structure):
+    """Mirror of ``qgemm_slot``: panel rows row0 .. row0 + ndraft."""
+    _fields_ = [("row0", ctypes.c_int32), ("ndraft", ctypes.c_int32)]
 
 
 _lib = None
@@ -76,6 +82,10 @@ def lib() -> ctypes.CDLL:
         L.qgemm_auto_path.restype = ci
         L.qgemm_status_string.argtypes = [ci]
         L.qgemm_status_string.restype = ctypes.c_char_p
+        L.qgemm_verify_workspace_bytes.argtypes = [jp]
+        L.qgemm_verify_workspace_bytes.restype = sz
+        L.qgemm_verify_head.argtypes = [jp, vp, ctypes.POINTER(Slot), ci, vp, vp, vp, vp, sz, vp]
+        L.qgemm_verify_head.restype = ci
         _lib = L
     return _lib
 
@@ -179,3 +189,32 @@ def sweep_one(packed, bits: int, N: int, K: int, X, M: int, Y=None, path: int = 
     ws = Workspace(workspace_bytes([job], path), device=packed.device, stream=stream)
     sweep([job], ws, path, stream)
     return Y
+
+
+def make_head_job(packed, bits: int, N: int, K: int, X, M: int, Y=None) -> Job:
+    """Verify-head job: like make_job, but Y may be None (logits not written)."""
+    if Y is None:
+        return Job(packed.data_ptr(), X.data_ptr(), None, N, K, X.stride(0), 0, M, bits)
+    return make_job(packed, bits, N, K, X, Y, M)
+
+
+def verify_workspace_bytes(head: Job) -> int:
+    return int(lib().qgemm_verify_workspace_bytes(ctypes.byref(head)))
+
+
+def slot_array(slots):
+    """(row0, ndraft) pairs -> a ``qgemm_slot`` array."""
+    return (Slot * len(slots))(*[Slot(int(r), int(d)) for r, d in slots])
+
+
+def verify_head(head: Job, drafts, slots, argmax, accepted, workspace: Workspace, maxlogit=None,
+                stream=None) -> None:
+    """Greedy verify: argmax int32 [M], accepted int32 [len(slots)] (device
+    tensors, written), drafts int32 [M] device tensor or None, slots a list of
+    (row0, ndraft) or a slot_array."""
+    arr = slots if isinstance(slots, ctypes.Array) else slot_array(slots)
+    _check(lib().qgemm_verify_head(ctypes.byref(head), drafts.data_ptr() if drafts is not None else None,
+                                   arr, len(arr), argmax.data_ptr(),
+                                   maxlogit.data_ptr() if maxlogit is not None else None,
+                                   accepted.data_ptr(), workspace.ptr, workspace.nbytes,
+                                   _stream_ptr(stream)), "qgemm_verify_head")

@@ -79,8 +79,13 @@ def _stack(cfg: int, bits: int, outliers: bool, layers: int = LAYERS) -> list:
     return mats
 
 
+VOCAB = 248320  # output rows of the lm_head-class verify head
+
+
 def workload(cfg: int, layers: int = LAYERS) -> Workload:
-    """Workload ``cfg`` (1..5).  ``layers`` shrinks workloads 4/5 for tests."""
+    """Workload ``cfg`` (1..6).  ``layers`` shrinks workloads 4/5 for tests.
+    Workload 6 is the verify head: the lm_head-class matrix 5120 -> 248320,
+    4-bit, at M = 6 (one slot, five drafts) and M = 48 (eight such slots)."""
     if cfg == 1:
         mats = [MatrixSpec("linear", 1024, 1024, 4, 0)]
         return Workload(1, "linear 1024x1024 4-bit M=1", mats, [1], _xseeds(1, [1024]))
@@ -100,6 +105,9 @@ def workload(cfg: int, layers: int = LAYERS) -> Workload:
         mats = _stack(5, 5, True, layers)
         return Workload(5, f"{layers}-layer stack 5-bit M sweep", mats,
                         [1, 2, 4, 8, 16, 32, 48, 64], _xseeds(5, [HIDDEN, 17408]))
+    if cfg == 6:
+        mats = [MatrixSpec("lm_head", VOCAB, HIDDEN, 4, 6_000_000)]
+        return Workload(6, "verify head 5120->248320 4-bit", mats, [6, 48], _xseeds(6, [HIDDEN]))
     raise ValueError(f"unknown workload {cfg}")
 
 

@@ -112,3 +112,28 @@ def test_no_cpu_fallback_in_product_path():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "from oracle" not in text and "import oracle" not in text, f
                 assert "qg_oracle" not in text, f
+
+
+def test_verify_head_validation_rejects_before_any_launch():
+    L = qgemm.lib()
+    head = _job(M=6, Y=0)                      # logits not written: allowed
+    ws = qgemm.verify_workspace_bytes(head)
+    assert ws > 0 and ws % 8 == 0
+    assert qgemm.verify_workspace_bytes(_job(M=0, Y=0)) == 0
+    good = qgemm.slot_array([(0, 5)])
+    drafts, am, acc, mx, wsp = 0x50000000, 0x50001000, 0x50002000, 0x50003000, 0x40000000
+
+    def call(h=head, d=drafts, slots=good, n=None, a=am, c=acc, w=wsp, nb=ws):
+        return L.qgemm_verify_head(ctypes.byref(h), d, slots, len(slots) if n is None else n, a, mx, c, w, nb, None)
+
+    assert call(h=_job(M=0, Y=0)) == qgemm.ERR_INVALID_ARG
+    assert call(n=0) == qgemm.ERR_INVALID_ARG
+    assert call(slots=qgemm.slot_array([(0, 0)] * 65)) == qgemm.ERR_INVALID_ARG
+    for bad in ([(-1, 2)], [(0, -1)], [(0, 6)], [(3, 3)], [(0, 5), (6, 0)]):
+        assert call(slots=qgemm.slot_array(bad)) == qgemm.ERR_INVALID_ARG, bad
+    assert call(d=None) == qgemm.ERR_INVALID_ARG           # drafts needed when a slot drafts
+    assert call(a=None) == qgemm.ERR_INVALID_ARG
+    assert call(c=None) == qgemm.ERR_INVALID_ARG
+    assert call(w=0) == qgemm.ERR_INVALID_ARG
+    assert call(w=wsp + 8) == qgemm.ERR_INVALID_ARG
+    assert call(nb=ws - 8) == qgemm.ERR_INVALID_ARG
