@@ -13,6 +13,14 @@ dequantized inside the weight-streaming product; group 32 and 4/5 bits):
   ``s = fp16_RNE(double(max|w|) / Qmax)`` and
   ``q = clamp(RNE(double(w) / double(s)), -Qmax, Qmax)`` (q = 0 when s = 0).
 * ``pack`` / ``unpack``: the tiled group-32 layout, written and read bit by bit.
+* Format variants (a format code in place of ``bits``): ``Q4_G64`` (4-bit
+  symmetric with one scale per 64 weights, the Quasar/q27 wiki's Q4_G64 byte
+  accounting) and ``Q4_ZP`` (4-bit group-32 asymmetric with an integer zero
+  point per group, the INT4 W4A16 weights of the qwen38 model notes):
+  ``s = fp16_RNE((max(0, max w) - min(0, min w)) / 15)``,
+  ``z = clamp(RNE(-min(0, min w) / s), 0, 15)``,
+  ``u = clamp(RNE(w / s) + z, 0, 15)`` and ``w_hat = (u - z) * s``.  For
+  ``Q4_ZP`` the quantizer and ``unpack`` return ``(u, scales, zeros)``.
 * ``sweep``: ``Y[m, n] = sum_k X[m, k] * (q[n, k] * s[n, k//32])`` in fp64,
   ascending k, decoded from the packed bytes.
 * ``compare``: the acceptance test -- relative L2 over a job's Y at most 1e-4
@@ -35,6 +43,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+Q4, Q5, Q4_G64, Q4_ZP = 4, 5, 0x104, 0x204
+FORMATS = (Q4, Q5, Q4_G64, Q4_ZP)
 
 REL_L2_TOL = 1e-4
 MAX_ABS_COEF = 1e-3
@@ -59,11 +70,11 @@ def lib() -> ctypes.CDLL:
         L.oracle_f16_to_f64_array.restype = None
         L.oracle_packed_bytes.argtypes = [ci, i64, i64]
         L.oracle_packed_bytes.restype = i64
-        L.oracle_quantize.argtypes = [vp, i64, i64, i64, ci, vp, vp]
+        L.oracle_quantize.argtypes = [vp, i64, i64, i64, ci, vp, vp, vp]
         L.oracle_quantize.restype = ci
-        L.oracle_pack.argtypes = [vp, vp, i64, i64, ci, vp]
+        L.oracle_pack.argtypes = [vp, vp, vp, i64, i64, ci, vp]
         L.oracle_pack.restype = ci
-        L.oracle_unpack.argtypes = [vp, i64, i64, ci, vp, vp]
+        L.oracle_unpack.argtypes = [vp, i64, i64, ci, vp, vp, vp]
         L.oracle_unpack.restype = ci
         L.oracle_dequant.argtypes = [vp, i64, i64, ci, i64, i64, vp]
         L.oracle_dequant.restype = ci
@@ -101,57 +112,77 @@ def f16_bits_to_f64(h) -> np.ndarray:
     return out.reshape(np.shape(h))
 
 
-def packed_bytes(bits: int, N: int, K: int) -> int:
-    return int(lib().oracle_packed_bytes(bits, N, K))
+def group_size(fmt: int) -> int:
+    return 64 if fmt == Q4_G64 else 32
 
 
-def quantize(W: np.ndarray, bits: int):
-    """Codes q (int8, [N, K]) and scale bits (uint16, [N, K/32])."""
+def packed_bytes(fmt: int, N: int, K: int) -> int:
+    return int(lib().oracle_packed_bytes(fmt, N, K))
+
+
+def quantize(W: np.ndarray, fmt: int):
+    """Codes q (int8, [N, K]) and scale bits (uint16, [N, K/group]); for
+    ``Q4_ZP`` the codes are u (0..15) and the zero points (uint8, [N, K/32])
+    come third."""
     W = np.ascontiguousarray(W, dtype=np.float32)
     N, K = W.shape
+    G = K // group_size(fmt)
     codes = np.empty((N, K), dtype=np.int8)
-    scales = np.empty((N, K // 32), dtype=np.uint16)
-    rc = lib().oracle_quantize(W.ctypes.data, K, N, K, bits, codes.ctypes.data,
-                               scales.ctypes.data)
+    scales = np.empty((N, G), dtype=np.uint16)
+    zeros = np.empty((N, G), dtype=np.uint8) if fmt == Q4_ZP else None
+    rc = lib().oracle_quantize(W.ctypes.data, K, N, K, fmt, codes.ctypes.data,
+                               scales.ctypes.data, None if zeros is None else zeros.ctypes.data)
     if rc == 3:
         raise NonFiniteError("non-finite weight or fp16 scale overflow")
-    return codes, scales
+    if rc:
+        raise ValueError(f"bad format {fmt:#x} or K {K}")
+    return (codes, scales) if zeros is None else (codes, scales, zeros)
 
 
-def pack(codes: np.ndarray, scales: np.ndarray, bits: int) -> np.ndarray:
+def pack(codes: np.ndarray, scales: np.ndarray, fmt: int, zeros: np.ndarray | None = None) -> np.ndarray:
     codes = np.ascontiguousarray(codes, dtype=np.int8)
     scales = np.ascontiguousarray(scales, dtype=np.uint16)
     N, K = codes.shape
-    out = np.empty(packed_bytes(bits, N, K), dtype=np.uint8)
-    lib().oracle_pack(codes.ctypes.data, scales.ctypes.data, N, K, bits, out.ctypes.data)
+    if zeros is not None:
+        zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+    out = np.empty(packed_bytes(fmt, N, K), dtype=np.uint8)
+    rc = lib().oracle_pack(codes.ctypes.data, scales.ctypes.data,
+                           None if zeros is None else zeros.ctypes.data, N, K, fmt, out.ctypes.data)
+    if rc:
+        raise ValueError(f"bad format {fmt:#x}, K {K} or missing zero points")
     return out
 
 
-def quantize_pack(W: np.ndarray, bits: int) -> np.ndarray:
-    c, s = quantize(W, bits)
-    return pack(c, s, bits)
+def quantize_pack(W: np.ndarray, fmt: int) -> np.ndarray:
+    q = quantize(W, fmt)
+    return pack(q[0], q[1], fmt, q[2] if len(q) > 2 else None)
 
 
-def unpack(packed: np.ndarray, N: int, K: int, bits: int):
+def unpack(packed: np.ndarray, N: int, K: int, fmt: int):
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    G = K // group_size(fmt)
     codes = np.empty((N, K), dtype=np.int8)
-    scales = np.empty((N, K // 32), dtype=np.uint16)
-    lib().oracle_unpack(packed.ctypes.data, N, K, bits, codes.ctypes.data, scales.ctypes.data)
-    return codes, scales
+    scales = np.empty((N, G), dtype=np.uint16)
+    zeros = np.empty((N, G), dtype=np.uint8) if fmt == Q4_ZP else None
+    rc = lib().oracle_unpack(packed.ctypes.data, N, K, fmt, codes.ctypes.data, scales.ctypes.data,
+                             None if zeros is None else zeros.ctypes.data)
+    if rc:
+        raise ValueError(f"bad format {fmt:#x} or K {K}")
+    return (codes, scales) if zeros is None else (codes, scales, zeros)
 
 
-def dequant(packed: np.ndarray, N: int, K: int, bits: int, row0: int = 0,
+def dequant(packed: np.ndarray, N: int, K: int, fmt: int, row0: int = 0,
             nrows: int | None = None) -> np.ndarray:
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
     nrows = N - row0 if nrows is None else nrows
     out = np.empty((nrows, K), dtype=np.float64)
-    rc = lib().oracle_dequant(packed.ctypes.data, N, K, bits, row0, nrows, out.ctypes.data)
+    rc = lib().oracle_dequant(packed.ctypes.data, N, K, fmt, row0, nrows, out.ctypes.data)
     if rc:
-        raise ValueError("row range out of bounds")
+        raise ValueError("bad format or row range out of bounds")
     return out
 
 
-def sweep(packed: np.ndarray, N: int, K: int, bits: int, X: np.ndarray, cols=None,
+def sweep(packed: np.ndarray, N: int, K: int, fmt: int, X: np.ndarray, cols=None,
           nthreads: int | None = None) -> np.ndarray:
     """Yref [M, ncols] in fp64 for X fp16 [M, K]; cols = None means all N."""
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
@@ -164,7 +195,7 @@ def sweep(packed: np.ndarray, N: int, K: int, bits: int, X: np.ndarray, cols=Non
         cols = np.ascontiguousarray(np.asarray(cols, dtype=np.int64))
         c_ptr, ncols = cols.ctypes.data, cols.size
     Y = np.empty((M, ncols), dtype=np.float64)
-    rc = lib().oracle_sweep_f64(packed.ctypes.data, N, K, bits, Xb.ctypes.data, K, M,
+    rc = lib().oracle_sweep_f64(packed.ctypes.data, N, K, fmt, Xb.ctypes.data, K, M,
                                 Y.ctypes.data, ncols, c_ptr, ncols, _threads(nthreads))
     if rc:
         raise RuntimeError(f"oracle_sweep_f64 failed ({rc})")
@@ -191,8 +222,8 @@ def compare(Y: np.ndarray, Yref: np.ndarray, X: np.ndarray, smax: float) -> dict
     }
 
 
-def max_scale(packed: np.ndarray, N: int, K: int, bits: int) -> float:
-    _, s = unpack(packed, N, K, bits)
+def max_scale(packed: np.ndarray, N: int, K: int, fmt: int) -> float:
+    s = unpack(packed, N, K, fmt)[1]
     return float(np.abs(f16_bits_to_f64(s)).max())
 
 
@@ -215,10 +246,10 @@ def accept(argmax, drafts, slots) -> list:
     return out
 
 
-def verify_head(packed: np.ndarray, N: int, K: int, bits: int, X: np.ndarray, drafts, slots,
+def verify_head(packed: np.ndarray, N: int, K: int, fmt: int, X: np.ndarray, drafts, slots,
                 nthreads: int | None = None):
     """(argmax [M], max logit [M], accepted per slot, logits [M, N]) in fp64."""
-    Y = sweep(packed, N, K, bits, X, nthreads=nthreads)
+    Y = sweep(packed, N, K, fmt, X, nthreads=nthreads)
     am = argmax_rows(Y)
     mx = Y[np.arange(Y.shape[0]), am]
     return am, mx, accept(am, drafts, slots), Y
