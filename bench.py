@@ -12,7 +12,7 @@ tokens/s per sweep is M / step time.  The workloads that fit in the 256 MB
 last-level cache rotate over enough packed copies (>= 1 GB) that every step
 streams its weights from HBM.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only 2|3|4|5|6]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only 2|3|4|5|6|7|8]
        [--no-cpu] [--stack-layers L]
        python bench.py --copy-calib MIB   (a plain device copy of MIB MiB, the
        reference for scaling the HBM byte counters)
@@ -228,7 +228,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", type=int, default=0,
                     help="time one workload (2, 3 or 4) only; 5 times the 5-bit stack at every M of its "
-                         "sweep; 6 times the verify head")
+                         "sweep; 6 times the verify head; 7 and 8 the group-64 and zero-point 4-bit "
+                         "stacks at M = 1, 8, 48")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--stack-layers", type=int, default=64)
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB")
@@ -277,10 +278,11 @@ def main():
             print(json.dumps(r), flush=True)
         return
 
-    if args.only == 5:
-        # the 5-bit stack at each M of its sweep (same weights, fresh panels);
-        # one JSON line per M, no headline
-        b = Bench(5, layers=args.stack_layers)
+    if args.only in (5, 7, 8):
+        # a stack (5-bit; 7: 4-bit group-64; 8: 4-bit zero-point) at each M
+        # of its sweep (same weights, fresh panels); one JSON line per M, no
+        # headline
+        b = Bench(args.only, layers=args.stack_layers)
         for M in b.wl.Ms:
             b.set_M(M)
             ms, wall = b.run(args.steps, args.warmup)

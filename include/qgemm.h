@@ -39,6 +39,26 @@
  * (8 consecutive k) of the four groups of row r, already in fp16-pair order.
  * Size: qgemm_packed_bytes(); 4.5 (4-bit) / 5.5 (5-bit) bits per weight.
  *
+ * Format variants.  Wherever an argument or field is called `bits` it takes a
+ * format code: 4 and 5 are the formats above; the variants keep the tile grid
+ * and the code words and change the scale group or add zero points.
+ *   QGEMM_FMT_Q4_G64: 4-bit symmetric, one scale per 64 weights (Quasar/q27
+ *     wiki, "Batching & prefill notes": the group-64 format of 4.25 bits per
+ *     weight).  Same quantizer with the amax over 64 consecutive k; K % 64 ==
+ *     0.  Tiles of 1088 bytes: the codes, then s(n, 2kt + h) (h = (k mod 128)
+ *     / 64) as binary16 at byte 1024 + 4r + 2h.  4.25 bits per weight.
+ *   QGEMM_FMT_Q4_ZP: 4-bit group-32 asymmetric with a 4-bit zero point per
+ *     group (the INT4 W4A16 group-32 asymmetric weights of the qwen38 model
+ *     notes, "Path 1 -- vLLM" section).  Per row n and group g:
+ *       lo = min(0, min W), hi = max(0, max W)        (fp32)
+ *       s  = fp16_RNE(((double)hi - (double)lo) / 15)
+ *       z  = 0 if s == 0, else clamp(RNE(-(double)lo / s), 0, 15)
+ *       u  = z if s == 0, else clamp(RNE((double)W / s) + z, 0, 15)
+ *     and W is taken as (u - z) * s.  u is stored in the code words (no
+ *     offset), s at 1024 + 8r + 2j, and z of group j of row r in bits 4j ..
+ *     4j + 3 of the little-endian 16-bit word at byte 1152 + 2r; tiles of
+ *     1184 bytes (4.625 bits per weight).  Padding: u = 0, z = 0, s = +0.
+ *
  * ---------------------------------------------------------------------------
  * Sweep (qgemm_sweep).  For each job: Y[m][n] = sum_k X[m][k] * q[n][k] *
  * s[n][k/32] for m < M, n < N.  X is fp16 (binary16 bits), Y is fp32 and is
@@ -85,10 +105,17 @@ typedef enum {
 #define QGEMM_MAX_M 64
 #define QGEMM_GEMV_MAX_M 8
 
+/* Weight format codes (the `bits` argument and field). */
+#define QGEMM_FMT_Q4 4
+#define QGEMM_FMT_Q5 5
+#define QGEMM_FMT_Q4_G64 0x104
+#define QGEMM_FMT_Q4_ZP 0x204
+
 /* One matrix of a sweep.  Pointers are device pointers.
- *   packed : QG32 tiled buffer from qgemm_pack, 256-byte aligned, read-only
- *   bits   : 4 or 5, as packed
- *   N, K   : 1 <= N <= 2^30; 32 <= K <= 2^24 and K % 32 == 0
+ *   packed : tiled buffer from qgemm_pack, 256-byte aligned, read-only
+ *   bits   : the format code it was packed with (QGEMM_FMT_*)
+ *   N, K   : 1 <= N <= 2^30; 32 <= K <= 2^24 and K % 32 == 0 (64 for
+ *            QGEMM_FMT_Q4_G64)
  *   X      : binary16 [M][ldx], 16-byte aligned, ldx % 8 == 0, K <= ldx <= 2^24
  *   Y      : fp32 [M][ldy], 16-byte aligned, ldy % 4 == 0, ldy >= N
  *   M      : 1 .. QGEMM_MAX_M

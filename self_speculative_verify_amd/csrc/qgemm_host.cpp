@@ -18,8 +18,8 @@ namespace qg {
 hipError_t launch_pack(const float* W, int64_t ldw, int N, int K, int bits, void* packed,
                        unsigned* flag, hipStream_t stream);
 hipError_t launch_fill_zero(void* p, int64_t words, hipStream_t stream);
-int sweep_blocks_per_cu(int kind, int cls);
-hipError_t launch_sweep(int kind, int cls, const SweepArgs& args, int grid, hipStream_t stream);
+int sweep_blocks_per_cu(int kind, int cls, bool all);
+hipError_t launch_sweep(int kind, int cls, bool all, const SweepArgs& args, int grid, hipStream_t stream);
 hipError_t launch_accept(const AcceptArgs& a, unsigned long long* keys, const int32_t* drafts, int32_t* argmax,
                          float* maxval, int32_t* accepted, hipStream_t stream);
 }  // namespace qg
@@ -38,9 +38,10 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int64_t nkt_of(int64_t K) { return (K + qg::kTileK - 1) / qg::kTileK; }
 int64_t nrb_of(int64_t N) { return (N + qg::kTileRows - 1) / qg::kTileRows; }
 
+// bits: a format code (4, 5 or the QGEMM_FMT_* variants)
 bool valid_shape(int bits, int64_t N, int64_t K) {
-  return (bits == 4 || bits == 5) && N >= 1 && N <= kMaxN && K >= qg::kGroup && K <= kMaxK &&
-         K % qg::kGroup == 0;
+  return qg::valid_fmt(bits) && N >= 1 && N <= kMaxN && K >= qg::fmt_group(bits) && K <= kMaxK &&
+         K % qg::fmt_group(bits) == 0;
 }
 
 int path_of(int path, int M) {
@@ -92,6 +93,7 @@ enum Kind { kStreamGemv = 0, kStreamMfma = 1, kGroupMfma = 2 };
 struct Launch {
   int kind;
   int cls;
+  bool all = false;           // some job uses a format beyond the 4/5-bit group-32 ones
   std::vector<JobDesc> descs;
   int64_t total = 0;          // stream: flat units; group: row-block groups
   int64_t rgs = 0;            // stream: row groups (arrival counters)
@@ -133,7 +135,7 @@ int64_t cut_row_groups(const std::vector<JobDesc>& descs, int64_t T, int64_t W) 
   for (int64_t w = 1; w < W; w++) {
     const int64_t f = w * q + std::min(w, rem);  // start of wave w (as in the kernel)
     while (f >= descs[j].uend) j++;
-    const int64_t wt = qg::unit_weight(descs[j].bits), span = (int64_t)descs[j].nkt * wt;
+    const int64_t wt = qg::unit_weight(descs[j].fmt), span = (int64_t)descs[j].nkt * wt;
     const int64_t r = (f - descs[j].ubeg) % span;
     if (r > 0 && r <= span - wt) cuts++;
   }
@@ -153,7 +155,7 @@ int64_t stream_waves_uncached(const std::vector<JobDesc>& descs, int64_t T) {
   std::vector<int64_t> cand = {std::min<int64_t>(qg::kStreamWaves, wmax)};
   for (const auto& d : descs)
     for (int64_t k = 1; k <= 8; k++) {
-      const int64_t per = k * d.nkt * qg::unit_weight(d.bits);
+      const int64_t per = k * d.nkt * qg::unit_weight(d.fmt);
       if (T % per == 0) cand.push_back(T / per);
     }
   int64_t best = -1, best_cuts = 0;
@@ -180,7 +182,7 @@ int64_t stream_waves(const std::vector<JobDesc>& descs, int64_t T) {
   for (const auto& d : descs) {
     key.push_back(d.nkt);
     key.push_back(d.nrg);
-    key.push_back(d.bits);
+    key.push_back(d.fmt);
   }
   static std::mutex mu;
   static std::map<std::vector<int64_t>, int64_t> cache;
@@ -221,6 +223,7 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* k
       dst->kind = kind;
       dst->cls = cls;
     }
+    if (j.bits != qg::kFmtQ4 && j.bits != qg::kFmtQ5) dst->all = true;
     JobDesc d;
     std::memset(&d, 0, sizeof(d));
     d.packed = (const uint8_t*)j.packed;
@@ -232,7 +235,7 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* k
     d.N = (int32_t)j.N;
     d.K = (int32_t)j.K;
     d.M = j.M;
-    d.bits = j.bits;
+    d.fmt = j.bits;
     d.nkt = (int32_t)nkt_of(j.K);
     d.ngroups = (int32_t)(j.K / qg::kGroup);
     d.nrb = (int32_t)nrb_of(j.N);
@@ -246,7 +249,7 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* k
       const int R = qg::stream_rows(kind, cls);
       d.nrg = (d.nrb + R - 1) / R;
       d.ubeg = (int32_t)std::min(dst->total, kMaxSteps);
-      dst->total += (int64_t)d.nrg * d.nkt * qg::unit_weight(d.bits);
+      dst->total += (int64_t)d.nrg * d.nkt * qg::unit_weight(d.fmt);
       d.uend = (int32_t)std::min(dst->total, kMaxSteps);
       d.rg_begin = (int32_t)dst->rgs;
       dst->rgs += d.nrg;
@@ -290,13 +293,13 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* k
   return P;
 }
 
-int blocks_per_cu(int kind, int cls) {
+int blocks_per_cu(int kind, int cls, bool all) {
   static std::mutex mu;
-  static int cache[3][65] = {};
+  static int cache[2][3][65] = {};
   std::lock_guard<std::mutex> g(mu);
-  int& c = cache[kind][cls];
+  int& c = cache[all ? 1 : 0][kind][cls];
   if (c == 0) {
-    c = qg::sweep_blocks_per_cu(kind, cls);
+    c = qg::sweep_blocks_per_cu(kind, cls, all);
     if (c <= 0) c = 1;
   }
   return c;
@@ -457,7 +460,7 @@ qgemm_status run_plan(Plan& P, void* workspace, void* stream) {
     }
     int grid;
     if (l.kind == kGroupMfma) {
-      grid = (int)std::max<int64_t>(1, std::min<int64_t>(l.total, (int64_t)cus * blocks_per_cu(l.kind, l.cls)));
+      grid = (int)std::max<int64_t>(1, std::min<int64_t>(l.total, (int64_t)cus * blocks_per_cu(l.kind, l.cls, l.all)));
     } else {
       args.counters = (int*)(ws + l.counters_off);
       args.slots = (float*)(ws + l.slots_off);
@@ -467,7 +470,7 @@ qgemm_status run_plan(Plan& P, void* workspace, void* stream) {
       args.slot_rows = l.cls;
       grid = (l.nwaves + qg::kStreamWavesPerBlock - 1) / qg::kStreamWavesPerBlock;
     }
-    if (qg::launch_sweep(l.kind, l.cls, args, grid, s) != hipSuccess) return QGEMM_ERR_HIP;
+    if (qg::launch_sweep(l.kind, l.cls, l.all, args, grid, s) != hipSuccess) return QGEMM_ERR_HIP;
   }
   return QGEMM_OK;
 }

@@ -14,6 +14,20 @@ constexpr int kHiOff = 1152;         // 5-bit: bit 4 of every code
 constexpr int kTile4 = 1152;
 constexpr int kTile5 = 1408;
 
+// Weight formats (the public format codes).  All share the tile grid and the
+// 1024 code bytes of a tile; they differ in the scale group and what follows.
+constexpr int kFmtQ4 = 4;            // 4-bit symmetric, group 32
+constexpr int kFmtQ5 = 5;            // 5-bit symmetric, group 32 (high bits at kHiOff)
+constexpr int kFmtG64 = 0x104;       // 4-bit symmetric, group 64: one scale per row and half tile
+constexpr int kFmtZP = 0x204;        // 4-bit asymmetric, group 32: u stored, zero points at kZeroOff
+constexpr int kZeroOff = 1152;       // kFmtZP: 16 rows x one 16-bit word of four 4-bit zero points
+constexpr int kTileG64 = 1088;
+constexpr int kTileZP = 1184;
+inline __host__ __device__ constexpr bool valid_fmt(int f) {
+  return f == kFmtQ4 || f == kFmtQ5 || f == kFmtG64 || f == kFmtZP;
+}
+inline __host__ __device__ constexpr int fmt_group(int f) { return f == kFmtG64 ? 64 : kGroup; }
+
 constexpr int kMaxInline = 12;       // jobs passed by value in the kernel arguments
 constexpr int kXRowBytes = 272;      // LDS row stride of a staged X chunk (256 + 16 pad)
 
@@ -35,13 +49,19 @@ constexpr int kGroupRows = 2;
 constexpr int kStreamRows = 4;
 constexpr int stream_rows(int kind, int cls) { return (void)kind, (void)cls, kStreamRows; }
 
-inline __host__ __device__ int tile_bytes(int bits) { return bits == 4 ? kTile4 : kTile5; }
+inline __host__ __device__ constexpr int tile_bytes(int f) {
+  return f == kFmtQ5 ? kTile5 : f == kFmtG64 ? kTileG64 : f == kFmtZP ? kTileZP : kTile4;
+}
 
-// Stream kernels split work by weight bytes: a step of a 4-bit job weighs 9
-// units, of a 5-bit job 11 (tile bytes / 128), and every wave gets at least
-// kMaxUnitWeight units, so every wave holds at least one step.
-inline __host__ __device__ int unit_weight(int bits) { return tile_bytes(bits) / kTileK; }
-constexpr int kMaxUnitWeight = kTile5 / kTileK;
+// Stream kernels split work by weight bytes: a step weighs its tile bytes /
+// 128 rounded to the nearest unit (9 for the 4-bit formats, 11 for 5-bit),
+// and every wave gets at least kMaxUnitWeight units, so every wave holds at
+// least one step.
+inline __host__ __device__ constexpr int unit_weight(int f) { return (tile_bytes(f) + kTileK / 2) / kTileK; }
+constexpr int kMaxUnitWeight = 11;
+static_assert(unit_weight(kFmtQ4) == 9 && unit_weight(kFmtQ5) == 11 && unit_weight(kFmtG64) == 9 &&
+                  unit_weight(kFmtZP) == 9,
+              "unit weights");
 
 // One job as the kernels see it.  All sizes are derived on the host.
 struct JobDesc {
@@ -54,7 +74,7 @@ struct JobDesc {
   int32_t ubeg;          // stream kernel: units [ubeg, uend) of this job's steps
   int32_t uend;          //   (a step weighs unit_weight(bits) units)
   int32_t N, K;
-  int32_t M, bits;
+  int32_t M, fmt;         // fmt: a weight format code (kFmt*)
   int32_t nkt;           // ceil(K / 128)
   int32_t ngroups;       // K / 32
   int32_t nrb;           // ceil(N / 16)

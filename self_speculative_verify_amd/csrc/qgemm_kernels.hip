@@ -58,68 +58,105 @@ __device__ uint16_t f64_to_f16_bits(double x) {
   return sign | (uint16_t)(((e + 15) << 10) | (int)(r - 1024));
 }
 
-// One thread per (row n of the padded grid, k tile): quantizes the tile's four
-// groups of that row and writes its 4 x 16 code bytes, 8 scale bytes and (5-bit)
-// 4 x 4 high-bit bytes.  No two threads write the same byte.
-template <int BITS>
+// One thread per (row n of the padded grid, k tile): quantizes the tile's
+// groups of that row and writes its 4 x 16 code bytes, its scales and (5-bit)
+// 4 x 4 high-bit bytes or (zero-point format) its 16-bit zero-point word.  No
+// two threads write the same byte.
+//   symmetric (Q4, Q5, G64): s = fp16(amax / Qmax), u = clamp(rint(w / s)) + bias
+//   zero point (ZP): lo = min(0, min w), hi = max(0, max w),
+//     s = fp16((hi - lo) / 15), z = clamp(rint(-lo / s), 0, 15),
+//     u = clamp(rint(w / s) + z, 0, 15)
+template <int F>
 __global__ void __launch_bounds__(256) pack_kernel(const float* __restrict__ W, int64_t ldw, int N,
                                                    int K, int nkt, int64_t total,
                                                    uint8_t* __restrict__ packed,
                                                    unsigned* __restrict__ flag) {
+  constexpr int BITS = F == kFmtQ5 ? 5 : 4;
+  constexpr bool kZP = F == kFmtZP;
+  constexpr int GS = fmt_group(F), NG = kTileK / GS;  // groups of a row in a tile
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= total) return;
   const int n = (int)(idx / nkt), kt = (int)(idx % nkt);
   const int r = n & 15;
-  const int qmax = (1 << (BITS - 1)) - 1, bias = 1 << (BITS - 1);
-  const int G = K / kGroup;
-  uint8_t* tile = packed + ((int64_t)(n >> 4) * nkt + kt) * (BITS == 4 ? kTile4 : kTile5);
+  const int qmax = (1 << (BITS - 1)) - 1, bias = kZP ? 0 : 1 << (BITS - 1);
+  const int G = K / GS;
+  uint8_t* tile = packed + ((int64_t)(n >> 4) * nkt + kt) * tile_bytes(F);
   uint32_t code[4][4];
   uint32_t hi[4] = {0, 0, 0, 0};
-  uint16_t sc[4];
+  uint16_t sc[NG];
+  uint32_t zw = 0;
   bool bad = false;
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int g = 4 * kt + j;
-    int u[32];
+  for (int h = 0; h < NG; h++) {
+    const int g = NG * kt + h;
+    int u[GS];
     uint16_t sb = 0;
     if (n < N && g < G) {
-      const float* w = W + (int64_t)n * ldw + (int64_t)g * kGroup;
-      float v[32];
-      float amax = 0.f;
+      const float* w = W + (int64_t)n * ldw + (int64_t)g * GS;
+      float v[GS];
 #pragma unroll
-      for (int t = 0; t < 32; t++) {
+      for (int t = 0; t < GS; t++) {
         v[t] = w[t];
         if (!isfinite(v[t])) bad = true;
-        amax = fmaxf(amax, fabsf(v[t]));
       }
-      sb = f64_to_f16_bits((double)amax / (double)qmax);
-      if ((sb & 0x7c00u) == 0x7c00u) bad = true;
-      const double s = (double)__builtin_bit_cast(_Float16, sb);
+      if constexpr (!kZP) {
+        float amax = 0.f;
 #pragma unroll
-      for (int t = 0; t < 32; t++) {
-        int q = 0;
-        if (s != 0.0 && isfinite(v[t]) && isfinite(s)) {
-          double qq = rint((double)v[t] / s);
-          qq = fmin(fmax(qq, (double)-qmax), (double)qmax);
-          q = (int)qq;
+        for (int t = 0; t < GS; t++) amax = fmaxf(amax, fabsf(v[t]));
+        sb = f64_to_f16_bits((double)amax / (double)qmax);
+        if ((sb & 0x7c00u) == 0x7c00u) bad = true;
+        const double s = (double)__builtin_bit_cast(_Float16, sb);
+#pragma unroll
+        for (int t = 0; t < GS; t++) {
+          int q = 0;
+          if (s != 0.0 && isfinite(v[t]) && isfinite(s)) {
+            double qq = rint((double)v[t] / s);
+            qq = fmin(fmax(qq, (double)-qmax), (double)qmax);
+            q = (int)qq;
+          }
+          u[t] = q + bias;
         }
-        u[t] = q + bias;
+      } else {
+        float lo = 0.f, hi_ = 0.f;
+#pragma unroll
+        for (int t = 0; t < GS; t++) {
+          lo = v[t] < lo ? v[t] : lo;
+          hi_ = v[t] > hi_ ? v[t] : hi_;
+        }
+        sb = f64_to_f16_bits(((double)hi_ - (double)lo) / 15.0);
+        if ((sb & 0x7c00u) == 0x7c00u) bad = true;
+        const double s = (double)__builtin_bit_cast(_Float16, sb);
+        const bool ok = s != 0.0 && isfinite(s);
+        int z = 0;
+        if (ok) z = (int)fmin(fmax(rint(-(double)lo / s), 0.0), 15.0);
+        zw |= (uint32_t)z << (4 * h);
+#pragma unroll
+        for (int t = 0; t < GS; t++) {
+          int uu = z;
+          if (ok && isfinite(v[t])) uu = (int)fmin(fmax(rint((double)v[t] / s) + z, 0.0), 15.0);
+          u[t] = uu;
+        }
       }
     } else {
 #pragma unroll
-      for (int t = 0; t < 32; t++) u[t] = bias;
+      for (int t = 0; t < GS; t++) u[t] = bias;
     }
-    sc[j] = sb;
+    sc[h] = sb;
+    // the 32-k groups j of this scale group, as code words
 #pragma unroll
-    for (int c = 0; c < 4; c++) {
-      uint32_t word = 0;
+    for (int jj = 0; jj < GS / 32; jj++) {
+      const int j = h * (GS / 32) + jj;
 #pragma unroll
-      for (int e = 0; e < 8; e++) {
-        const int uu = u[8 * c + e];
-        word |= (uint32_t)(uu & 15) << (4 * (e >> 1) + 16 * (e & 1));
-        if (BITS == 5) hi[c] |= (uint32_t)((uu >> 4) & 1) << ((4 + 16 * (e & 1) + 4 * (e >> 1) + j) & 31);
+      for (int c = 0; c < 4; c++) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const int uu = u[32 * jj + 8 * c + e];
+          word |= (uint32_t)(uu & 15) << (4 * (e >> 1) + 16 * (e & 1));
+          if (BITS == 5) hi[c] |= (uint32_t)((uu >> 4) & 1) << ((4 + 16 * (e & 1) + 4 * (e >> 1) + j) & 31);
+        }
+        code[c][j] = word;
       }
-      code[c][j] = word;
     }
   }
 #pragma unroll
@@ -128,8 +165,13 @@ __global__ void __launch_bounds__(256) pack_kernel(const float* __restrict__ W, 
     *(u4_t*)(tile + 16 * (r + 16 * c)) = v;
     if (BITS == 5) *(uint32_t*)(tile + kHiOff + 4 * (r + 16 * c)) = hi[c];
   }
-  u2_t s2 = {(uint32_t)sc[0] | ((uint32_t)sc[1] << 16), (uint32_t)sc[2] | ((uint32_t)sc[3] << 16)};
-  *(u2_t*)(tile + kScaleOff + 8 * r) = s2;
+  if constexpr (NG == 4) {
+    u2_t s2 = {(uint32_t)sc[0] | ((uint32_t)sc[1] << 16), (uint32_t)sc[2] | ((uint32_t)sc[3] << 16)};
+    *(u2_t*)(tile + kScaleOff + 8 * r) = s2;
+  } else {
+    *(uint32_t*)(tile + kScaleOff + 4 * r) = (uint32_t)sc[0] | ((uint32_t)sc[1] << 16);
+  }
+  if constexpr (kZP) *(uint16_t*)(tile + kZeroOff + 2 * r) = (uint16_t)zw;
   if (bad) atomicOr(flag, 1u);
 }
 
@@ -180,17 +222,27 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
   return r;
 }
 
-template <int BITS>
+// Zero-point format: u is stored as is and the subtrahends are per group:
+// -(1024 + z) for the first form, -(64 + z) for the second, as fp16 pairs
+// built from the zero-point word zz (the row's 16-bit word in both halves):
+// 0xE400 | z is -(1024 + z) and 0xD400 | 16 z is -(64 + z), both exact.
+template <int F>
 __device__ __forceinline__ void unpack8(uint32_t w, uint32_t h, int J, h2_t (&q)[4]) {
   constexpr uint32_t kMagic = 0x64006400u;
-  constexpr _Float16 kOff0 = (_Float16)(-1024 - (1 << (BITS - 1)));
-  constexpr _Float16 kOff1 = (_Float16)(-64 - (1 << (BITS - 1)));
-  const h2_t off0 = {kOff0, kOff0}, off1 = {kOff1, kOff1};
+  constexpr int kBias = F == kFmtQ5 ? 16 : 8;
+  constexpr _Float16 kOff0 = (_Float16)(-1024 - kBias);
+  constexpr _Float16 kOff1 = (_Float16)(-64 - kBias);
+  h2_t off0 = {kOff0, kOff0}, off1 = {kOff1, kOff1};
+  if constexpr (F == kFmtZP) {
+    off0 = __builtin_bit_cast(h2_t, and_or(J ? __builtin_amdgcn_alignbit(h, h, 4 * J) : h, 0x000F000Fu, 0xE400E400u));
+    off1 = __builtin_bit_cast(h2_t, and_or(J == 1 ? h : __builtin_amdgcn_alignbit(h, h, (4 * J + 28) & 31),
+                                           0x00F000F0u, 0xD400D400u));
+  }
   const h2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   const uint32_t w2 = w >> 8;
   uint32_t t0 = and_or(w, 0x000F000Fu, kMagic), t1 = and_or(w, 0x00F000F0u, kMagic);
   uint32_t t2 = and_or(w2, 0x000F000Fu, kMagic), t3 = and_or(w2, 0x00F000F0u, kMagic);
-  if constexpr (BITS == 5) {
+  if constexpr (F == kFmtQ5) {
     const uint32_t h0 = __builtin_amdgcn_alignbit(h, h, J);
     const uint32_t h2 = __builtin_amdgcn_alignbit(h, h, J + 8);
     t0 = and_or(h0, 0x00100010u, t0);
@@ -204,6 +256,14 @@ __device__ __forceinline__ void unpack8(uint32_t w, uint32_t h, int J, h2_t (&q)
   q[3] = __builtin_elementwise_fma(__builtin_bit_cast(h2_t, t3), sixteenth, off1);
 }
 
+// The per-row word a format keeps beside the codes, as unpack8 takes it: the
+// 5-bit high word, or the zero-point word in both halves.
+template <int F>
+__device__ __forceinline__ uint32_t side_word(uint32_t h) {
+  if constexpr (F == kFmtZP) return h | (h << 16);
+  return h;
+}
+
 __device__ __forceinline__ h8_t cat8(const h2_t (&q)[4]) {
   h8_t o;
 #pragma unroll
@@ -215,10 +275,10 @@ __device__ __forceinline__ h8_t cat8(const h2_t (&q)[4]) {
 }
 
 // (J is a constant after unrolling, so the rotations take immediates.)
-template <int BITS>
+template <int F>
 __device__ __forceinline__ h8_t unpack_chunk(uint32_t w, uint32_t hi, int J) {
   h2_t q[4];
-  unpack8<BITS>(w, hi, J, q);
+  unpack8<F>(w, hi, J, q);
   return cat8(q);
 }
 
@@ -301,11 +361,13 @@ struct Stream {
   // steps in flight per wave: about 8 tiles (9-11 KB) per wave
   static constexpr int kDepth = 4;
 
-  template <int BITS>
+  // one step's loads: codes, scales (group 64: the pair of word s.x), the
+  // side word (5-bit high bits or zero points) and the X chunk
+  template <int F>
   struct Step {
     u4_t c[kR];
     u2_t s[kR];
-    uint32_t h[BITS == 5 ? kR : 1];
+    uint32_t h[F == kFmtQ5 || F == kFmtZP ? kR : 1];
     u4_t x[kXP];
   };
 
@@ -393,7 +455,7 @@ struct Stream {
           acc[r][m] = v;
         }
     }
-    const int wt = unit_weight(D[j].bits);
+    const int wt = unit_weight(D[j].fmt);
     const int first = D[j].ubeg + rg * nkt * wt;   // first unit of the row group's first step
     const int last = first + (nkt - 1) * wt;       // ... and of its last step
     const int nn = lane & 15;
@@ -474,7 +536,7 @@ struct Stream {
   // its first and last steps; its arrival counter is at counters[rg_begin + rg].
   static __device__ __forceinline__ void span(const Ctx& cx, int j, int rg, int& wf, int& wl) {
     const QG_CONST JobDesc* D = cx.D;
-    const int wt = unit_weight(D[j].bits), nkt = D[j].nkt;
+    const int wt = unit_weight(D[j].fmt), nkt = D[j].nkt;
     const int first = D[j].ubeg + rg * nkt * wt;
     wf = wave_of(first, cx.q, cx.rem);
     wl = wave_of(first + (nkt - 1) * wt, cx.q, cx.rem);
@@ -601,15 +663,22 @@ struct Stream {
   // streamed once) and the X chunk.  X reads outside [0, M) x [0, K) are
   // clamped into the matrix (see above); xlane[p] is the lane's byte offset
   // into X for k = 0.
-  template <int BITS>
-  static __device__ __forceinline__ void load(Step<BITS>& t, const Cur& c, const uint16_t* X,
+  template <int F>
+  static __device__ __forceinline__ void load(Step<F>& t, const Cur& c, const uint16_t* X,
                                               const uint32_t (&xlane)[kXP], int K, int lane) {
 #pragma unroll
     for (int r = 0; r < kR; r++) {
       const uint8_t* tp = c.wp + c.roff[r];
       t.c[r] = __builtin_nontemporal_load(gload_ptr<u4_t>(tp + 16 * lane));
-      t.s[r] = __builtin_nontemporal_load(gload_ptr<u2_t>(tp + kScaleOff + 8 * (lane & 15)));
-      if constexpr (BITS == 5) t.h[r] = __builtin_nontemporal_load(gload_ptr<uint32_t>(tp + kHiOff + 4 * lane));
+      if constexpr (F == kFmtG64) {
+        t.s[r].x = __builtin_nontemporal_load(gload_ptr<uint32_t>(tp + kScaleOff + 4 * (lane & 15)));
+        t.s[r].y = 0u;
+      } else {
+        t.s[r] = __builtin_nontemporal_load(gload_ptr<u2_t>(tp + kScaleOff + 8 * (lane & 15)));
+      }
+      if constexpr (F == kFmtQ5) t.h[r] = __builtin_nontemporal_load(gload_ptr<uint32_t>(tp + kHiOff + 4 * lane));
+      if constexpr (F == kFmtZP)
+        t.h[r] = __builtin_nontemporal_load(gload_ptr<uint16_t>(tp + kZeroOff + 2 * (lane & 15)));
     }
     const uint8_t* xb = (const uint8_t*)X;
     const int k0 = c.kt * kTileK;
@@ -642,25 +711,36 @@ struct Stream {
     }
   }
 
-  template <int BITS>
-  static __device__ __forceinline__ void compute(float (&acc)[kR][kA], const Step<BITS>& t, uint8_t* xs,
+  template <int F>
+  static __device__ __forceinline__ void compute(float (&acc)[kR][kA], const Step<F>& t, uint8_t* xs,
                                                  int lane) {
+    constexpr bool kSide = F == kFmtQ5 || F == kFmtZP;
     if constexpr (kMfma) {
       const f4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int r = 0; r < kR; r++) {
+        const uint32_t side = side_word<F>(t.h[kSide ? r : 0]);
         f4_t p[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          const h8_t q = unpack_chunk<BITS>(t.c[r][j], t.h[BITS == 5 ? r : 0], j);
-          p[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, t.x[j]), q, zero, 0, 0, 0);
+          const h8_t q = unpack_chunk<F>(t.c[r][j], side, j);
+          // group 64: the second half of a group accumulates onto the first
+          const f4_t c0 = (F == kFmtG64 && (j & 1)) ? p[j ^ 1] : zero;
+          p[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, t.x[j]), q, c0, 0, 0, 0);
         }
         const h2_t s01 = scale_pair(t.s[r].x), s23 = scale_pair(t.s[r].y);
         const _Float16 sh[4] = {s01.x, s01.y, s23.x, s23.y};
+        if constexpr (F == kFmtG64) {
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+          for (int h = 0; h < 2; h++)
 #pragma unroll
-          for (int i = 0; i < kA; i++) acc[r][i] = __builtin_fmaf((float)sh[j], p[j][i], acc[r][i]);
+            for (int i = 0; i < kA; i++) acc[r][i] = __builtin_fmaf((float)sh[h], p[2 * h + 1][i], acc[r][i]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int i = 0; i < kA; i++) acc[r][i] = __builtin_fmaf((float)sh[j], p[j][i], acc[r][i]);
+        }
       }
     } else {
       const int c = lane >> 4;
@@ -675,20 +755,25 @@ struct Stream {
       for (int r = 0; r < kR; r++) {
         const h2_t s01 = scale_pair(t.s[r].x), s23 = scale_pair(t.s[r].y);
         const _Float16 sh[4] = {s01.x, s01.y, s23.x, s23.y};
+        const uint32_t side = side_word<F>(t.h[kSide ? r : 0]);
+        float dp[kCap];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
           h2_t q[4];
-          unpack8<BITS>(t.c[r][j], t.h[BITS == 5 ? r : 0], j, q);
-          const float sj = (float)sh[j];
+          unpack8<F>(t.c[r][j], side, j, q);
+          // group 64: the dot products of both halves, then one scale
+          const float sj = (float)sh[F == kFmtG64 ? j >> 1 : j];
+          const bool first = F != kFmtG64 || !(j & 1), last = F != kFmtG64 || (j & 1);
 #pragma unroll
           for (int m = 0; m < kCap; m++) {
             const h8_t x = lds_h8(xs + m * kXRowBytes + 64 * j + 16 * c);
             const h2_t x0 = {x[0], x[1]}, x1 = {x[2], x[3]}, x2 = {x[4], x[5]}, x3 = {x[6], x[7]};
-            float d = __builtin_amdgcn_fdot2(q[0], x0, 0.f, false);
+            float d = __builtin_amdgcn_fdot2(q[0], x0, first ? 0.f : dp[m], false);
             d = __builtin_amdgcn_fdot2(q[1], x1, d, false);
             d = __builtin_amdgcn_fdot2(q[2], x2, d, false);
             d = __builtin_amdgcn_fdot2(q[3], x3, d, false);
-            acc[r][m] = __builtin_fmaf(sj, d, acc[r][m]);
+            dp[m] = d;
+            if (last) acc[r][m] = __builtin_fmaf(sj, d, acc[r][m]);
           }
         }
       }
@@ -703,12 +788,12 @@ struct Stream {
       for (int i = 0; i < kA; i++) acc[r][i] = 0.f;
   }
 
-  // Steps [s0, s1) of job j (local step index rg * NKT + kt), BITS fixed.
-  template <int BITS>
+  // Steps [s0, s1) of job j (local step index rg * NKT + kt), format F.
+  template <int F>
   static __device__ __forceinline__ void segment(Ctx& cx, int j, int s0, int s1, uint8_t* xs) {
     const QG_CONST JobDesc* D = cx.D;
     const int lane = cx.lane;
-    constexpr int TB = BITS == 4 ? kTile4 : kTile5;
+    constexpr int TB = tile_bytes(F);
     const int nkt = D[j].nkt, nrb = D[j].nrb, M = D[j].M, K = D[j].K;
     const int64_t ldx = D[j].ldx;
     const uint16_t* X = D[j].X;
@@ -741,10 +826,10 @@ struct Stream {
     // them at X, which every wave keeps reading and so stays cached, instead
     // of fetching weights again; X smaller than a tile: the last step.
     const uint8_t* xover = 2 * ((int64_t)(M - 1) * ldx + K) >= kTile5 ? (const uint8_t*)X : nullptr;
-    Step<BITS> buf[kDepth];
+    Step<F> buf[kDepth];
 #pragma unroll
     for (int p = 0; p < kDepth; p++) {
-      load<BITS>(buf[p], pc, X, xlane, K, lane);
+      load<F>(buf[p], pc, X, xlane, K, lane);
       if (pleft > 0) {
         advance(pc, nkt, nrb, rstride, TB);
         pleft--;
@@ -759,7 +844,7 @@ struct Stream {
 #pragma unroll
       for (int p = 0; p < kDepth; p++) {
         if (f + p < n) {
-          compute<BITS>(acc, buf[p], xs, lane);
+          compute<F>(acc, buf[p], xs, lane);
           if (kt == nkt - 1 || f + p == n - 1) {
             flush(acc, cx, j, rg);
             zero(acc);
@@ -769,7 +854,7 @@ struct Stream {
             rg++;
           }
         }
-        load<BITS>(buf[p], pc, X, xlane, K, lane);
+        load<F>(buf[p], pc, X, xlane, K, lane);
         if (pleft > 0) {
           advance(pc, nkt, nrb, rstride, TB);
           pleft--;
@@ -779,6 +864,15 @@ struct Stream {
       }
     }
     if (D[j].keys) publish(cx, D[j].keys + (cx.gw % kKeyCopies) * kKeyRows, M);
+  }
+
+  // The steps of job j whose first unit lies in [u0, u1) (units from the
+  // job's first).
+  template <int F>
+  static __device__ __forceinline__ void segment_in(Ctx& cx, int j, int u0, int u1, uint8_t* xs) {
+    constexpr int wt = unit_weight(F);
+    const int s0 = (u0 + wt - 1) / wt, s1 = (u1 + wt - 1) / wt;
+    if (s0 < s1) segment<F>(cx, j, s0, s1, xs);
   }
 
   // Verify head: the segment's best key per row, over the 16 lanes holding
@@ -797,6 +891,9 @@ struct Stream {
   // Inlined into the kernel on purpose: the job table pointer below is the
   // address of the kernel argument in the constant (kernarg) address space,
   // which a by-reference copy on the stack would not be.
+  // kAll: jobs may use every format; else only the 4- and 5-bit group-32
+  // ones (a kernel with fewer paths, so fewer registers)
+  template <bool kAll>
   static __device__ __forceinline__ void run(const SweepArgs& args, uint8_t* xs) {
     Ctx cx;
     cx.D = job_table(args);
@@ -832,15 +929,12 @@ struct Stream {
     // unit lies in the range
     for (int f = cx.a; f < cx.b; j++) {
       const int ub = cx.D[j].ubeg;
-    static_assert(kTile4 / kTileK == 9 && kTile5 / kTileK == 11, "unit weights");
       const int e = cx.D[j].uend < cx.b ? cx.D[j].uend : cx.b;
-      if (cx.D[j].bits == 4) {
-        const int s0 = (f - ub + 8) / 9, s1 = (e - ub + 8) / 9;
-        if (s0 < s1) segment<4>(cx, j, s0, s1, xs);
-      } else {
-        const int s0 = (f - ub + 10) / 11, s1 = (e - ub + 10) / 11;
-        if (s0 < s1) segment<5>(cx, j, s0, s1, xs);
-      }
+      const int fmt = cx.D[j].fmt;
+      if (fmt == kFmtQ4) segment_in<kFmtQ4>(cx, j, f - ub, e - ub, xs);
+      else if (!kAll || fmt == kFmtQ5) segment_in<kFmtQ5>(cx, j, f - ub, e - ub, xs);
+      else if (fmt == kFmtG64) segment_in<kFmtG64>(cx, j, f - ub, e - ub, xs);
+      else segment_in<kFmtZP>(cx, j, f - ub, e - ub, xs);
       f = e;
     }
     if (cx.pend_j0 >= 0 || cx.pend_j1 >= 0) {
@@ -854,11 +948,11 @@ struct Stream {
   }
 };
 
-template <bool kMfma, int kCap>
+template <bool kMfma, int kCap, bool kAll>
 __global__ void __launch_bounds__(64 * kStreamWavesPerBlock) stream_kernel(SweepArgs args) {
   using S = Stream<kMfma, kCap>;
   __shared__ __attribute__((aligned(16))) uint8_t xs[kStreamWavesPerBlock][kMfma ? 16 : kCap * kXRowBytes];
-  S::run(args, xs[threadIdx.x >> 6]);
+  S::template run<kAll>(args, xs[threadIdx.x >> 6]);
 }
 
 // --------------------------------------------------------------------------
@@ -926,17 +1020,19 @@ struct Group {
   static constexpr int kRingBytes = kBufs * kBufBytes > kYBytes ? kBufs * kBufBytes : kYBytes;
   static constexpr int kLdsBytes = kRingBytes + kMPad * 8;           // then one argmax key per row
 
-  template <int BITS>
+  template <int F>
+  static constexpr bool kSide = F == kFmtQ5 || F == kFmtZP;   // a side word per row block
+  template <int F>
   struct Tiles {
     u4_t c[kRG];
-    uint32_t h[BITS == 5 ? kRG : 1];
+    uint32_t h[kSide<F> ? kRG : 1];
   };
   // vector memory instructions of one k tile per wave: X copies, the scale
   // copy, then the weight loads
-  template <int BITS>
-  static constexpr int kLoadsW = kRG * (BITS == 5 ? 2 : 1);
-  template <int BITS>
-  static constexpr int kLoadsTile = kND + 1 + kLoadsW<BITS>;
+  template <int F>
+  static constexpr int kLoadsW = kRG * (kSide<F> ? 2 : 1);
+  template <int F>
+  static constexpr int kLoadsTile = kND + 1 + kLoadsW<F>;
 
   // Direct-to-LDS copy of this wave's X slots of k tile kt (clamped to the
   // last) into the buffer at LDS address buf.  Slot rows past M repeat row
@@ -956,14 +1052,16 @@ struct Group {
     }
   }
 
-  template <int BITS>
-  static __device__ __forceinline__ void load_w(Tiles<BITS>& t, const uint8_t* w0, int64_t rstride,
+  template <int F>
+  static __device__ __forceinline__ void load_w(Tiles<F>& t, const uint8_t* w0, int64_t rstride,
                                                 int nrows, int lane) {
 #pragma unroll
     for (int r = 0; r < kRG; r++) {
       const uint8_t* tp = w0 + (int64_t)(r < nrows ? r : nrows - 1) * rstride;
       t.c[r] = __builtin_nontemporal_load(gload_ptr<u4_t>(tp + 16 * lane));
-      if constexpr (BITS == 5) t.h[r] = __builtin_nontemporal_load(gload_ptr<uint32_t>(tp + kHiOff + 4 * lane));
+      if constexpr (F == kFmtQ5) t.h[r] = __builtin_nontemporal_load(gload_ptr<uint32_t>(tp + kHiOff + 4 * lane));
+      if constexpr (F == kFmtZP)
+        t.h[r] = __builtin_nontemporal_load(gload_ptr<uint16_t>(tp + kZeroOff + 2 * (lane & 15)));
     }
   }
 
@@ -973,31 +1071,31 @@ struct Group {
   // scale copy puts row r's four scales of both row blocks side by side (16
   // bytes per row): lane l copies word l & 1 of row l >> 2, row block
   // (l >> 1) & 1, whose offset from the tile is soff.
-  template <int BITS>
+  template <int F>
   static __device__ __forceinline__ void copies(const JobDesc& d, int kx, uint32_t buf, const uint8_t* wbase,
                                                 uint32_t soff, int wave, int lane) {
-    constexpr int TB = BITS == 4 ? kTile4 : kTile5;
+    constexpr int TB = tile_bytes(F);
     const uint8_t* tile = wbase + (int64_t)(kx < d.nkt ? kx : d.nkt - 1) * TB;
     copy_x(d, kx, buf, wave, lane);
     lds_copy4(tile + soff, buf + (uint32_t)(kXBytes + 256 * wave));
   }
-  template <int BITS>
-  static __device__ __forceinline__ void codes(const JobDesc& d, int kw, Tiles<BITS>& t, const uint8_t* wbase,
+  template <int F>
+  static __device__ __forceinline__ void codes(const JobDesc& d, int kw, Tiles<F>& t, const uint8_t* wbase,
                                                int64_t rstride, int nrows, int lane) {
-    constexpr int TB = BITS == 4 ? kTile4 : kTile5;
-    load_w<BITS>(t, wbase + (int64_t)(kw < d.nkt ? kw : d.nkt - 1) * TB, rstride, nrows, lane);
+    constexpr int TB = tile_bytes(F);
+    load_w<F>(t, wbase + (int64_t)(kw < d.nkt ? kw : d.nkt - 1) * TB, rstride, nrows, lane);
   }
 
   // One unit: row blocks rb0 + kRG * wave + r (r < kRG) of job d, all k tiles.
-  template <int BITS>
+  template <int F>
   static __device__ void run_unit(const JobDesc& d, int rb0, uint8_t* xs, uint32_t xs_lds, int tid) {
-    constexpr int TB = BITS == 4 ? kTile4 : kTile5;
+    constexpr int TB = tile_bytes(F);
     // Issue order: codes of tile 0, then per tile t (the prologue for
     // t < kDepth - 1, else the end of tile t - kDepth + 1): copies of tile t,
     // codes of tile t + 1.  The copies of tile kt are therefore complete once
     // at most this many younger loads of this wave are outstanding: the codes
     // of tile kt + 1 and kDepth - 2 whole tiles.
-    constexpr int kXWait = kLoadsW<BITS> + (kDepth - 2) * kLoadsTile<BITS>;
+    constexpr int kXWait = kLoadsW<F> + (kDepth - 2) * kLoadsTile<F>;
     static_assert(kXWait < 64, "vmcnt range");
     // s_waitcnt encoding (gfx9): vmcnt low 4 bits, expcnt 7, lgkmcnt 15, vmcnt high 2 bits
     constexpr int kXWaitImm = (kXWait & 15) | (7 << 4) | (15 << 8) | ((kXWait >> 4) << 14);
@@ -1010,16 +1108,20 @@ struct Group {
     const int nr = nrows > 0 ? nrows : 1;
     const uint8_t* wbase = d.packed + (int64_t)rbl * rstride;
     const int srb = ((lane >> 1) & 1) < nr ? (lane >> 1) & 1 : nr - 1;
-    const uint32_t soff = (uint32_t)(srb * rstride) + (uint32_t)(kScaleOff + 8 * (lane >> 2) + 4 * (lane & 1));
-    Tiles<BITS> buf[kDepth];
+    // group 64: a row's two scales are one word, which both lanes of the
+    // pair copy (so words 0 and 1 of a row block are the same)
+    const uint32_t soff = (uint32_t)(srb * rstride) +
+                          (uint32_t)(F == kFmtG64 ? kScaleOff + 4 * (lane >> 2)
+                                                  : kScaleOff + 8 * (lane >> 2) + 4 * (lane & 1));
+    Tiles<F> buf[kDepth];
     __builtin_amdgcn_sched_barrier(0);
-    codes<BITS>(d, 0, buf[0], wbase, rstride, nr, lane);
+    codes<F>(d, 0, buf[0], wbase, rstride, nr, lane);
 #pragma unroll
     for (int p = 0; p < kDepth - 1; p++) {
       __builtin_amdgcn_sched_barrier(0);
-      copies<BITS>(d, p, xs_lds + (uint32_t)(p * kBufBytes), wbase, soff, wave, lane);
+      copies<F>(d, p, xs_lds + (uint32_t)(p * kBufBytes), wbase, soff, wave, lane);
       __builtin_amdgcn_sched_barrier(0);
-      codes<BITS>(d, p + 1, buf[p + 1], wbase, rstride, nr, lane);
+      codes<F>(d, p + 1, buf[p + 1], wbase, rstride, nr, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
     f4_t acc[kRG][kMb];
@@ -1049,6 +1151,7 @@ struct Group {
           const uint8_t* xb = xs + p * kBufBytes;
           // scales of row mr: words 0, 1 of row block 0, then of row block 1
           const u4_t sc = *(const u4_t*)(xb + sread);
+          f4_t pr[kRG][kMb];
           // group by group: the A fragments of group j serve all kRG row blocks
 #pragma unroll
           for (int j = 0; j < 4; j++) {
@@ -1057,21 +1160,29 @@ struct Group {
             for (int mb = 0; mb < kMb; mb++) a[mb] = lds_h8(xb + aoff[j] + 4096 * mb);
             // every MFMA of the group is issued before the first of its
             // results is scaled, so the matrix-core latency overlaps
-            f4_t pr[kRG][kMb];
+            // group 64: the odd half of a group accumulates onto the even
+            // half's products, which are scaled once, after it
+            constexpr bool kG64 = F == kFmtG64;
 #pragma unroll
             for (int r = 0; r < kRG; r++) {
-              const h8_t q = unpack_chunk<BITS>(buf[p].c[r][j], buf[p].h[BITS == 5 ? r : 0], j);
-#pragma unroll
-              for (int mb = 0; mb < kMb; mb++) pr[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb], q, zero, 0, 0, 0);
-            }
-#pragma unroll
-            for (int r = 0; r < kRG; r++) {
-              const uint32_t sp = sc[2 * r + (j >> 1)];
-              const float sj = (j & 1) ? scale_f32<1>(sp) : scale_f32<0>(sp);
+              const h8_t q = unpack_chunk<F>(buf[p].c[r][j], side_word<F>(buf[p].h[kSide<F> ? r : 0]), j);
 #pragma unroll
               for (int mb = 0; mb < kMb; mb++)
+                pr[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb], q, (kG64 && (j & 1)) ? pr[r][mb] : zero, 0, 0, 0);
+            }
+            if (!kG64 || (j & 1)) {
 #pragma unroll
-                for (int i = 0; i < 4; i++) acc[r][mb][i] = __builtin_fmaf(sj, pr[r][mb][i], acc[r][mb][i]);
+              for (int r = 0; r < kRG; r++) {
+                // group 32: word j / 2 of the row block holds groups (j & ~1, j | 1);
+                // group 64: word 0 holds halves (0, 1)
+                const uint32_t sp = sc[2 * r + (kG64 ? 0 : j >> 1)];
+                const int hi = kG64 ? j >> 1 : j & 1;
+                const float sj = hi ? scale_f32<1>(sp) : scale_f32<0>(sp);
+#pragma unroll
+                for (int mb = 0; mb < kMb; mb++)
+#pragma unroll
+                  for (int i = 0; i < 4; i++) acc[r][mb][i] = __builtin_fmaf(sj, pr[r][mb][i], acc[r][mb][i]);
+              }
             }
           }
         }
@@ -1080,10 +1191,10 @@ struct Group {
         // they (kept for exact wait counts) re-read the last tile into
         // buffers no wave reads again.
         __builtin_amdgcn_sched_barrier(0);
-        copies<BITS>(d, kt + kDepth - 1, xs_lds + (uint32_t)(((p + kDepth - 1) % kBufs) * kBufBytes), wbase, soff,
-                     wave, lane);
+        copies<F>(d, kt + kDepth - 1, xs_lds + (uint32_t)(((p + kDepth - 1) % kBufs) * kBufBytes), wbase, soff,
+                  wave, lane);
         __builtin_amdgcn_sched_barrier(0);
-        codes<BITS>(d, kt + kDepth, buf[p], wbase, rstride, nr, lane);
+        codes<F>(d, kt + kDepth, buf[p], wbase, rstride, nr, lane);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -1150,7 +1261,7 @@ struct Group {
   }
 };
 
-template <int kMPad>
+template <int kMPad, bool kAll>
 __global__ void __launch_bounds__(64 * group_waves(kMPad)) __attribute__((amdgpu_waves_per_eu(kMPad >= 64 ? 2 : 3)))
 group_kernel(SweepArgs args) {
   using S = Group<kMPad>;
@@ -1171,8 +1282,10 @@ group_kernel(SweepArgs args) {
     while (u >= D[j].grp_end) j++;
     const JobDesc d = D[j];
     const int rb0 = (u - d.grp_begin) * S::kW * kGroupRows;
-    if (d.bits == 4) S::template run_unit<4>(d, rb0, xs, xs_lds, tid);
-    else S::template run_unit<5>(d, rb0, xs, xs_lds, tid);
+    if (d.fmt == kFmtQ4) S::template run_unit<kFmtQ4>(d, rb0, xs, xs_lds, tid);
+    else if (!kAll || d.fmt == kFmtQ5) S::template run_unit<kFmtQ5>(d, rb0, xs, xs_lds, tid);
+    else if (d.fmt == kFmtG64) S::template run_unit<kFmtG64>(d, rb0, xs, xs_lds, tid);
+    else S::template run_unit<kFmtZP>(d, rb0, xs, xs_lds, tid);
   }
 }
 
@@ -1224,12 +1337,11 @@ hipError_t launch_pack(const float* W, int64_t ldw, int N, int K, int bits, void
   const int nrb = (N + kTileRows - 1) / kTileRows;
   const int64_t total = (int64_t)nrb * kTileRows * nkt;
   const int64_t blocks = (total + 255) / 256;
-  if (bits == 4)
-    hipLaunchKernelGGL(pack_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream, W, ldw, N, K, nkt,
-                       total, (uint8_t*)packed, flag);
-  else
-    hipLaunchKernelGGL(pack_kernel<5>, dim3((unsigned)blocks), dim3(256), 0, stream, W, ldw, N, K, nkt,
-                       total, (uint8_t*)packed, flag);
+  // bits: a format code
+  auto f = bits == kFmtQ5 ? pack_kernel<kFmtQ5> : bits == kFmtG64 ? pack_kernel<kFmtG64>
+         : bits == kFmtZP ? pack_kernel<kFmtZP> : pack_kernel<kFmtQ4>;
+  hipLaunchKernelGGL(f, dim3((unsigned)blocks), dim3(256), 0, stream, W, ldw, N, K, nkt, total, (uint8_t*)packed,
+                     flag);
   return hipGetLastError();
 }
 
@@ -1244,37 +1356,40 @@ hipError_t launch_fill_zero(void* p, int64_t words, hipStream_t stream) {
 typedef void (*sweep_fn)(SweepArgs);
 
 // kind: 0 = stream GEMV (cls = rows 1, 2, 4, 8), 1 = stream MFMA (cls 1, 2, 4, 8, 16),
-//       2 = group MFMA (cls = padded rows 32, 48, 64)
-static sweep_fn pick(int kind, int cls) {
+//       2 = group MFMA (cls = padded rows 32, 48, 64); all: some job uses a
+//       format other than the 4- and 5-bit group-32 ones
+template <bool kAll>
+static sweep_fn pick_set(int kind, int cls) {
   if (kind == 0) {
     switch (cls) {
-      case 1: return stream_kernel<false, 1>;
-      case 2: return stream_kernel<false, 2>;
-      case 4: return stream_kernel<false, 4>;
-      case 8: return stream_kernel<false, 8>;
+      case 1: return stream_kernel<false, 1, kAll>;
+      case 2: return stream_kernel<false, 2, kAll>;
+      case 4: return stream_kernel<false, 4, kAll>;
+      case 8: return stream_kernel<false, 8, kAll>;
     }
   } else if (kind == 1) {
     switch (cls) {
-      case 1: return stream_kernel<true, 1>;
-      case 2: return stream_kernel<true, 2>;
-      case 4: return stream_kernel<true, 4>;
-      case 8: return stream_kernel<true, 8>;
-      case 16: return stream_kernel<true, 16>;
+      case 1: return stream_kernel<true, 1, kAll>;
+      case 2: return stream_kernel<true, 2, kAll>;
+      case 4: return stream_kernel<true, 4, kAll>;
+      case 8: return stream_kernel<true, 8, kAll>;
+      case 16: return stream_kernel<true, 16, kAll>;
     }
   } else {
     switch (cls) {
-      case 32: return group_kernel<32>;
-      case 48: return group_kernel<48>;
-      case 64: return group_kernel<64>;
+      case 32: return group_kernel<32, kAll>;
+      case 48: return group_kernel<48, kAll>;
+      case 64: return group_kernel<64, kAll>;
     }
   }
   return nullptr;
 }
+static sweep_fn pick(int kind, int cls, bool all) { return all ? pick_set<true>(kind, cls) : pick_set<false>(kind, cls); }
 
 int sweep_threads(int kind, int cls) { return kind == 2 ? 64 * group_waves(cls) : 64 * kStreamWavesPerBlock; }
 
-int sweep_blocks_per_cu(int kind, int cls) {
-  sweep_fn f = pick(kind, cls);
+int sweep_blocks_per_cu(int kind, int cls, bool all) {
+  sweep_fn f = pick(kind, cls, all);
   if (!f) return 0;
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void*)f, sweep_threads(kind, cls), 0) != hipSuccess)
@@ -1282,8 +1397,8 @@ int sweep_blocks_per_cu(int kind, int cls) {
   return nb;
 }
 
-hipError_t launch_sweep(int kind, int cls, const SweepArgs& args, int grid, hipStream_t stream) {
-  sweep_fn f = pick(kind, cls);
+hipError_t launch_sweep(int kind, int cls, bool all, const SweepArgs& args, int grid, hipStream_t stream) {
+  sweep_fn f = pick(kind, cls, all);
   if (!f) return hipErrorInvalidValue;
   hipLaunchKernelGGL(f, dim3(grid), dim3(sweep_threads(kind, cls)), 0, stream, args);
   return hipGetLastError();

@@ -17,6 +17,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NONFINITE, ERR_HIP = 0, 1, 2, 3, 4
 PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
 MAX_M = 64
 GEMV_MAX_M = 8
+FMT_Q4, FMT_Q5, FMT_Q4_G64, FMT_Q4_ZP = 4, 5, 0x104, 0x204
 
 # every symbol the boundary header declares
 EXPORTS = (

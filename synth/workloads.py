@@ -82,10 +82,16 @@ def _stack(cfg: int, bits: int, outliers: bool, layers: int = LAYERS) -> list:
 VOCAB = 248320  # output rows of the lm_head-class verify head
 
 
+FMT_G64 = 0x104   # 4-bit symmetric, one scale per 64 weights
+FMT_ZP = 0x204    # 4-bit group-32 asymmetric with 4-bit zero points
+
+
 def workload(cfg: int, layers: int = LAYERS) -> Workload:
-    """Workload ``cfg`` (1..6).  ``layers`` shrinks workloads 4/5 for tests.
+    """Workload ``cfg`` (1..8).  ``layers`` shrinks workloads 4/5/7/8 for tests.
     Workload 6 is the verify head: the lm_head-class matrix 5120 -> 248320,
-    4-bit, at M = 6 (one slot, five drafts) and M = 48 (eight such slots)."""
+    4-bit, at M = 6 (one slot, five drafts) and M = 48 (eight such slots).
+    Workloads 7 and 8 are the 64-layer stack in the group-64 and the
+    zero-point 4-bit formats, swept at M = 1, 8 and 48."""
     if cfg == 1:
         mats = [MatrixSpec("linear", 1024, 1024, 4, 0)]
         return Workload(1, "linear 1024x1024 4-bit M=1", mats, [1], _xseeds(1, [1024]))
@@ -108,6 +114,14 @@ def workload(cfg: int, layers: int = LAYERS) -> Workload:
     if cfg == 6:
         mats = [MatrixSpec("lm_head", VOCAB, HIDDEN, 4, 6_000_000)]
         return Workload(6, "verify head 5120->248320 4-bit", mats, [6, 48], _xseeds(6, [HIDDEN]))
+    if cfg == 7:
+        mats = _stack(7, FMT_G64, True, layers)
+        return Workload(7, f"{layers}-layer stack 4-bit group-64 M sweep", mats, [1, 8, 48],
+                        _xseeds(7, [HIDDEN, 17408]))
+    if cfg == 8:
+        mats = _stack(8, FMT_ZP, True, layers)
+        return Workload(8, f"{layers}-layer stack 4-bit zero-point M sweep", mats, [1, 8, 48],
+                        _xseeds(8, [HIDDEN, 17408]))
     raise ValueError(f"unknown workload {cfg}")
 
 
@@ -126,5 +140,11 @@ def ragged_slots(M: int, seed: int = 5_000_777) -> list:
 
 
 def weight_bytes(bits: int, N: int, K: int) -> int:
-    """Algorithmic code + scale bytes: bits/8 per weight plus one fp16 per 32."""
+    """Algorithmic code + scale bytes of a format (4, 5 or a variant code):
+    bits/8 per weight plus one fp16 per group (32, or 64 for the group-64
+    format), plus half a byte per group of zero points in the zero-point one."""
+    if bits == FMT_G64:
+        return N * K // 2 + N * (K // 64) * 2
+    if bits == FMT_ZP:
+        return N * K // 2 + N * (K // 32) * 2 + N * (K // 32) // 2
     return N * K * bits // 8 + N * (K // 32) * 2

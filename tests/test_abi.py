@@ -38,6 +38,13 @@ def test_packed_bytes_agrees_with_oracle():
         for N, K in [(1, 32), (15, 96), (16, 128), (1024, 1024), (34816, 5120), (5120, 17408),
                      (7168, 5120), (33, 416)]:
             assert qgemm.packed_bytes(bits, N, K) == oracle.packed_bytes(bits, N, K) > 0
+    for fmt in (qgemm.FMT_Q4_G64, qgemm.FMT_Q4_ZP):
+        for N, K in [(1, 64), (15, 192), (16, 128), (34816, 5120), (5120, 17408), (33, 448)]:
+            assert qgemm.packed_bytes(fmt, N, K) == oracle.packed_bytes(fmt, N, K) > 0
+    assert qgemm.packed_bytes(qgemm.FMT_Q4_ZP, 3, 96) == oracle.packed_bytes(qgemm.FMT_Q4_ZP, 3, 96) > 0
+    assert qgemm.packed_bytes(qgemm.FMT_Q4_G64, 16, 96) == 0          # K % 64
+    assert qgemm.packed_bytes(qgemm.FMT_Q4_G64, 16, 32) == 0
+    assert qgemm.packed_bytes(0x304, 16, 128) == 0
     assert qgemm.packed_bytes(3, 16, 128) == 0
     assert qgemm.packed_bytes(4, 16, 100) == 0
     assert qgemm.packed_bytes(4, 0, 128) == 0
@@ -59,6 +66,7 @@ def _job(**kw):
 
 BAD = [
     dict(M=0), dict(M=65), dict(bits=3), dict(bits=8), dict(K=100), dict(K=0), dict(N=0),
+    dict(bits=0x104, K=96, ldx=96), dict(bits=0x304), dict(bits=0x105),
     dict(packed=0), dict(X=0), dict(Y=0), dict(packed=0x100080), dict(X=0x200008),
     dict(Y=0x10000004), dict(ldx=255), dict(ldx=260), dict(ldy=63), dict(ldy=66),
     dict(Y=0x200000),                      # Y overlaps X
@@ -74,7 +82,8 @@ def test_validation_rejects(kw):
 
 
 def test_validation_accepts_and_sizes_workspace():
-    jobs = [_job(), _job(Y=0x20000000, M=33, bits=5, N=17, K=416, ldx=416, ldy=20)]
+    jobs = [_job(), _job(Y=0x20000000, M=33, bits=5, N=17, K=416, ldx=416, ldy=20),
+            _job(Y=0x30000000, bits=0x104, K=448, ldx=448), _job(Y=0x38000000, bits=0x204, M=20)]
     ws = qgemm.workspace_bytes(jobs)
     assert ws > 0 and ws % 256 == 0
     assert qgemm.validate(jobs, qgemm.PATH_AUTO, 0x40000000, ws) == qgemm.OK

@@ -1,6 +1,7 @@
 """GPU parity at full size: the 64-layer 27B-class stacks (workload 4: 4-bit,
-M = 48; workload 5: 5-bit, M swept over 1..64), swept in one call over all
-256 matrices exactly as the benchmark launches them.
+M = 48; workload 5: 5-bit, M swept over 1..64; workloads 7 and 8: the
+group-64 and zero-point 4-bit formats at M = 1, 8, 48), swept in one call over
+all 256 matrices exactly as the benchmark launches them.
 
 The weights are generated on the device (Philox twin of the host generator),
 packed on the device, and checked on samples the oracle computes one by one:
@@ -112,7 +113,7 @@ def torch_isfinite_all(Y):
 
 
 def _check_pack_blocks(st):
-    tb = 1152 if st.wl.matrices[0].bits == 4 else 1408
+    tb = oracle.packed_bytes(st.wl.matrices[0].bits, 16, 128)
     for i, m in enumerate(st.wl.matrices):
         nkt = (m.K + 127) // 128
         nrb = (m.N + 15) // 16
@@ -154,3 +155,16 @@ def test_fullsize_workload5(M):
             a, b = Ys[i].double(), Yo[i].double()
             rel = (torch.linalg.norm(a - b) / torch.linalg.norm(a)).item()
             assert rel <= 2 * oracle.REL_L2_TOL, f"{m.name}: paths differ rel {rel}"
+
+
+@pytest.mark.parametrize("cfg", [7, 8])
+def test_fullsize_format_stack_pack_blocks(cfg):
+    _check_pack_blocks(stack(cfg))
+
+
+@pytest.mark.parametrize("cfg,M", [(7, 1), (7, 8), (7, 48), (8, 1), (8, 8), (8, 48)])
+def test_fullsize_format_stack(cfg, M):
+    st = stack(cfg)
+    say(f"workload {cfg} M={M}")
+    X, Ys = _sweep_all(st, M)
+    _check_samples(st, M, X, Ys)

@@ -76,3 +76,13 @@ def test_workload_shapes():
     for M in w5.Ms:
         slots = workloads.ragged_slots(M)
         assert sum(slots) == M and all(1 <= s <= 7 for s in slots)
+
+
+def test_weight_bytes_of_every_format_match_the_packed_size():
+    """For tile-aligned shapes the packed buffer holds exactly the algorithmic
+    code, scale and zero-point bytes."""
+    from oracle import oracle
+
+    for fmt in (4, 5, workloads.FMT_G64, workloads.FMT_ZP):
+        for N, K in [(34816, 5120), (5120, 17408), (16, 128)]:
+            assert workloads.weight_bytes(fmt, N, K) == oracle.packed_bytes(fmt, N, K)
