@@ -12,7 +12,7 @@ tokens/s per sweep is M / step time.  The workloads that fit in the 256 MB
 last-level cache rotate over enough packed copies (>= 1 GB) that every step
 streams its weights from HBM.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only 2|3|4|5|6|7|8]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only 2|3|4|5|6|7|8|9]
        [--no-cpu] [--stack-layers L]
        python bench.py --copy-calib MIB   (a plain device copy of MIB MiB, the
        reference for scaling the HBM byte counters)
@@ -194,6 +194,93 @@ class Bench:
         }
 
 
+def round_bench(args):
+    """Round replay: the 4-bit 64-layer stack as one sweep per matrix in layer
+    order (256 launches, as an engine that interleaves other work between
+    layers issues them), then the verify head over the lm_head-class matrix,
+    at M = 6 (one slot, five drafts).  Times a round issued call by call
+    against the same round replayed as one graph, and the host time to issue
+    each; one JSON line."""
+    import ctypes
+
+    import torch
+
+    from self_speculative_verify_amd import qgemm as q
+    from synth import workloads
+
+    M = 6
+    b = Bench(4, layers=args.stack_layers, rotate_bytes=0)
+    b.set_M(M)
+    h = Bench(6, rotate_bytes=0)
+    dev = torch.device("cuda:0")
+    jobs = b.jobsets[0]
+    mh = h.wl.matrices[0]
+    head = q.make_head_job(h.copies[0][0], mh.bits, mh.N, mh.K, b.X[mh.K], M)
+    slots = [(0, M - 1)]
+    drafts = torch.zeros(M, dtype=torch.int32, device=dev)
+    am = torch.empty(M, dtype=torch.int32, device=dev)
+    acc = torch.empty(1, dtype=torch.int32, device=dev)
+    sweeps = [([j], q.PATH_AUTO) for j in jobs]
+    # call by call: one workspace per sweep (a workspace's layout follows its jobs)
+    wss = [q.Workspace(q.workspace_bytes(j, p), device=dev) for j, p in sweeps]
+    arrs = [q.job_array(j) for j, _ in sweeps]
+    vws = q.Workspace(q.verify_workspace_bytes(head), device=dev)
+    slot_arr = q.slot_array(slots)
+    L = q.lib()
+    st = torch.cuda.current_stream()
+    sp = st.cuda_stream
+
+    def eager():
+        for a, ws in zip(arrs, wss):
+            L.qgemm_sweep(a, 1, ws.ptr, ws.nbytes, sp)
+        L.qgemm_verify_head(ctypes.byref(head), drafts.data_ptr(), slot_arr, 1, am.data_ptr(), None,
+                            acc.data_ptr(), vws.ptr, vws.nbytes, sp)
+
+    rsw = q.round_sweeps(sweeps)
+    rws = q.Workspace(q.round_workspace_bytes(rsw, head), device=dev)
+    rnd = q.Round(rsw, rws, head, drafts, slots, am, acc)
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        host = (time.perf_counter() - t0) / steps
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps, host * 1e3
+
+    # the fused alternative: every matrix in one launch, then the head
+    fused_arr = q.job_array(jobs)
+    fws = q.Workspace(q.workspace_bytes(jobs), device=dev)
+
+    def fused():
+        L.qgemm_sweep(fused_arr, len(jobs), fws.ptr, fws.nbytes, sp)
+        L.qgemm_verify_head(ctypes.byref(head), drafts.data_ptr(), slot_arr, 1, am.data_ptr(), None,
+                            acc.data_ptr(), vws.ptr, vws.nbytes, sp)
+
+    eager_ms, eager_host = timed(eager, args.steps, args.warmup)
+    graph_ms, graph_host = timed(rnd.launch, args.steps, args.warmup)
+    fused_ms, fused_host = timed(fused, args.steps, args.warmup)
+    torch.cuda.synchronize()
+    rnd.destroy()
+    wb = b.weight_bytes + workloads.weight_bytes(mh.bits, mh.N, mh.K)
+    print(json.dumps({
+        "workload": f"round: {len(jobs)} one-matrix sweeps of the {args.stack_layers}-layer 4-bit stack + verify head, M={M}",
+        "kernels_per_round": rnd.kernels if rnd.handle else len(jobs) + 2,
+        "eager_ms": round(eager_ms, 4), "eager_host_ms": round(eager_host, 4),
+        "graph_ms": round(graph_ms, 4), "graph_host_ms": round(graph_host, 4),
+        "fused_launch_ms": round(fused_ms, 4),
+        "graph_speedup": round(eager_ms / graph_ms, 3),
+        "graph_weight_GBps": round(wb / (graph_ms / 1e3) / 1e9, 1),
+        "weight_bytes": wb,
+    }), flush=True)
+
+
 def cpu_baseline():
     """The oracle, untuned, on the host cores: the full M = 1 sweep of the
     34816 x 5120 4-bit gate+up matrix (generation and packing untimed)."""
@@ -229,7 +316,8 @@ def main():
     ap.add_argument("--only", type=int, default=0,
                     help="time one workload (2, 3 or 4) only; 5 times the 5-bit stack at every M of its "
                          "sweep; 6 times the verify head; 7 and 8 the group-64 and zero-point 4-bit "
-                         "stacks at M = 1, 8, 48")
+                         "stacks at M = 1, 8, 48; 9 a round of per-matrix sweeps plus the verify head, "
+                         "issued call by call and replayed as one graph")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--stack-layers", type=int, default=64)
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB")
@@ -276,6 +364,10 @@ def main():
             r["rounds_per_s"] = round(1e3 / ms, 1)
             r["plain_sweep_ms"] = round(ms_sweep, 5)
             print(json.dumps(r), flush=True)
+        return
+
+    if args.only == 9:
+        round_bench(args)
         return
 
     if args.only in (5, 7, 8):

@@ -150,8 +150,12 @@ qgemm_status qgemm_pack(const float* W, int64_t ldw, int64_t N, int64_t K, int b
  * the job table (more than 12 jobs), split-K arrival counters and partial
  * sums.  The buffer must be zero-filled before its first use (for instance
  * with qgemm_workspace_init); every completed sweep leaves its counters at
- * zero again.  A workspace serves one sweep at a time: sweeps that overlap on
- * one workspace race. */
+ * zero again, so the same set of jobs (same shapes and path) may sweep on it
+ * any number of times.  Its layout depends on those shapes: before a
+ * different set of jobs uses a workspace, zero-fill it again (or keep one
+ * workspace per set of jobs, or record the sweeps as a round, below, whose
+ * layout serves all of them).  A workspace serves one sweep at a time: sweeps
+ * that overlap on one workspace race. */
 size_t qgemm_workspace_bytes(const qgemm_job* jobs, int njobs, int path);
 
 /* Zero-fill `ws_bytes` (a multiple of 4) of a workspace with a fill kernel on
@@ -213,6 +217,59 @@ size_t qgemm_verify_workspace_bytes(const qgemm_job* head);
 qgemm_status qgemm_verify_head(const qgemm_job* head, const int32_t* drafts, const qgemm_slot* slots, int nslots,
                                int32_t* argmax, float* maxlogit, int32_t* accepted, void* workspace,
                                size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Round replay.  A decode round issues the same launches every step -- the
+ * weight sweeps in dependency order (one per layer's matrix group, say), then
+ * the verify head -- on the same buffers, and the host cost of issuing them
+ * one call at a time adds up (Quasar/q27 wiki: "decode physics" paragraph, a
+ * residual tail of about 140 launches per token; intro bullets, whole
+ * fused-verify rounds replayed as shape-keyed graphs).  qgemm_round_create
+ * records one round as a HIP graph; qgemm_round_launch replays it on any
+ * stream with one call.  The graph holds kernel launches only (no copies or
+ * memsets): job tables are uploaded into the workspace at creation.
+ *
+ *   sweeps    : host array of nsweeps (>= 0) sweeps, recorded in order; each
+ *               as qgemm_sweep_path would run it (its jobs and path)
+ *   head...   : an optional verify head (NULL: none, and then nsweeps >= 1) with
+ *               the arguments of qgemm_verify_head, recorded last
+ *   workspace : qgemm_round_workspace_bytes() bytes, 256-byte aligned,
+ *               zero-filled before creation; it holds the tables of every
+ *               sweep and one scratch region the sweeps share (they run in
+ *               order) and must stay untouched while the round exists
+ *   stream    : the tables are copied on it and it is synchronized once;
+ *               recording itself uses a stream of the library's own
+ *   out       : the new round (NULL on error)
+ * Pointers and shapes are fixed at creation; buffer contents are read when
+ * the round runs, so a caller refills X (and drafts) and replays.  The caller
+ * keys rounds by shape and pointers and keeps as many as it likes.  Replays
+ * on one workspace must not overlap.  Creation validates everything first
+ * (QGEMM_ERR_INVALID_ARG before any HIP call) and may allocate host memory
+ * and a HIP graph, freed by qgemm_round_destroy. */
+typedef struct qgemm_round_s qgemm_round;
+
+typedef struct {
+  const qgemm_job* jobs;  /* host array of njobs jobs, read during creation only */
+  int32_t njobs;
+  int32_t path;           /* qgemm_path */
+} qgemm_round_sweep;
+
+size_t qgemm_round_workspace_bytes(const qgemm_round_sweep* sweeps, int nsweeps, const qgemm_job* head);
+
+qgemm_status qgemm_round_create(const qgemm_round_sweep* sweeps, int nsweeps, const qgemm_job* head,
+                                const int32_t* drafts, const qgemm_slot* slots, int nslots, int32_t* argmax,
+                                float* maxlogit, int32_t* accepted, void* workspace, size_t ws_bytes,
+                                void* stream, qgemm_round** out);
+
+/* Replay the round on `stream` (asynchronous, one graph launch). */
+qgemm_status qgemm_round_launch(const qgemm_round* round, void* stream);
+
+/* Kernel launches one replay makes (0 for NULL). */
+int qgemm_round_kernels(const qgemm_round* round);
+
+/* Free the round (NULL is a no-op).  Synchronize the streams of its replays
+ * first. */
+void qgemm_round_destroy(qgemm_round* round);
 
 /* The argument checks of qgemm_sweep_path alone (host only, no HIP call). */
 qgemm_status qgemm_validate(const qgemm_job* jobs, int njobs, int path, void* workspace,

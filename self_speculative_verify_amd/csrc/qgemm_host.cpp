@@ -106,9 +106,18 @@ struct Launch {
 // Flat units and row-block groups are 32-bit in the kernels.
 constexpr int64_t kMaxSteps = ((int64_t)1 << 31) - 1;
 
+// Workspace of a plan: the job tables of its launches, then their arrival
+// counters, then their partial-sum slots (three regions, each a 256-byte
+// multiple).  A completed sweep leaves its counters at zero and its slots
+// holding stale sums, so sweeps that run one after another may share the
+// counter and slot regions as long as no counter ever lands on another
+// plan's slots or table: counters need a region of their own.
 struct Plan {
   std::vector<Launch> launches;
-  size_t total = 0;
+  size_t table_bytes = 0;
+  size_t counter_bytes = 0;
+  size_t slot_bytes = 0;
+  size_t total = 0;           // the three regions, at least 256
   bool ok = true;             // false: a launch exceeds the 32-bit unit range
 };
 
@@ -256,7 +265,7 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* k
     }
     dst->descs.push_back(d);
   }
-  size_t off = 0;
+  size_t off = 0, coff = 0, soff = 0;
   for (auto& l : P.launches) {
     if (l.total > kMaxSteps) {
       P.ok = false;
@@ -282,14 +291,17 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* k
     }
     if (l.kind != kGroupMfma) {
       l.nwaves = (int)stream_waves(l.descs, l.total);
-      l.counters_off = off;
-      off = round_up(off + (size_t)l.rgs * sizeof(int), 256);
-      l.slots_off = off;
+      l.counters_off = coff;
+      coff = round_up(coff + (size_t)l.rgs * sizeof(int), 256);
+      l.slots_off = soff;
       const size_t slot_floats = (size_t)l.cls * qg::stream_rows(l.kind, l.cls) * qg::kTileRows;
-      off = round_up(off + (size_t)2 * l.nwaves * slot_floats * sizeof(float), 256);
+      soff = round_up(soff + (size_t)2 * l.nwaves * slot_floats * sizeof(float), 256);
     }
   }
-  P.total = off ? off : 256;
+  P.table_bytes = off;
+  P.counter_bytes = coff;
+  P.slot_bytes = soff;
+  P.total = std::max<size_t>(off + coff + soff, 256);
   return P;
 }
 
@@ -318,6 +330,9 @@ int cu_count() {
 }
 
 qgemm_status run_plan(Plan& P, void* workspace, void* stream);
+qgemm_status upload_tables(const Plan& P, uint8_t* tables, hipStream_t s);
+qgemm_status launch_plan(const Plan& P, uint8_t* tables, uint8_t* counters, uint8_t* slots, hipStream_t s);
+int grid_of(const Launch& l);
 
 }  // namespace
 
@@ -396,14 +411,18 @@ size_t qgemm_verify_workspace_bytes(const qgemm_job* head) {
   return P.ok ? verify_total(P) : 0;
 }
 
-qgemm_status qgemm_verify_head(const qgemm_job* head, const int32_t* drafts, const qgemm_slot* slots, int nslots,
-                               int32_t* argmax, float* maxlogit, int32_t* accepted, void* workspace,
-                               size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of a verify head call (host only) and the acceptance kernel's
+// arguments.
+qgemm_status head_args(const qgemm_job* head, const int32_t* drafts, const qgemm_slot* slots, int nslots,
+                       const int32_t* argmax, const int32_t* accepted, qg::AcceptArgs& a) {
   qgemm_status st = validate(head, 1, QGEMM_PATH_AUTO, true);
   if (st != QGEMM_OK) return st;
-  if (!workspace || !aligned(workspace, 256) || !argmax || !accepted) return QGEMM_ERR_INVALID_ARG;
+  if (!argmax || !accepted) return QGEMM_ERR_INVALID_ARG;
   if (!slots || nslots < 1 || nslots > qg::kMaxSlots) return QGEMM_ERR_INVALID_ARG;
-  qg::AcceptArgs a;
   std::memset(&a, 0, sizeof(a));
   a.nslots = nslots;
   a.M = head->M;
@@ -416,6 +435,22 @@ qgemm_status qgemm_verify_head(const qgemm_job* head, const int32_t* drafts, con
     a.ndraft[i] = sl.ndraft;
   }
   if (any_draft && !drafts) return QGEMM_ERR_INVALID_ARG;
+  return QGEMM_OK;
+}
+
+constexpr size_t kKeyBytes = (size_t)qg::kKeyCopies * qg::kKeyRows * sizeof(unsigned long long);
+
+}  // namespace
+
+extern "C" {
+
+qgemm_status qgemm_verify_head(const qgemm_job* head, const int32_t* drafts, const qgemm_slot* slots, int nslots,
+                               int32_t* argmax, float* maxlogit, int32_t* accepted, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  qg::AcceptArgs a;
+  qgemm_status st = head_args(head, drafts, slots, nslots, argmax, accepted, a);
+  if (st != QGEMM_OK) return st;
+  if (!workspace || !aligned(workspace, 256)) return QGEMM_ERR_INVALID_ARG;
   const Plan P0 = make_plan(head, 1, QGEMM_PATH_AUTO);
   if (!P0.ok) return QGEMM_ERR_UNSUPPORTED;
   if (ws_bytes < verify_total(P0)) return QGEMM_ERR_INVALID_ARG;
@@ -428,6 +463,144 @@ qgemm_status qgemm_verify_head(const qgemm_job* head, const int32_t* drafts, con
              : QGEMM_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// round replay: the sweeps of a round and its verify head as one HIP graph
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+struct qgemm_round_s {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  int kernels = 0;
+};
+
+namespace {
+
+// Plans of a round and its workspace layout: every sweep's tables one after
+// another, then one counter region and one slot region that all sweeps share
+// (they run in order; each region as large as the largest sweep's), then the
+// head's argmax keys.
+struct RoundPlan {
+  std::vector<Plan> sweeps;
+  Plan head;
+  bool has_head = false;
+  std::vector<size_t> table_off;
+  size_t head_table_off = 0, counters_off = 0, slots_off = 0, keys_off = 0, total = 0;
+};
+
+qgemm_status round_plan(const qgemm_round_sweep* sweeps, int nsweeps, const qgemm_job* head, RoundPlan& R,
+                        unsigned long long* keys_base) {
+  if (nsweeps < 0 || (nsweeps > 0 && !sweeps) || (nsweeps == 0 && !head)) return QGEMM_ERR_INVALID_ARG;
+  size_t tables = 0, counters = 0, slots = 0;
+  for (int i = 0; i < nsweeps; i++) {
+    const qgemm_status st = validate(sweeps[i].jobs, sweeps[i].njobs, sweeps[i].path);
+    if (st != QGEMM_OK) return st;
+    R.sweeps.push_back(make_plan(sweeps[i].jobs, sweeps[i].njobs, sweeps[i].path));
+    if (!R.sweeps.back().ok) return QGEMM_ERR_UNSUPPORTED;
+    R.table_off.push_back(tables);
+    tables += R.sweeps.back().table_bytes;
+    counters = std::max(counters, R.sweeps.back().counter_bytes);
+    slots = std::max(slots, R.sweeps.back().slot_bytes);
+  }
+  if (head) {
+    const qgemm_status st = validate(head, 1, QGEMM_PATH_AUTO, true);
+    if (st != QGEMM_OK) return st;
+    R.has_head = true;
+    R.head_table_off = tables;
+    R.head = make_plan(head, 1, QGEMM_PATH_AUTO);
+    if (!R.head.ok) return QGEMM_ERR_UNSUPPORTED;
+    tables += R.head.table_bytes;
+    counters = std::max(counters, R.head.counter_bytes);
+    slots = std::max(slots, R.head.slot_bytes);
+  }
+  R.counters_off = tables;
+  R.slots_off = tables + counters;
+  R.keys_off = round_up(tables + counters + slots, 256);
+  R.total = std::max<size_t>(R.keys_off + (head ? kKeyBytes : 0), 256);
+  if (head && keys_base) {
+    // the head's jobs carry the key pointer
+    R.head = make_plan(head, 1, QGEMM_PATH_AUTO, (unsigned long long*)((uint8_t*)keys_base + R.keys_off));
+  }
+  return QGEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qgemm_round_workspace_bytes(const qgemm_round_sweep* sweeps, int nsweeps, const qgemm_job* head) {
+  RoundPlan R;
+  return round_plan(sweeps, nsweeps, head, R, nullptr) == QGEMM_OK ? R.total : 0;
+}
+
+qgemm_status qgemm_round_create(const qgemm_round_sweep* sweeps, int nsweeps, const qgemm_job* head,
+                                const int32_t* drafts, const qgemm_slot* slots, int nslots, int32_t* argmax,
+                                float* maxlogit, int32_t* accepted, void* workspace, size_t ws_bytes,
+                                void* stream, qgemm_round** out) {
+  if (!out) return QGEMM_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!workspace || !aligned(workspace, 256)) return QGEMM_ERR_INVALID_ARG;
+  qg::AcceptArgs a;
+  if (head) {
+    const qgemm_status st = head_args(head, drafts, slots, nslots, argmax, accepted, a);
+    if (st != QGEMM_OK) return st;
+  }
+  RoundPlan R;
+  qgemm_status st = round_plan(sweeps, nsweeps, head, R, (unsigned long long*)workspace);
+  if (st != QGEMM_OK) return st;
+  if (ws_bytes < R.total) return QGEMM_ERR_INVALID_ARG;
+  uint8_t* ws = (uint8_t*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  // tables in place (and every kernel's grid known) before recording starts
+  for (size_t i = 0; i < R.sweeps.size(); i++) {
+    if ((st = upload_tables(R.sweeps[i], ws + R.table_off[i], s)) != QGEMM_OK) return st;
+    for (const auto& l : R.sweeps[i].launches) (void)grid_of(l);
+  }
+  if (R.has_head) {
+    if ((st = upload_tables(R.head, ws + R.head_table_off, s)) != QGEMM_OK) return st;
+    for (const auto& l : R.head.launches) (void)grid_of(l);
+  }
+  if (hipStreamSynchronize(s) != hipSuccess) return QGEMM_ERR_HIP;
+  hipStream_t cs = nullptr;
+  if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return QGEMM_ERR_HIP;
+  qgemm_round* r = new qgemm_round();
+  bool ok = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) == hipSuccess;
+  bool capturing = ok;
+  for (size_t i = 0; ok && i < R.sweeps.size(); i++) {
+    ok = launch_plan(R.sweeps[i], ws + R.table_off[i], ws + R.counters_off, ws + R.slots_off, cs) == QGEMM_OK;
+    r->kernels += (int)R.sweeps[i].launches.size();
+  }
+  if (ok && R.has_head) {
+    ok = launch_plan(R.head, ws + R.head_table_off, ws + R.counters_off, ws + R.slots_off, cs) == QGEMM_OK &&
+         qg::launch_accept(a, (unsigned long long*)(ws + R.keys_off), drafts, argmax, maxlogit, accepted, cs) ==
+             hipSuccess;
+    r->kernels += (int)R.head.launches.size() + 1;
+  }
+  if (capturing) ok = hipStreamEndCapture(cs, &r->graph) == hipSuccess && ok;
+  ok = ok && hipGraphInstantiate(&r->exec, r->graph, nullptr, nullptr, 0) == hipSuccess;
+  if (hipStreamDestroy(cs) != hipSuccess) ok = false;
+  if (!ok) {
+    qgemm_round_destroy(r);
+    return QGEMM_ERR_HIP;
+  }
+  *out = r;
+  return QGEMM_OK;
+}
+
+qgemm_status qgemm_round_launch(const qgemm_round* r, void* stream) {
+  if (!r || !r->exec) return QGEMM_ERR_INVALID_ARG;
+  return hipGraphLaunch(r->exec, (hipStream_t)stream) == hipSuccess ? QGEMM_OK : QGEMM_ERR_HIP;
+}
+
+int qgemm_round_kernels(const qgemm_round* r) { return r ? r->kernels : 0; }
+
+void qgemm_round_destroy(qgemm_round* r) {
+  if (!r) return;
+  if (r->exec) (void)hipGraphExecDestroy(r->exec);
+  if (r->graph) (void)hipGraphDestroy(r->graph);
+  delete r;
+}
+
 }  // extern "C"
 
 namespace {
@@ -435,42 +608,61 @@ namespace {
 qgemm_status run_plan(Plan& P, void* workspace, void* stream) {
   uint8_t* ws = (uint8_t*)workspace;
   hipStream_t s = (hipStream_t)stream;
-  const int cus = cu_count();
-  for (auto& l : P.launches) {
+  const qgemm_status st = upload_tables(P, ws, s);
+  if (st != QGEMM_OK) return st;
+  return launch_plan(P, ws, ws + P.table_bytes, ws + P.table_bytes + P.counter_bytes, s);
+}
+
+// One copy per launch with more than kMaxInline jobs: its job table, then
+// the stream kernel's job index, at its offset in the table region.
+qgemm_status upload_tables(const Plan& P, uint8_t* tables, hipStream_t s) {
+  for (const auto& l : P.launches) {
+    if ((int)l.descs.size() <= qg::kMaxInline) continue;
+    const size_t tb = l.descs.size() * sizeof(JobDesc);
+    std::vector<uint8_t> host(tb + l.index.size() * sizeof(int32_t));
+    std::memcpy(host.data(), l.descs.data(), tb);
+    if (!l.index.empty()) std::memcpy(host.data() + tb, l.index.data(), l.index.size() * sizeof(int32_t));
+    if (hipMemcpyAsync(tables + l.table_off, host.data(), host.size(), hipMemcpyHostToDevice, s) != hipSuccess)
+      return QGEMM_ERR_HIP;
+  }
+  return QGEMM_OK;
+}
+
+// The grid of a launch (queries the device on first use of a kernel, so a
+// graph recording calls this for every launch before it starts).
+int grid_of(const Launch& l) {
+  if (l.kind == kGroupMfma)
+    return (int)std::max<int64_t>(1, std::min<int64_t>(l.total, (int64_t)cu_count() * blocks_per_cu(l.kind, l.cls, l.all)));
+  return (l.nwaves + qg::kStreamWavesPerBlock - 1) / qg::kStreamWavesPerBlock;
+}
+
+// The kernels of a plan whose tables are in place: nothing but launches, so
+// it can be recorded into a graph.
+qgemm_status launch_plan(const Plan& P, uint8_t* tables, uint8_t* counters, uint8_t* slots, hipStream_t s) {
+  for (const auto& l : P.launches) {
     qg::SweepArgs args;
     std::memset(&args, 0, sizeof(args));
     args.njobs = (int32_t)l.descs.size();
     args.total = (int32_t)l.total;
     if ((int)l.descs.size() > qg::kMaxInline) {
-      // one copy: the job table, then the stream kernel's job index
-      uint8_t* table = ws + l.table_off;
-      const size_t tb = l.descs.size() * sizeof(JobDesc);
-      std::vector<uint8_t> host(tb + l.index.size() * sizeof(int32_t));
-      std::memcpy(host.data(), l.descs.data(), tb);
-      if (!l.index.empty()) std::memcpy(host.data() + tb, l.index.data(), l.index.size() * sizeof(int32_t));
-      if (hipMemcpyAsync(table, host.data(), host.size(), hipMemcpyHostToDevice, s) != hipSuccess)
-        return QGEMM_ERR_HIP;
+      uint8_t* table = tables + l.table_off;
       args.table = (const JobDesc*)table;
-      args.index = l.index.empty() ? nullptr : (const int32_t*)(table + tb);
+      args.index = l.index.empty() ? nullptr : (const int32_t*)(table + l.descs.size() * sizeof(JobDesc));
       args.bshift = l.bshift;
     } else {
       for (size_t i = 0; i < l.descs.size(); i++) args.inl[i] = l.descs[i];
       args.table = nullptr;
       args.index = nullptr;
     }
-    int grid;
-    if (l.kind == kGroupMfma) {
-      grid = (int)std::max<int64_t>(1, std::min<int64_t>(l.total, (int64_t)cus * blocks_per_cu(l.kind, l.cls, l.all)));
-    } else {
-      args.counters = (int*)(ws + l.counters_off);
-      args.slots = (float*)(ws + l.slots_off);
+    if (l.kind != kGroupMfma) {
+      args.counters = (int*)(counters + l.counters_off);
+      args.slots = (float*)(slots + l.slots_off);
       args.nwaves = l.nwaves;
       args.q = (int32_t)(l.total / l.nwaves);
       args.rem = (int32_t)(l.total % l.nwaves);
       args.slot_rows = l.cls;
-      grid = (l.nwaves + qg::kStreamWavesPerBlock - 1) / qg::kStreamWavesPerBlock;
     }
-    if (qg::launch_sweep(l.kind, l.cls, l.all, args, grid, s) != hipSuccess) return QGEMM_ERR_HIP;
+    if (qg::launch_sweep(l.kind, l.cls, l.all, args, grid_of(l), s) != hipSuccess) return QGEMM_ERR_HIP;
   }
   return QGEMM_OK;
 }

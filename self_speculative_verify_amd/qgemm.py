@@ -24,6 +24,8 @@ EXPORTS = (
     "qgemm_packed_bytes", "qgemm_pack", "qgemm_workspace_bytes", "qgemm_workspace_init",
     "qgemm_sweep", "qgemm_sweep_path", "qgemm_validate", "qgemm_auto_path",
     "qgemm_status_string", "qgemm_verify_workspace_bytes", "qgemm_verify_head",
+    "qgemm_round_workspace_bytes", "qgemm_round_create", "qgemm_round_launch", "qgemm_round_kernels",
+    "qgemm_round_destroy",
 )
 MAX_SLOTS = 64
 
@@ -52,6 +54,11 @@ class Job(ctypes.Structure):
 class Slot(ctypes.Structure):
     """Mirror of ``qgemm_slot``: panel rows row0 .. row0 + ndraft."""
     _fields_ = [("row0", ctypes.c_int32), ("ndraft", ctypes.c_int32)]
+
+
+class RoundSweep(ctypes.Structure):
+    """Mirror of ``qgemm_round_sweep``."""
+    _fields_ = [("jobs", ctypes.POINTER(Job)), ("njobs", ctypes.c_int32), ("path", ctypes.c_int32)]
 
 
 _lib = None
@@ -87,6 +94,18 @@ def lib() -> ctypes.CDLL:
         L.qgemm_verify_workspace_bytes.restype = sz
         L.qgemm_verify_head.argtypes = [jp, vp, ctypes.POINTER(Slot), ci, vp, vp, vp, vp, sz, vp]
         L.qgemm_verify_head.restype = ci
+        rp = ctypes.POINTER(RoundSweep)
+        L.qgemm_round_workspace_bytes.argtypes = [rp, ci, jp]
+        L.qgemm_round_workspace_bytes.restype = sz
+        L.qgemm_round_create.argtypes = [rp, ci, jp, vp, ctypes.POINTER(Slot), ci, vp, vp, vp, vp, sz, vp,
+                                         ctypes.POINTER(vp)]
+        L.qgemm_round_create.restype = ci
+        L.qgemm_round_launch.argtypes = [vp, vp]
+        L.qgemm_round_launch.restype = ci
+        L.qgemm_round_kernels.argtypes = [vp]
+        L.qgemm_round_kernels.restype = ci
+        L.qgemm_round_destroy.argtypes = [vp]
+        L.qgemm_round_destroy.restype = None
         _lib = L
     return _lib
 
@@ -219,3 +238,49 @@ def verify_head(head: Job, drafts, slots, argmax, accepted, workspace: Workspace
                                    maxlogit.data_ptr() if maxlogit is not None else None,
                                    accepted.data_ptr(), workspace.ptr, workspace.nbytes,
                                    _stream_ptr(stream)), "qgemm_verify_head")
+
+
+def round_sweeps(sweeps):
+    """[(jobs, path), ...] -> a ``qgemm_round_sweep`` array (the job arrays are
+    kept alive on it)."""
+    arrs = [job_array(j) for j, _ in sweeps]
+    out = (RoundSweep * len(sweeps))(*[RoundSweep(a, len(a), int(p)) for a, (_, p) in zip(arrs, sweeps)])
+    out._keep = arrs
+    return out
+
+
+def round_workspace_bytes(sweeps, head: Job | None = None) -> int:
+    arr = sweeps if isinstance(sweeps, ctypes.Array) else round_sweeps(sweeps)
+    return int(lib().qgemm_round_workspace_bytes(arr, len(arr), ctypes.byref(head) if head is not None else None))
+
+
+class Round:
+    """A recorded round (``qgemm_round``): sweeps in order, then optionally
+    the verify head, replayed as one HIP graph."""
+
+    def __init__(self, sweeps, workspace: "Workspace", head: Job | None = None, drafts=None, slots=(),
+                 argmax=None, accepted=None, maxlogit=None, stream=None):
+        self._sweeps = sweeps if isinstance(sweeps, ctypes.Array) else round_sweeps(sweeps)
+        self._head = head
+        self._slots = slot_array(slots) if slots else None
+        self.workspace = workspace
+        h = ctypes.c_void_p()
+        ptr = lambda t: t.data_ptr() if t is not None else None
+        _check(lib().qgemm_round_create(self._sweeps, len(self._sweeps),
+                                        ctypes.byref(head) if head is not None else None, ptr(drafts),
+                                        self._slots, len(self._slots) if self._slots else 0, ptr(argmax),
+                                        ptr(maxlogit), ptr(accepted), workspace.ptr, workspace.nbytes,
+                                        _stream_ptr(stream), ctypes.byref(h)), "qgemm_round_create")
+        self.handle = h.value
+
+    @property
+    def kernels(self) -> int:
+        return int(lib().qgemm_round_kernels(self.handle))
+
+    def launch(self, stream=None) -> None:
+        _check(lib().qgemm_round_launch(self.handle, _stream_ptr(stream)), "qgemm_round_launch")
+
+    def destroy(self) -> None:
+        if self.handle:
+            lib().qgemm_round_destroy(self.handle)
+            self.handle = None

@@ -146,3 +146,44 @@ def test_verify_head_validation_rejects_before_any_launch():
     assert call(w=0) == qgemm.ERR_INVALID_ARG
     assert call(w=wsp + 8) == qgemm.ERR_INVALID_ARG
     assert call(nb=ws - 8) == qgemm.ERR_INVALID_ARG
+
+
+def test_round_validation_rejects_before_any_launch():
+    L = qgemm.lib()
+    a = [_job()]
+    b = [_job(Y=0x20000000, M=40, N=300, ldy=300)]
+    sweeps = qgemm.round_sweeps([(a, qgemm.PATH_AUTO), (b, qgemm.PATH_MFMA)])
+    ws = qgemm.round_workspace_bytes(sweeps)
+    assert ws > 0 and ws % 256 == 0
+    head = _job(M=6, Y=0)
+    wsh = qgemm.round_workspace_bytes(sweeps, head)
+    assert wsh >= ws + 16 * 64 * 8
+    # invalid sweeps or head: size 0
+    assert qgemm.round_workspace_bytes(qgemm.round_sweeps([([_job(M=0)], 0)])) == 0
+    assert qgemm.round_workspace_bytes(qgemm.round_sweeps([(a, 9)])) == 0
+    assert qgemm.round_workspace_bytes(sweeps, _job(M=65, Y=0)) == 0
+    assert L.qgemm_round_workspace_bytes(None, 0, None) == 0
+    out = ctypes.c_void_p()
+    good = qgemm.slot_array([(0, 5)])
+
+    def create(sw=sweeps, n=None, h=None, slots=None, w=0x40000000, nb=wsh, o=ctypes.byref(out), d=0x50000000,
+               am=0x50001000, acc=0x50002000):
+        return L.qgemm_round_create(sw, len(sw) if n is None else n, ctypes.byref(h) if h is not None else None,
+                                    d, slots, len(slots) if slots else 0, am, None, acc, w, nb, None, o)
+
+    assert create(o=None) == qgemm.ERR_INVALID_ARG
+    assert create(w=0) == qgemm.ERR_INVALID_ARG
+    assert create(w=0x40000008) == qgemm.ERR_INVALID_ARG
+    assert create(nb=ws - 256) == qgemm.ERR_INVALID_ARG
+    assert create(n=-1) == qgemm.ERR_INVALID_ARG
+    assert create(sw=qgemm.round_sweeps([([_job(K=100)], 0)])) == qgemm.ERR_INVALID_ARG
+    assert create(h=head, slots=qgemm.slot_array([(0, 6)])) == qgemm.ERR_INVALID_ARG
+    assert create(h=head, slots=good, am=None) == qgemm.ERR_INVALID_ARG
+    assert create(h=head, slots=good, d=None) == qgemm.ERR_INVALID_ARG
+    assert create(h=head, slots=good, nb=wsh - 256) == qgemm.ERR_INVALID_ARG
+    assert L.qgemm_round_create(None, 0, None, None, None, 0, None, None, None, 0x40000000, 1 << 20, None,
+                                ctypes.byref(out)) == qgemm.ERR_INVALID_ARG
+    assert out.value is None
+    assert L.qgemm_round_launch(None, None) == qgemm.ERR_INVALID_ARG
+    assert L.qgemm_round_kernels(None) == 0
+    L.qgemm_round_destroy(None)
