@@ -33,6 +33,14 @@ dequantized inside the weight-streaming product; group 32 and 4/5 bits):
   it equals the argmax of row r0 + i; the accepted count is the longest such
   prefix, and the round's next token is the argmax of the first row that
   disagrees.  ``argmax_rows`` takes the lowest column among equal maxima.
+* ``attn_verify``: the attention half of a verify round, per slot and layer:
+  the W verify positions of a slot (the last W of its L cached positions)
+  attend causally over the slot's keys and values, 6 query heads per KV head,
+  4 KV heads, head dim 256 (the full-attention layers as the Quasar/q27 wiki
+  sizes their KV bytes; GQA 6 in its fp8-KV note), all in fp64.
+  ``e4m3_to_f64`` / ``f64_to_e4m3`` are the OCP E4M3 byte format of an fp8
+  KV cache: a plain decode, and the saturating scale-free conversion the
+  wiki's KV-cache item describes (nearest code, ties to even, clamp at 448).
 """
 from __future__ import annotations
 
@@ -260,3 +268,72 @@ def top2_gap(Y: np.ndarray) -> np.ndarray:
     Y = np.asarray(Y, dtype=np.float64)
     part = np.partition(Y, Y.shape[1] - 2, axis=1)
     return part[:, -1] - part[:, -2]
+
+
+# ---------------------------------------------------------------------------
+# Shared-KV attention verify (the attention half of a verify round)
+# ---------------------------------------------------------------------------
+# Geometry of the full-attention layers on the Quasar/q27 wiki: 4 KV heads of
+# head_dim 256 (long-context note on KV bytes per token) and 6 query heads per
+# KV head (the fp8-KV note: GQA = 6).  A slot's cache holds L positions; the
+# last W of them are the slot's verify positions (the accepted token and its
+# drafts), and query w sits at position L - W + w and attends causally to
+# positions 0 .. L - W + w.  All W * 6 queries of a KV head read that head's
+# keys and values once: the "shared-KV verify".
+ATTN_HKV, ATTN_GROUP, ATTN_D = 4, 6, 256
+ATTN_HQ = ATTN_HKV * ATTN_GROUP
+KV_FP16, KV_FP8 = 0, 1
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """OCP FP8 E4M3 bytes -> values: sign, 4 exponent bits (bias 7), 3
+    mantissa bits; exponent 0 is subnormal (m / 8 * 2^-6); S.1111.111 is NaN
+    and there are no infinities (largest finite 448)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    v = np.where(e == 0, m / 8 * 2.0 ** -6, (1 + m / 8) * np.ldexp(1.0, e - 7))
+    v = np.where((c & 0x7F) == 0x7F, np.nan, v)
+    return s * v
+
+
+def f64_to_e4m3(x) -> np.ndarray:
+    """Saturating conversion to E4M3 (the KV cache's scale-free fp8 form on
+    the Quasar/q27 wiki, KV-cache item: no per-row scale; values beyond the
+    largest finite 448 clamp to it): the nearest code, ties to the even
+    mantissa; NaN -> 0x7F.  Written as a search over the 127 finite
+    non-negative codes."""
+    x = np.asarray(x, dtype=np.float64)
+    vals = e4m3_to_f64(np.arange(127, dtype=np.uint8))        # 0 .. 448 ascending
+    a = np.minimum(np.abs(x), 448.0)
+    idx = np.searchsorted(vals, a)                            # vals[idx-1] < a <= vals[idx]
+    idx = np.clip(idx, 1, 126)
+    lo, hi = vals[idx - 1], vals[idx]
+    pick_hi = (a - lo > hi - a) | ((a - lo == hi - a) & (idx % 2 == 0))
+    code = np.where(a == 0, 0, np.where(pick_hi, idx, idx - 1))
+    code = np.where(a <= vals[0], 0, code)
+    out = (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), out).astype(np.uint8)
+
+
+def attn_verify(Q, K, V, W: int, scale: float) -> np.ndarray:
+    """One slot, one layer.  Q fp16 [W, 24, 256]; K, V values [L, 4, 256]
+    (fp16 arrays, or fp64 values decoded from fp8); returns O [W, 24, 256] in
+    fp64: for query head h (KV head h // 6) at position p = L - W + w,
+    O = sum_j softmax_j(scale * q . k_j) v_j over j = 0 .. p, the softmax
+    taken with its maximum subtracted (exact in fp64 up to rounding)."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    L = K.shape[0]
+    assert Q.shape == (W, ATTN_HQ, ATTN_D) and K.shape == V.shape == (L, ATTN_HKV, ATTN_D) and 1 <= W <= L
+    O = np.empty((W, ATTN_HQ, ATTN_D), dtype=np.float64)
+    for w in range(W):
+        p = L - W + w
+        for h in range(ATTN_HQ):
+            g = h // ATTN_GROUP
+            s = scale * (K[:p + 1, g, :] @ Q[w, h, :])
+            e = np.exp(s - s.max())
+            O[w, h, :] = (e @ V[:p + 1, g, :]) / e.sum()
+    return O
