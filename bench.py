@@ -12,7 +12,7 @@ tokens/s per sweep is M / step time.  The workloads that fit in the 256 MB
 last-level cache rotate over enough packed copies (>= 1 GB) that every step
 streams its weights from HBM.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only 2|3|4|5|6|7|8|9]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only 2|3|4|5|6|7|8|9|10]
        [--no-cpu] [--stack-layers L]
        python bench.py --copy-calib MIB   (a plain device copy of MIB MiB, the
        reference for scaling the HBM byte counters)
@@ -281,6 +281,74 @@ def round_bench(args):
     }), flush=True)
 
 
+def attn_bench(args):
+    """Attention verify over the 16 full-attention layers of a round: per
+    layer one call for every slot (W = 6 verify positions each), caches of
+    distinct layers in distinct buffers (2 GB and more, so they stream from
+    HBM).  One JSON line per (cache format, slots, L)."""
+    import torch
+
+    from self_speculative_verify_amd import qgemm as q
+    from synth import synth
+
+    dev = torch.device("cuda:0")
+    layers, W, HQ, HKV, D = 16, 6, 24, 4, 256
+    for kv in (q.KV_FP16, q.KV_FP8):
+        for nslots, L in ((1, 32768), (8, 8192)):
+            esz = 2 if kv == q.KV_FP16 else 1
+            # values: standard normals (fp16) or random finite E4M3 bytes of
+            # the same spread (|v| < 4); the timing does not depend on them
+            base = torch.from_numpy(synth.x_fp16(77, 64, HKV * D)).to(dev)
+            per_layer = []
+            for li in range(layers):
+                slots = []
+                for si in range(nslots):
+                    Qt = base[:W * HQ * D // (HKV * D)].reshape(W, HQ, D).contiguous()
+                    if kv == q.KV_FP16:
+                        Kt = base[0].repeat(L).reshape(L, HKV, D).contiguous()
+                        Vt = base[1].repeat(L).reshape(L, HKV, D).contiguous()
+                    else:
+                        g = torch.Generator(device=dev)
+                        g.manual_seed(li * 100 + si)
+                        Kt = torch.randint(0, 0x4C, (L, HKV, D), dtype=torch.uint8, device=dev, generator=g)
+                        Vt = torch.randint(0, 0x4C, (L, HKV, D), dtype=torch.uint8, device=dev, generator=g)
+                        Kt |= torch.randint(0, 2, (L, HKV, D), dtype=torch.uint8, device=dev, generator=g) << 7
+                    Ot = torch.empty((W, HQ, D), dtype=torch.float32, device=dev)
+                    slots.append((Qt, Kt, Vt, Ot, L, W))
+                arr = q.attn_slots(slots)
+                per_layer.append((arr, slots))
+            ws = q.Workspace(q.attn_workspace_bytes(per_layer[0][0], kv), device=dev)
+            L_ = q.lib()
+            sp = torch.cuda.current_stream().cuda_stream
+
+            def step():
+                for arr, _ in per_layer:
+                    L_.qgemm_attn_verify(arr, len(arr), kv, 0.0625, ws.ptr, ws.nbytes, sp)
+
+            for _ in range(args.warmup):
+                step()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                step()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            kv_bytes = layers * nslots * L * HKV * D * 2 * esz
+            io_bytes = layers * nslots * W * HQ * D * (2 + 4)
+            print(json.dumps({
+                "workload": f"attention verify, {layers} layers, {nslots} slot(s) x L={L}, W={W}, "
+                            f"{'fp16' if kv == q.KV_FP16 else 'e4m3'} KV",
+                "ms_per_round": round(ms, 4), "us_per_layer": round(ms * 1e3 / layers, 2),
+                "kv_GBps": round(kv_bytes / (ms / 1e3) / 1e9, 1),
+                "hbm_frac": round((kv_bytes + io_bytes) / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "kv_bytes": kv_bytes,
+            }), flush=True)
+            del per_layer, ws
+            torch.cuda.empty_cache()
+
+
 def cpu_baseline():
     """The oracle, untuned, on the host cores: the full M = 1 sweep of the
     34816 x 5120 4-bit gate+up matrix (generation and packing untimed)."""
@@ -317,7 +385,7 @@ def main():
                     help="time one workload (2, 3 or 4) only; 5 times the 5-bit stack at every M of its "
                          "sweep; 6 times the verify head; 7 and 8 the group-64 and zero-point 4-bit "
                          "stacks at M = 1, 8, 48; 9 a round of per-matrix sweeps plus the verify head, "
-                         "issued call by call and replayed as one graph")
+                         "issued call by call and replayed as one graph; 10 the attention verify")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--stack-layers", type=int, default=64)
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB")
@@ -368,6 +436,10 @@ def main():
 
     if args.only == 9:
         round_bench(args)
+        return
+
+    if args.only == 10:
+        attn_bench(args)
         return
 
     if args.only in (5, 7, 8):

@@ -271,6 +271,56 @@ int qgemm_round_kernels(const qgemm_round* round);
  * first. */
 void qgemm_round_destroy(qgemm_round* round);
 
+/* ---------------------------------------------------------------------------
+ * Attention verify (shared KV).  The attention half of a verify round, per
+ * full-attention layer: each slot's W verify positions (the accepted token
+ * and its drafts, whose keys and values are already the last W of the slot's
+ * L cached positions) attend causally over the slot's cache.  Query w sits
+ * at position L - W + w and sees positions 0 .. L - W + w:
+ *     O[w][h] = sum_j softmax_j(scale * Q[w][h] . K[j][h / 6]) V[j][h / 6]
+ * Geometry of the Quasar/q27 wiki's full-attention layers: 4 KV heads of
+ * head_dim 256 (long-context note on KV bytes per token) and 6 query heads
+ * per KV head (fp8-KV note, GQA 6), so 24 query heads.  All W * 6 queries of
+ * a KV head read its keys and values once (wiki intro bullets: one shared-KV
+ * verify).  The cache is binary16, or OCP E4M3 bytes with no scale (the
+ * wiki's KV-cache item: scale-free saturating fp8); E4M3 values are exact in
+ * binary16 and the product runs in binary16 MFMA with fp32 accumulation.
+ * Result: within relative L2 1e-3 of the exact attention over a slot's O and
+ * max |O - exact| <= 2e-3 * max |V| (probabilities enter the value product
+ * rounded to binary16).
+ *
+ *   Q     : binary16 [W][24][256], 16-byte aligned
+ *   K, V  : [L][4][256] elements (binary16, or one E4M3 byte each), 16-byte
+ *           aligned; NaN codes give unspecified outputs
+ *   O     : fp32 [W][24][256], 16-byte aligned, overwritten; must not overlap
+ *           Q, K, V or another slot's O
+ *   W     : 1 .. QGEMM_ATTN_MAX_W;  L: W .. 2^24
+ * Slots are independent; nslots 1 .. QGEMM_ATTN_MAX_SLOTS per call.  Two
+ * launches on `stream`: chunks of positions in parallel, then their merge.
+ * The workspace (qgemm_attn_workspace_bytes, 256-byte aligned, any contents)
+ * holds the per-chunk partials; calls that overlap on one workspace race. */
+#define QGEMM_KV_FP16 0
+#define QGEMM_KV_FP8 1
+#define QGEMM_ATTN_HKV 4
+#define QGEMM_ATTN_GROUP 6
+#define QGEMM_ATTN_D 256
+#define QGEMM_ATTN_MAX_W 16
+#define QGEMM_ATTN_MAX_SLOTS 16
+
+typedef struct {
+  const uint16_t* Q;
+  const void* K;
+  const void* V;
+  float* O;
+  int32_t L;
+  int32_t W;
+} qgemm_attn_slot;
+
+size_t qgemm_attn_workspace_bytes(const qgemm_attn_slot* slots, int nslots, int kv);
+
+qgemm_status qgemm_attn_verify(const qgemm_attn_slot* slots, int nslots, int kv, float scale, void* workspace,
+                               size_t ws_bytes, void* stream);
+
 /* The argument checks of qgemm_sweep_path alone (host only, no HIP call). */
 qgemm_status qgemm_validate(const qgemm_job* jobs, int njobs, int path, void* workspace,
                             size_t ws_bytes);

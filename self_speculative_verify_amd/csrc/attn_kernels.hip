@@ -1,0 +1,282 @@
+// gfx950 kernels of the shared-KV attention verify.
+//
+// A verify round scores W positions per slot (the accepted token and its
+// drafts, already appended to the slot's cache): query w at position
+// L - W + w attends causally to positions 0 .. L - W + w.  The 6 query heads
+// of a KV head at all W positions -- up to 96 query rows -- read that head's
+// keys and values once ("shared-KV verify", Quasar/q27 wiki, intro bullets),
+// as the weight sweep's panel rows share one weight read.
+//
+// attn_partial: one workgroup per (slot, KV head, chunk of positions), one
+// wave per 16-row block of queries.  Per step of 32 positions the keys
+// (as [position][dim]) and the values (transposed, [dim][position]) go
+// through LDS, widened to binary16 when the cache is E4M3 (exact).  Scores
+// are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_f16 (A = 16
+// positions x 32 dims of K, B = 32 dims x 16 query rows of Q), so lane l
+// holds 8 scores of query row l % 16: positions 4c .. 4c + 3 and 16 + 4c ..
+// 16 + 4c + 3 of the step (c = l / 16).  The online softmax keeps a running
+// maximum per row (base-2 units) and a per-lane partial sum; the
+// probabilities, rounded to binary16, are then exactly the B operand of the
+// value product O^T += V^T P^T (A = 16 dims x those 8 positions of V, read
+// from the transposed tile), whose accumulator again holds row l % 16 in
+// lane l, so the rescaling by exp2(m_old - m_new) is one multiply per value.
+// Each chunk leaves its unnormalized output, maximum and sum in the
+// workspace; attn_combine merges the chunks of every row.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_internal.h"
+
+namespace qa {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+
+// LDS rows padded so that the 16 rows one fragment read touches fall on
+// distinct banks.
+constexpr int kKRow = kD + 8;                // halves per K row (528 bytes)
+constexpr int kVRow = kBlk + 4;              // halves per transposed V row (72 bytes)
+constexpr int kKBytes = kBlk * kKRow * 2;
+constexpr int kVBytes = kD * kVRow * 2;
+
+// Two E4M3 bytes (bits 0-7 and 8-15 of u) -> two binary16 values, exactly.
+// The 7 magnitude bits e.mmm shifted up by 7 are the binary16 with exponent
+// field e and mantissa mmm000_0000: (1 + m/8) 2^(e-15), or m 2^-17 when e = 0
+// (a binary16 subnormal); one multiply by 2^8 rebiases both cases to the E4M3
+// value, exactly (the largest, 448, included).  The sign bits are copied.
+// (The NaN codes S.1111.111 come out as +-480: outputs are then unspecified.)
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t e4m3x2_to_h2(uint32_t u) {
+  const uint32_t mag = ((u & 0x007Fu) << 7) | ((u & 0x7F00u) << 15);
+  const uint32_t sgn = ((u & 0x0080u) << 8) | ((u & 0x8000u) << 16);
+  const h2_t k256 = {(_Float16)256.0f, (_Float16)256.0f};
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, mag) * k256) | sgn;
+}
+
+// Global pieces (16 bytes) of one step, for KV head g, in registers.  K is
+// read piece-fastest (a position's 512 or 256 bytes by consecutive lanes)
+// and written to LDS row by row.  V is read position-fastest, so that the
+// transposed LDS writes of consecutive lanes are consecutive halves of one
+// row (no bank conflicts).
+template <bool kFp8>
+struct Tile {
+  static constexpr int kE = kFp8 ? 1 : 2;                 // bytes per cached element
+  static constexpr int kPerPos = kD * kE / 16;            // 16-byte pieces per position and head
+  static constexpr int kPieces = kBlk * kPerPos;          // per tensor and step
+  static constexpr int kIters = (kPieces + kThreads - 1) / kThreads;
+  u4_t k[kIters], v[kIters];
+
+  // positions >= L read as zeros (they are masked; a zero keeps their
+  // products zero)
+  __device__ __forceinline__ void load(const uint8_t* K, const uint8_t* V, int g, int p0, int L, int tid) {
+#pragma unroll
+    for (int i = 0; i < kIters; i++) {
+      const int q = tid + kThreads * i;
+      k[i] = v[i] = u4_t{0u, 0u, 0u, 0u};
+      if (q >= kPieces) continue;
+      const int pk = p0 + q / kPerPos, ck = q % kPerPos;
+      const int pv = p0 + q % kBlk, cv = q / kBlk;
+      if (pk < L) k[i] = __builtin_nontemporal_load((const u4_t*)(K + ((size_t)pk * kHkv + g) * (kD * kE) + ck * 16));
+      if (pv < L) v[i] = __builtin_nontemporal_load((const u4_t*)(V + ((size_t)pv * kHkv + g) * (kD * kE) + cv * 16));
+    }
+  }
+
+  // Into LDS: K at [position][dim], V at [dim][position] (binary16).
+  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
+    _Float16* ks = (_Float16*)lds;
+    uint16_t* vt = (uint16_t*)(lds + kKBytes);
+#pragma unroll
+    for (int i = 0; i < kIters; i++) {
+      const int q = tid + kThreads * i;
+      if (q >= kPieces) continue;
+      const int pk = q / kPerPos, dk = (q % kPerPos) * (16 / kE);
+      const int pv = q % kBlk, dv = (q / kBlk) * (16 / kE);
+      if constexpr (!kFp8) {
+        *(u4_t*)(ks + pk * kKRow + dk) = k[i];
+#pragma unroll
+        for (int t = 0; t < 8; t++) vt[(dv + t) * kVRow + pv] = (uint16_t)(v[i][t >> 1] >> (16 * (t & 1)));
+      } else {
+        const u4_t lo = {e4m3x2_to_h2(k[i][0]), e4m3x2_to_h2(k[i][0] >> 16), e4m3x2_to_h2(k[i][1]),
+                         e4m3x2_to_h2(k[i][1] >> 16)};
+        const u4_t hi = {e4m3x2_to_h2(k[i][2]), e4m3x2_to_h2(k[i][2] >> 16), e4m3x2_to_h2(k[i][3]),
+                         e4m3x2_to_h2(k[i][3] >> 16)};
+        *(u4_t*)(ks + pk * kKRow + dk) = lo;
+        *(u4_t*)(ks + pk * kKRow + dk + 8) = hi;
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+          const uint32_t h2 = e4m3x2_to_h2(v[i][t >> 1] >> (16 * (t & 1)));
+          vt[(dv + 2 * t) * kVRow + pv] = (uint16_t)h2;
+          vt[(dv + 2 * t + 1) * kVRow + pv] = (uint16_t)(h2 >> 16);
+        }
+      }
+    }
+  }
+};
+
+// Running softmax state of one lane's query row: maximum (base-2 units) and
+// this lane's part of the sum.
+struct Row {
+  float m, l;
+};
+
+// One step of 32 positions from the LDS tiles: scores, online softmax, and
+// the value product into acc.
+__device__ __forceinline__ void step(Row& st_, f4_t (&acc)[kD / 16], const h8_t (&qf)[kD / 32], const _Float16* ks,
+                                     const _Float16* vt, int pb, int lim, int lane, float scale_log2e) {
+  const int c = lane >> 4;
+  // S^T for positions pb .. pb + 15 and pb + 16 .. pb + 31 (the two
+  // accumulation chains interleaved)
+  f4_t st[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int s = 0; s < kD / 32; s++)
+#pragma unroll
+    for (int sb = 0; sb < 2; sb++) {
+      const h8_t kf = *(const h8_t*)(ks + (16 * sb + (lane & 15)) * kKRow + 32 * s + 8 * c);
+      st[sb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[s], st[sb], 0, 0, 0);
+    }
+  // element j of this lane: position pb + (j < 4 ? 4c + j : 16 + 4c + j - 4)
+  float x[8];
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const int pos = pb + (j < 4 ? 4 * c + j : 16 + 4 * c + j - 4);
+    x[j] = pos <= lim ? st[j >> 2][j & 3] * scale_log2e : -__builtin_inff();
+    mx = fmaxf(mx, x[j]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(st_.m, mx);
+  const float ms = m_new == -__builtin_inff() ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(st_.m - ms);
+  h8_t pf;
+  float ps = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const float p = __builtin_amdgcn_exp2f(x[j] - ms);
+    ps += p;
+    pf[j] = (_Float16)p;
+  }
+  st_.l = st_.l * alpha + ps;
+  st_.m = m_new;
+  // O^T[dims 16 db ..][rows] += V^T[dims][this lane's 8 positions] P^T
+#pragma unroll
+  for (int db = 0; db < kD / 16; db++) {
+    const _Float16* vrow = vt + (16 * db + (lane & 15)) * kVRow;
+    const u2_t lo = *(const u2_t*)(vrow + 4 * c);
+    const u2_t hi = *(const u2_t*)(vrow + 16 + 4 * c);
+    const u4_t va = {lo.x, lo.y, hi.x, hi.y};
+    acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, va), pf, acc[db] * alpha, 0, 0, 0);
+  }
+}
+
+template <bool kFp8>
+__global__ void __launch_bounds__(kThreads) attn_partial(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kKBytes + kVBytes];
+  const int si = blockIdx.z, ci = blockIdx.x, g = blockIdx.y;
+  if (si >= a.nslots) return;
+  const AttnSlot S = a.s[si];
+  if (ci >= S.nchunks) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int R = kGroup * S.W;                  // query rows of this KV head
+  const bool active = 16 * wave < R;
+  const int c = lane >> 4;
+  const int row = 16 * wave + (lane & 15);     // query row held by this lane
+  const int rr = row < R ? row : R - 1;        // rows past R repeat the last (never written)
+  const int w = rr / kGroup;
+  const int lim = S.L - S.W + w;               // last position this row sees
+  const int p0 = ci * a.chunk;
+  const int pend = min(S.L, p0 + a.chunk);
+  const int nblk = (pend - p0 + kBlk - 1) / kBlk;
+
+  // this lane's query fragments: row rr, dims 32 s + 8 c .. + 7
+  h8_t qf[kD / 32];
+  {
+    const _Float16* qrow = (const _Float16*)S.Q + ((size_t)w * kHq + kGroup * g + rr % kGroup) * kD;
+#pragma unroll
+    for (int s = 0; s < kD / 32; s++) qf[s] = *(const h8_t*)(qrow + 32 * s + 8 * c);
+  }
+  f4_t acc[kD / 16];
+#pragma unroll
+  for (int db = 0; db < kD / 16; db++) acc[db] = f4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_inff(), l_run = 0.f;
+
+  // two steps in flight: the loads of step b + 2 are issued while step b
+  // computes (two register sets, the loop unrolled by two)
+  Tile<kFp8> t0, t1;
+  t0.load(S.K, S.V, g, p0, S.L, tid);
+  if (nblk > 1) t1.load(S.K, S.V, g, p0 + kBlk, S.L, tid);
+  const _Float16* ks = (const _Float16*)lds;
+  const _Float16* vt = (const _Float16*)(lds + kKBytes);
+  Row r_state{m_run, l_run};
+  for (int b = 0; b < nblk; b += 2) {
+    t0.store(lds, tid);
+    __syncthreads();
+    if (b + 2 < nblk) t0.load(S.K, S.V, g, p0 + (b + 2) * kBlk, S.L, tid);
+    if (active) step(r_state, acc, qf, ks, vt, p0 + b * kBlk, lim, lane, a.scale_log2e);
+    __syncthreads();
+    if (b + 1 < nblk) {
+      t1.store(lds, tid);
+      __syncthreads();
+      if (b + 3 < nblk) t1.load(S.K, S.V, g, p0 + (b + 3) * kBlk, S.L, tid);
+      if (active) step(r_state, acc, qf, ks, vt, p0 + (b + 1) * kBlk, lim, lane, a.scale_log2e);
+      __syncthreads();
+    }
+  }
+  m_run = r_state.m;
+  l_run = r_state.l;
+  if (!active) return;
+  // row sums over the four lanes of a row; the maximum is already common
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (row < R) {
+    const size_t part = (size_t)S.part0 + (size_t)g * S.nchunks + ci;
+    float* o = a.part_o + (part * kMaxRows + row) * kD + 4 * c;
+#pragma unroll
+    for (int db = 0; db < kD / 16; db++) *(f4_t*)(o + 16 * db) = acc[db];
+    if (c == 0) {
+      a.part_ml[(part * kMaxRows + row) * 2] = m_run;
+      a.part_ml[(part * kMaxRows + row) * 2 + 1] = l_tot;
+    }
+  }
+}
+
+// One workgroup per (query row, KV head, slot), one thread per dim: the
+// row's chunks merged with weights exp2(m_c - max m), divided by the merged
+// sum.  Chunk 0 always holds position 0, so the maximum is finite.
+__global__ void __launch_bounds__(kD) attn_combine(AttnArgs a) {
+  const int r = blockIdx.x, g = blockIdx.y, si = blockIdx.z, d = threadIdx.x;
+  if (si >= a.nslots) return;
+  const AttnSlot S = a.s[si];
+  if (r >= kGroup * S.W) return;
+  const size_t row0 = ((size_t)S.part0 + (size_t)g * S.nchunks) * kMaxRows + r;
+  const float* ml = a.part_ml + row0 * 2;
+  const float* po = a.part_o + row0 * kD + d;
+  const size_t mstep = (size_t)kMaxRows * 2, ostep = (size_t)kMaxRows * kD;
+  float M = -__builtin_inff();
+#pragma unroll 8
+  for (int c = 0; c < S.nchunks; c++) M = fmaxf(M, ml[c * mstep]);
+  float num = 0.f, den = 0.f;
+#pragma unroll 8
+  for (int c = 0; c < S.nchunks; c++) {
+    const float wgt = __builtin_amdgcn_exp2f(ml[c * mstep] - M);
+    den += wgt * ml[c * mstep + 1];
+    num += wgt * po[c * ostep];
+  }
+  S.O[((size_t)(r / kGroup) * kHq + kGroup * g + r % kGroup) * kD + d] = num / den;
+}
+
+hipError_t launch_attn(const AttnArgs& a, bool fp8, int max_chunks, hipStream_t stream) {
+  const dim3 grid((unsigned)max_chunks, kHkv, (unsigned)a.nslots);
+  if (fp8)
+    hipLaunchKernelGGL(attn_partial<true>, grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_partial<false>, grid, dim3(kThreads), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL(attn_combine, dim3(kMaxRows, kHkv, (unsigned)a.nslots), dim3(kD), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace qa

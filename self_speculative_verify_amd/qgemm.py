@@ -25,8 +25,10 @@ EXPORTS = (
     "qgemm_sweep", "qgemm_sweep_path", "qgemm_validate", "qgemm_auto_path",
     "qgemm_status_string", "qgemm_verify_workspace_bytes", "qgemm_verify_head",
     "qgemm_round_workspace_bytes", "qgemm_round_create", "qgemm_round_launch", "qgemm_round_kernels",
-    "qgemm_round_destroy",
+    "qgemm_round_destroy", "qgemm_attn_workspace_bytes", "qgemm_attn_verify",
 )
+KV_FP16, KV_FP8 = 0, 1
+ATTN_HKV, ATTN_GROUP, ATTN_D, ATTN_MAX_W, ATTN_MAX_SLOTS = 4, 6, 256, 16, 16
 MAX_SLOTS = 64
 
 
@@ -54,6 +56,12 @@ class Job(ctypes.Structure):
 class Slot(ctypes.Structure):
     """Mirror of ``qgemm_slot``: panel rows row0 .. row0 + ndraft."""
     _fields_ = [("row0", ctypes.c_int32), ("ndraft", ctypes.c_int32)]
+
+
+class AttnSlot(ctypes.Structure):
+    """Mirror of ``qgemm_attn_slot``."""
+    _fields_ = [("Q", ctypes.c_void_p), ("K", ctypes.c_void_p), ("V", ctypes.c_void_p), ("O", ctypes.c_void_p),
+                ("L", ctypes.c_int32), ("W", ctypes.c_int32)]
 
 
 class RoundSweep(ctypes.Structure):
@@ -106,6 +114,11 @@ def lib() -> ctypes.CDLL:
         L.qgemm_round_kernels.restype = ci
         L.qgemm_round_destroy.argtypes = [vp]
         L.qgemm_round_destroy.restype = None
+        ap = ctypes.POINTER(AttnSlot)
+        L.qgemm_attn_workspace_bytes.argtypes = [ap, ci, ci]
+        L.qgemm_attn_workspace_bytes.restype = sz
+        L.qgemm_attn_verify.argtypes = [ap, ci, ci, ctypes.c_float, vp, sz, vp]
+        L.qgemm_attn_verify.restype = ci
         _lib = L
     return _lib
 
@@ -284,3 +297,20 @@ class Round:
         if self.handle:
             lib().qgemm_round_destroy(self.handle)
             self.handle = None
+
+
+def attn_slots(slots):
+    """[(Q, K, V, O, L, W), ...] of device tensors / sizes -> a ``qgemm_attn_slot`` array."""
+    return (AttnSlot * len(slots))(*[AttnSlot(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), int(L), int(W))
+                                     for Q, K, V, O, L, W in slots])
+
+
+def attn_workspace_bytes(slots, kv: int) -> int:
+    arr = slots if isinstance(slots, ctypes.Array) else attn_slots(slots)
+    return int(lib().qgemm_attn_workspace_bytes(arr, len(arr), kv))
+
+
+def attn_verify(slots, kv: int, scale: float, workspace: "Workspace", stream=None) -> None:
+    arr = slots if isinstance(slots, ctypes.Array) else attn_slots(slots)
+    _check(lib().qgemm_attn_verify(arr, len(arr), kv, scale, workspace.ptr, workspace.nbytes, _stream_ptr(stream)),
+           "qgemm_attn_verify")

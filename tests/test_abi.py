@@ -187,3 +187,32 @@ def test_round_validation_rejects_before_any_launch():
     assert L.qgemm_round_launch(None, None) == qgemm.ERR_INVALID_ARG
     assert L.qgemm_round_kernels(None) == 0
     L.qgemm_round_destroy(None)
+
+
+def test_attn_validation_rejects_before_any_launch():
+    L = qgemm.lib()
+
+    def slot(Q=0x100000, K=0x200000, V=0x300000, O=0x40000000, Ln=100, W=6):
+        return qgemm.AttnSlot(Q, K, V, O, Ln, W)
+
+    def arr(*ss):
+        return (qgemm.AttnSlot * len(ss))(*ss)
+
+    good = arr(slot())
+    ws = qgemm.attn_workspace_bytes(good, qgemm.KV_FP16)
+    assert ws > 0 and ws % 256 == 0
+    assert qgemm.attn_workspace_bytes(good, qgemm.KV_FP8) == ws        # layout from positions only
+    bad = [slot(W=0), slot(W=17), slot(Ln=5), slot(Ln=(1 << 24) + 1), slot(Q=0), slot(O=0x40000008),
+           slot(K=0x200004), slot(O=0x100000), slot(O=0x300000 + 64)]
+    for b in bad:
+        assert qgemm.attn_workspace_bytes(arr(b), qgemm.KV_FP16) == 0
+        assert L.qgemm_attn_verify(arr(b), 1, qgemm.KV_FP16, 0.0625, 0x50000000, 1 << 30, None) == qgemm.ERR_INVALID_ARG
+    assert qgemm.attn_workspace_bytes(good, 2) == 0
+    assert L.qgemm_attn_verify(good, 0, 0, 0.0625, 0x50000000, 1 << 30, None) == qgemm.ERR_INVALID_ARG
+    assert L.qgemm_attn_verify(arr(*[slot(O=0x40000000 + (1 << 20) * i) for i in range(17)]), 17, 0, 0.0625,
+                               0x50000000, 1 << 30, None) == qgemm.ERR_INVALID_ARG
+    two = arr(slot(), slot(O=0x40000000 + 1024))                     # outputs overlap
+    assert L.qgemm_attn_verify(two, 2, 0, 0.0625, 0x50000000, 1 << 30, None) == qgemm.ERR_INVALID_ARG
+    assert L.qgemm_attn_verify(good, 1, 0, float("nan"), 0x50000000, 1 << 30, None) == qgemm.ERR_INVALID_ARG
+    assert L.qgemm_attn_verify(good, 1, 0, 0.0625, 0x50000008, 1 << 30, None) == qgemm.ERR_INVALID_ARG
+    assert L.qgemm_attn_verify(good, 1, 0, 0.0625, 0x50000000, ws - 256, None) == qgemm.ERR_INVALID_ARG
