@@ -1052,16 +1052,21 @@ struct Group {
     }
   }
 
+  // The code loads of one tile per row block as raw buffer loads over that
+  // tile alone (non-temporal).  A tile past the job's last (the prefetch
+  // running ahead of the final tiles) gets a zero-length range: its loads
+  // return zeros without touching memory but still count for the waits.
+  static constexpr int kNt = 2;  // cache policy: non-temporal
   template <int F>
   static __device__ __forceinline__ void load_w(Tiles<F>& t, const uint8_t* w0, int64_t rstride,
-                                                int nrows, int lane) {
+                                                int nrows, int len, int lane) {
 #pragma unroll
     for (int r = 0; r < kRG; r++) {
       const uint8_t* tp = w0 + (int64_t)(r < nrows ? r : nrows - 1) * rstride;
-      t.c[r] = __builtin_nontemporal_load(gload_ptr<u4_t>(tp + 16 * lane));
-      if constexpr (F == kFmtQ5) t.h[r] = __builtin_nontemporal_load(gload_ptr<uint32_t>(tp + kHiOff + 4 * lane));
-      if constexpr (F == kFmtZP)
-        t.h[r] = __builtin_nontemporal_load(gload_ptr<uint16_t>(tp + kZeroOff + 2 * (lane & 15)));
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)tp, (short)0, len, kBufWord3);
+      t.c[r] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, 0, kNt));
+      if constexpr (F == kFmtQ5) t.h[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, kHiOff + 4 * lane, 0, kNt);
+      if constexpr (F == kFmtZP) t.h[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, kZeroOff + 2 * (lane & 15), 0, kNt);
     }
   }
 
@@ -1083,7 +1088,7 @@ struct Group {
   static __device__ __forceinline__ void codes(const JobDesc& d, int kw, Tiles<F>& t, const uint8_t* wbase,
                                                int64_t rstride, int nrows, int lane) {
     constexpr int TB = tile_bytes(F);
-    load_w<F>(t, wbase + (int64_t)(kw < d.nkt ? kw : d.nkt - 1) * TB, rstride, nrows, lane);
+    load_w<F>(t, wbase + (int64_t)(kw < d.nkt ? kw : d.nkt - 1) * TB, rstride, nrows, kw < d.nkt ? TB : 0, lane);
   }
 
   // One unit: row blocks rb0 + kRG * wave + r (r < kRG) of job d, all k tiles.
