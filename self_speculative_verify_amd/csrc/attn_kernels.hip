@@ -79,7 +79,10 @@ struct Tile {
       const int pk = p0 + q / kPerPos, ck = q % kPerPos;
       const int pv = p0 + q % kBlk, cv = q / kBlk;
       if (pk < L) k[i] = __builtin_nontemporal_load((const u4_t*)(K + ((size_t)pk * kHkv + g) * (kD * kE) + ck * 16));
-      if (pv < L) v[i] = __builtin_nontemporal_load((const u4_t*)(V + ((size_t)pv * kHkv + g) * (kD * kE) + cv * 16));
+      // (ordinary loads: a wave reads 32 bytes of each of 64 lines here, and
+      // the rest of each line, read by other waves of the step, must stay
+      // in the L2 until then)
+      if (pv < L) v[i] = *(const u4_t*)(V + ((size_t)pv * kHkv + g) * (kD * kE) + cv * 16);
     }
   }
 
