@@ -10,7 +10,8 @@
 // attn_partial: one workgroup per (slot, KV head, chunk of positions), one
 // wave per 16-row block of queries.  Per step of 32 positions the keys
 // (as [position][dim]) and the values (transposed, [dim][position]) go
-// through LDS, widened to binary16 when the cache is E4M3 (exact).  Scores
+// through LDS, widened to binary16 when the cache is E4M3 (exact, by the
+// hardware conversion).  Scores
 // are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_f16 (A = 16
 // positions x 32 dims of K, B = 32 dims x 16 query rows of Q), so lane l
 // holds 8 scores of query row l % 16: positions 4c .. 4c + 3 and 16 + 4c ..
@@ -41,18 +42,14 @@ constexpr int kVRow = kBlk + 4;              // halves per transposed V row (72 
 constexpr int kKBytes = kBlk * kKRow * 2;
 constexpr int kVBytes = kD * kVRow * 2;
 
-// Two E4M3 bytes (bits 0-7 and 8-15 of u) -> two binary16 values, exactly.
-// The 7 magnitude bits e.mmm shifted up by 7 are the binary16 with exponent
-// field e and mantissa mmm000_0000: (1 + m/8) 2^(e-15), or m 2^-17 when e = 0
-// (a binary16 subnormal); one multiply by 2^8 rebiases both cases to the E4M3
-// value, exactly (the largest, 448, included).  The sign bits are copied.
-// (The NaN codes S.1111.111 come out as +-480: outputs are then unspecified.)
+// Two E4M3 bytes of the word u (bytes 0-1, or 2-3 when kHi) -> two
+// binary16 values: gfx950's scaled conversion with scale 1, exact for every
+// code (E4M3 values are binary16 values; checked against the format's
+// definition for all 256 codes, NaN included).
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+template <bool kHi>
 __device__ __forceinline__ uint32_t e4m3x2_to_h2(uint32_t u) {
-  const uint32_t mag = ((u & 0x007Fu) << 7) | ((u & 0x7F00u) << 15);
-  const uint32_t sgn = ((u & 0x0080u) << 8) | ((u & 0x8000u) << 16);
-  const h2_t k256 = {(_Float16)256.0f, (_Float16)256.0f};
-  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, mag) * k256) | sgn;
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u, 1.0f, kHi));
 }
 
 // Global pieces (16 bytes) of one step, for KV head g, in registers.  K is
@@ -101,15 +98,15 @@ struct Tile {
 #pragma unroll
         for (int t = 0; t < 8; t++) vt[(dv + t) * kVRow + pv] = (uint16_t)(v[i][t >> 1] >> (16 * (t & 1)));
       } else {
-        const u4_t lo = {e4m3x2_to_h2(k[i][0]), e4m3x2_to_h2(k[i][0] >> 16), e4m3x2_to_h2(k[i][1]),
-                         e4m3x2_to_h2(k[i][1] >> 16)};
-        const u4_t hi = {e4m3x2_to_h2(k[i][2]), e4m3x2_to_h2(k[i][2] >> 16), e4m3x2_to_h2(k[i][3]),
-                         e4m3x2_to_h2(k[i][3] >> 16)};
+        const u4_t lo = {e4m3x2_to_h2<false>(k[i][0]), e4m3x2_to_h2<true>(k[i][0]), e4m3x2_to_h2<false>(k[i][1]),
+                         e4m3x2_to_h2<true>(k[i][1])};
+        const u4_t hi = {e4m3x2_to_h2<false>(k[i][2]), e4m3x2_to_h2<true>(k[i][2]), e4m3x2_to_h2<false>(k[i][3]),
+                         e4m3x2_to_h2<true>(k[i][3])};
         *(u4_t*)(ks + pk * kKRow + dk) = lo;
         *(u4_t*)(ks + pk * kKRow + dk + 8) = hi;
 #pragma unroll
         for (int t = 0; t < 8; t++) {
-          const uint32_t h2 = e4m3x2_to_h2(v[i][t >> 1] >> (16 * (t & 1)));
+          const uint32_t h2 = (t & 1) ? e4m3x2_to_h2<true>(v[i][t >> 1]) : e4m3x2_to_h2<false>(v[i][t >> 1]);
           vt[(dv + 2 * t) * kVRow + pv] = (uint16_t)h2;
           vt[(dv + 2 * t + 1) * kVRow + pv] = (uint16_t)(h2 >> 16);
         }

@@ -113,3 +113,27 @@ def test_attn_long_context_workload(kv):
         Qs[:, hs] = Q[:, hs]
         Oref = oracle.attn_verify(Qs, Kv, Vv, W, SCALE)
         _check(O[:, hs], Oref[:, hs], Vv, f"L=32768 kv head {g}")
+
+
+@pytest.mark.parametrize("kv", [qgemm.KV_FP16, qgemm.KV_FP8])
+def test_attn_single_position_returns_values_exactly(kv):
+    """One visible position: the softmax weight is exactly 1, so O is the
+    value row decoded from the cache, bit for bit.  The E4M3 row holds all
+    256 codes (the NaN codes give NaN)."""
+    import torch
+
+    Q = synth.x_fp16(5, HQ, D).reshape(1, HQ, D)
+    if kv == qgemm.KV_FP8:
+        Kc = oracle.f64_to_e4m3(synth.x_fp16(6, HKV, D).astype(np.float64)).reshape(1, HKV, D)
+        Vc = np.tile(np.arange(256, dtype=np.uint8), (HKV, 1))[None]
+        Vv = oracle.e4m3_to_f64(Vc)
+    else:
+        Kc = synth.x_fp16(6, HKV, D).reshape(1, HKV, D)
+        Vc = synth.x_fp16(7, HKV, D).reshape(1, HKV, D)
+        Vv = Vc.astype(np.float64)
+    (O,), _ = _run([(Q, Kc, Vc, None, None)], kv)
+    for h in range(HQ):
+        want = Vv[0, h // qgemm.ATTN_GROUP]
+        got = O[0, h].astype(np.float64)
+        assert np.array_equal(np.isnan(got), np.isnan(want))
+        assert np.array_equal(got[~np.isnan(want)], want[~np.isnan(want)])
