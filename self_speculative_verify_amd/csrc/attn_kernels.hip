@@ -41,6 +41,7 @@ constexpr int kKRow = kD + 8;                // halves per K row (528 bytes)
 constexpr int kVRow = kBlk + 4;              // halves per transposed V row (72 bytes)
 constexpr int kKBytes = kBlk * kKRow * 2;
 constexpr int kVBytes = kD * kVRow * 2;
+constexpr int kBufBytes = kKBytes + kVBytes;   // one step's tiles; two buffers alternate
 
 // Two E4M3 bytes of the word u (bytes 0-1, or 2-3 when kHi) -> two
 // binary16 values: gfx950's scaled conversion with scale 1, exact for every
@@ -173,7 +174,7 @@ __device__ __forceinline__ void step(Row& st_, f4_t (&acc)[kD / 16], const h8_t 
 
 template <bool kFp8>
 __global__ void __launch_bounds__(kThreads) attn_partial(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kKBytes + kVBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBufBytes];
   const int si = blockIdx.z, ci = blockIdx.x, g = blockIdx.y;
   if (si >= a.nslots) return;
   const AttnSlot S = a.s[si];
@@ -203,27 +204,37 @@ __global__ void __launch_bounds__(kThreads) attn_partial(AttnArgs a) {
   for (int db = 0; db < kD / 16; db++) acc[db] = f4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_inff(), l_run = 0.f;
 
-  // two steps in flight: the loads of step b + 2 are issued while step b
-  // computes (two register sets, the loop unrolled by two)
+  // Steps alternate between two LDS buffers, so one barrier per step: step
+  // b + 1 is stored into the other buffer while step b is computed (the
+  // barrier ending step b - 1 freed it).  Loads run two steps ahead in two
+  // register sets: the set just stored is reloaded with step b + 3.
   Tile<kFp8> t0, t1;
   t0.load(S.K, S.V, g, p0, S.L, tid);
   if (nblk > 1) t1.load(S.K, S.V, g, p0 + kBlk, S.L, tid);
-  const _Float16* ks = (const _Float16*)lds;
-  const _Float16* vt = (const _Float16*)(lds + kKBytes);
+  t0.store(lds, tid);
+  if (nblk > 2) t0.load(S.K, S.V, g, p0 + 2 * kBlk, S.L, tid);
+  __syncthreads();
   Row r_state{m_run, l_run};
   for (int b = 0; b < nblk; b += 2) {
-    t0.store(lds, tid);
-    __syncthreads();
-    if (b + 2 < nblk) t0.load(S.K, S.V, g, p0 + (b + 2) * kBlk, S.L, tid);
-    if (active) step(r_state, acc, qf, ks, vt, p0 + b * kBlk, lim, lane, a.scale_log2e);
-    __syncthreads();
+    // step b from buffer 0; step b + 1 into buffer 1
     if (b + 1 < nblk) {
-      t1.store(lds, tid);
-      __syncthreads();
+      t1.store(lds + kBufBytes, tid);
       if (b + 3 < nblk) t1.load(S.K, S.V, g, p0 + (b + 3) * kBlk, S.L, tid);
-      if (active) step(r_state, acc, qf, ks, vt, p0 + (b + 1) * kBlk, lim, lane, a.scale_log2e);
-      __syncthreads();
     }
+    if (active)
+      step(r_state, acc, qf, (const _Float16*)lds, (const _Float16*)(lds + kKBytes), p0 + b * kBlk, lim, lane,
+           a.scale_log2e);
+    __syncthreads();
+    if (b + 1 >= nblk) break;
+    // step b + 1 from buffer 1; step b + 2 into buffer 0
+    if (b + 2 < nblk) {
+      t0.store(lds, tid);
+      if (b + 4 < nblk) t0.load(S.K, S.V, g, p0 + (b + 4) * kBlk, S.L, tid);
+    }
+    if (active)
+      step(r_state, acc, qf, (const _Float16*)(lds + kBufBytes), (const _Float16*)(lds + kBufBytes + kKBytes),
+           p0 + (b + 1) * kBlk, lim, lane, a.scale_log2e);
+    __syncthreads();
   }
   m_run = r_state.m;
   l_run = r_state.l;
