@@ -213,3 +213,26 @@ def test_verify_head_on_variant(fmt):
     _check(Yg, Yref, X, oracle.max_scale(ref_packed, N, K, fmt), "logits")
     assert np.array_equal(am.cpu().numpy(), oracle.argmax_rows(Yg))
     assert acc.cpu().numpy().tolist() == oracle.accept(am.cpu().numpy(), drafts, slots)
+
+
+EDGE = [
+    (G64, 1, 64, 1), (G64, 1, 64, 64), (G64, 17, 192, 3), (G64, 33, 448, 17), (G64, 129, 4160, 2),
+    (G64, 1000, 1088, 33), (ZP, 1, 32, 1), (ZP, 1, 32, 64), (ZP, 17, 96, 3), (ZP, 33, 416, 17),
+    (ZP, 15, 160, 7), (ZP, 31, 17408, 64), (ZP, 64, 128, 48),
+]
+
+
+@pytest.mark.parametrize("fmt,N,K,M", EDGE)
+def test_edge_shapes(fmt, N, K, M):
+    """Single rows and groups, ragged tiles and padded strides on every path."""
+    say(f"edge fmt={fmt:#x} N={N} K={K} M={M}")
+    W = _weights(N * 7 + K + fmt, N, K, True, shift=0.005)
+    ref_packed = oracle.quantize_pack(W, fmt)
+    packed = packed_dev(ref_packed)
+    X = synth.x_fp16(N + K + M, M, K)
+    Yref = oracle.sweep(ref_packed, N, K, fmt, X)
+    smax = oracle.max_scale(ref_packed, N, K, fmt)
+    paths = [qgemm.PATH_AUTO, qgemm.PATH_MFMA] + ([qgemm.PATH_GEMV] if M <= 8 else [])
+    for path in paths:
+        Y = run_one(packed, fmt, N, K, X, M, path, ldx=K + 24, ldy=N + (4 - N % 4) % 4 + 8)
+        _check(Y, Yref, X, smax, f"path={path}")
