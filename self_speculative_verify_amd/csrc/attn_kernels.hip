@@ -8,12 +8,12 @@
 // as the weight sweep's panel rows share one weight read.
 //
 // attn_partial: one workgroup per (slot, KV head, chunk of positions), one
-// wave per 16-row block of queries.  Per step of 32 positions the keys
-// (as [position][dim]) and the values (transposed, [dim][position]) go
-// through LDS, widened to binary16 when the cache is E4M3 (exact, by the
-// hardware conversion).  Scores
-// are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_f16 (A = 16
-// positions x 32 dims of K, B = 32 dims x 16 query rows of Q), so lane l
+// wave per 16-row block of queries.  Per step of 32 positions the keys (as
+// [position][dim]) and the values (transposed, [dim][position]) go through
+// LDS, widened to binary16 when the cache is E4M3 (exactly, by the hardware
+// conversion).  Scores are computed transposed, S^T = K Q^T, with
+// v_mfma_f32_16x16x32_f16 (A = 16 positions x 32 dims of K, B = 32 dims x
+// 16 query rows of Q), so lane l
 // holds 8 scores of query row l % 16: positions 4c .. 4c + 3 and 16 + 4c ..
 // 16 + 4c + 3 of the step (c = l / 16).  The online softmax keeps a running
 // maximum per row (base-2 units) and a per-lane partial sum; the
@@ -45,8 +45,9 @@ constexpr int kBufBytes = kKBytes + kVBytes;   // one step's tiles; two buffers 
 
 // Two E4M3 bytes of the word u (bytes 0-1, or 2-3 when kHi) -> two
 // binary16 values: gfx950's scaled conversion with scale 1, exact for every
-// code (E4M3 values are binary16 values; checked against the format's
-// definition for all 256 codes, NaN included).
+// code (E4M3 values are binary16 values; the attention tests compare the
+// decoded rows with the format's definition for all 256 codes, NaN
+// included).
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 template <bool kHi>
 __device__ __forceinline__ uint32_t e4m3x2_to_h2(uint32_t u) {
@@ -151,16 +152,23 @@ __device__ __forceinline__ void step(Row& st_, f4_t (&acc)[kD / 16], const h8_t 
   const float m_new = fmaxf(st_.m, mx);
   const float ms = m_new == -__builtin_inff() ? 0.f : m_new;
   const float alpha = __builtin_amdgcn_exp2f(st_.m - ms);
+  // the sum takes the probabilities as rounded for the value product, so
+  // the output is an exact average of V under those weights
   h8_t pf;
   float ps = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; j++) {
-    const float p = __builtin_amdgcn_exp2f(x[j] - ms);
-    ps += p;
-    pf[j] = (_Float16)p;
+    pf[j] = (_Float16)__builtin_amdgcn_exp2f(x[j] - ms);
+    ps += (float)pf[j];
   }
   st_.l = st_.l * alpha + ps;
   st_.m = m_new;
+  // the accumulators need rescaling only in a step that raised some row's
+  // maximum (alpha < 1); once the maxima settle, most steps skip it
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+    for (int db = 0; db < kD / 16; db++) acc[db] *= alpha;
+  }
   // O^T[dims 16 db ..][rows] += V^T[dims][this lane's 8 positions] P^T
 #pragma unroll
   for (int db = 0; db < kD / 16; db++) {
@@ -168,7 +176,7 @@ __device__ __forceinline__ void step(Row& st_, f4_t (&acc)[kD / 16], const h8_t 
     const u2_t lo = *(const u2_t*)(vrow + 4 * c);
     const u2_t hi = *(const u2_t*)(vrow + 16 + 4 * c);
     const u4_t va = {lo.x, lo.y, hi.x, hi.y};
-    acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, va), pf, acc[db] * alpha, 0, 0, 0);
+    acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, va), pf, acc[db], 0, 0, 0);
   }
 }
 
