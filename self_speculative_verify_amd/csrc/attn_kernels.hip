@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn_internal.h"
 
 namespace qa {
@@ -35,12 +37,12 @@ typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
 
-// LDS rows padded so that the 16 rows one fragment read touches fall on
+// LDS rows padded so that the rows one fragment read touches fall on
 // distinct banks.
 constexpr int kKRow = kD + 8;                // halves per K row (528 bytes)
-constexpr int kVRow = kBlk + 4;              // halves per transposed V row (72 bytes)
+constexpr int kVRow = kD + 16;               // halves per V row (544 bytes: 4 rows step 8 banks)
 constexpr int kKBytes = kBlk * kKRow * 2;
-constexpr int kVBytes = kD * kVRow * 2;
+constexpr int kVBytes = kBlk * kVRow * 2;
 constexpr int kBufBytes = kKBytes + kVBytes;   // one step's tiles; two buffers alternate
 
 // Two E4M3 bytes of the word u (bytes 0-1, or 2-3 when kHi) -> two
@@ -54,18 +56,21 @@ __device__ __forceinline__ uint32_t e4m3x2_to_h2(uint32_t u) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u, 1.0f, kHi));
 }
 
-// Global pieces (16 bytes) of one step, for KV head g, in registers.  K is
-// read piece-fastest (a position's 512 or 256 bytes by consecutive lanes)
-// and written to LDS row by row.  V is read position-fastest, so that the
-// transposed LDS writes of consecutive lanes are consecutive halves of one
-// row (no bank conflicts).
+// Global pieces (16 bytes) of one step, for KV head g, in registers, read
+// piece-fastest (a position's 512 or 256 bytes by consecutive lanes) and
+// written to LDS row by row ([position][dim]) for K and V alike; the value
+// product reads V transposed with gfx950's transposing LDS read.
 template <bool kFp8>
 struct Tile {
+  // a piece is 8 cached elements: 16 bytes of binary16, or 8 E4M3 bytes
+  // that widen to 16; either way one 16-byte LDS write per piece, and the
+  // pieces of a position are consecutive lanes (no bank conflicts)
   static constexpr int kE = kFp8 ? 1 : 2;                 // bytes per cached element
-  static constexpr int kPerPos = kD * kE / 16;            // 16-byte pieces per position and head
+  static constexpr int kPerPos = kD / 8;                  // pieces per position and head
   static constexpr int kPieces = kBlk * kPerPos;          // per tensor and step
   static constexpr int kIters = (kPieces + kThreads - 1) / kThreads;
-  u4_t k[kIters], v[kIters];
+  typedef typename std::conditional<kFp8, u2_t, u4_t>::type piece_t;
+  piece_t k[kIters], v[kIters];
 
   // positions >= L read as zeros (they are masked; a zero keeps their
   // products zero)
@@ -73,46 +78,36 @@ struct Tile {
 #pragma unroll
     for (int i = 0; i < kIters; i++) {
       const int q = tid + kThreads * i;
-      k[i] = v[i] = u4_t{0u, 0u, 0u, 0u};
+      k[i] = v[i] = piece_t{};
       if (q >= kPieces) continue;
-      const int pk = p0 + q / kPerPos, ck = q % kPerPos;
-      const int pv = p0 + q % kBlk, cv = q / kBlk;
-      if (pk < L) k[i] = __builtin_nontemporal_load((const u4_t*)(K + ((size_t)pk * kHkv + g) * (kD * kE) + ck * 16));
-      // (ordinary loads: a wave reads 32 bytes of each of 64 lines here, and
-      // the rest of each line, read by other waves of the step, must stay
-      // in the L2 until then)
-      if (pv < L) v[i] = *(const u4_t*)(V + ((size_t)pv * kHkv + g) * (kD * kE) + cv * 16);
+      const int p = p0 + q / kPerPos, piece = q % kPerPos;
+      if (p < L) {
+        const size_t off = ((size_t)p * kHkv + g) * (kD * kE) + piece * 8 * kE;
+        k[i] = __builtin_nontemporal_load((const piece_t*)(K + off));
+        v[i] = __builtin_nontemporal_load((const piece_t*)(V + off));
+      }
     }
   }
 
-  // Into LDS: K at [position][dim], V at [dim][position] (binary16).
+  static __device__ __forceinline__ u4_t widen(const piece_t& x) {
+    if constexpr (kFp8)
+      return u4_t{e4m3x2_to_h2<false>(x[0]), e4m3x2_to_h2<true>(x[0]), e4m3x2_to_h2<false>(x[1]),
+                  e4m3x2_to_h2<true>(x[1])};
+    else
+      return x;
+  }
+
+  // Into LDS: K and V at [position][dim] (binary16).
   __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
     _Float16* ks = (_Float16*)lds;
-    uint16_t* vt = (uint16_t*)(lds + kKBytes);
+    _Float16* vs = (_Float16*)(lds + kKBytes);
 #pragma unroll
     for (int i = 0; i < kIters; i++) {
       const int q = tid + kThreads * i;
       if (q >= kPieces) continue;
-      const int pk = q / kPerPos, dk = (q % kPerPos) * (16 / kE);
-      const int pv = q % kBlk, dv = (q / kBlk) * (16 / kE);
-      if constexpr (!kFp8) {
-        *(u4_t*)(ks + pk * kKRow + dk) = k[i];
-#pragma unroll
-        for (int t = 0; t < 8; t++) vt[(dv + t) * kVRow + pv] = (uint16_t)(v[i][t >> 1] >> (16 * (t & 1)));
-      } else {
-        const u4_t lo = {e4m3x2_to_h2<false>(k[i][0]), e4m3x2_to_h2<true>(k[i][0]), e4m3x2_to_h2<false>(k[i][1]),
-                         e4m3x2_to_h2<true>(k[i][1])};
-        const u4_t hi = {e4m3x2_to_h2<false>(k[i][2]), e4m3x2_to_h2<true>(k[i][2]), e4m3x2_to_h2<false>(k[i][3]),
-                         e4m3x2_to_h2<true>(k[i][3])};
-        *(u4_t*)(ks + pk * kKRow + dk) = lo;
-        *(u4_t*)(ks + pk * kKRow + dk + 8) = hi;
-#pragma unroll
-        for (int t = 0; t < 8; t++) {
-          const uint32_t h2 = (t & 1) ? e4m3x2_to_h2<true>(v[i][t >> 1]) : e4m3x2_to_h2<false>(v[i][t >> 1]);
-          vt[(dv + 2 * t) * kVRow + pv] = (uint16_t)h2;
-          vt[(dv + 2 * t + 1) * kVRow + pv] = (uint16_t)(h2 >> 16);
-        }
-      }
+      const int p = q / kPerPos, d0 = (q % kPerPos) * 8;
+      *(u4_t*)(ks + p * kKRow + d0) = widen(k[i]);
+      *(u4_t*)(vs + p * kVRow + d0) = widen(v[i]);
     }
   }
 };
@@ -169,13 +164,22 @@ __device__ __forceinline__ void step(Row& st_, f4_t (&acc)[kD / 16], const h8_t 
 #pragma unroll
     for (int db = 0; db < kD / 16; db++) acc[db] *= alpha;
   }
-  // O^T[dims 16 db ..][rows] += V^T[dims][this lane's 8 positions] P^T
+  // O^T[dims 16 db ..][rows] += V^T[dims][this lane's 8 positions] P^T.
+  // The A fragment (lane l: dim 16 db + l % 16 at positions 4c .. 4c + 3
+  // and 16 + 4c .. 16 + 4c + 3) comes from V at [position][dim] through
+  // ds_read_b64_tr_b16: in each 16-lane group, output lane i element j is
+  // element i % 4 of the 8 bytes that lane 4j + i / 4 addresses, so lane s
+  // of group c points at position 4c + s / 4, dims 16 db + 4 (s % 4).
+  const int s_ = lane & 15;
+  const _Float16* vsrc = vt + (4 * c + (s_ >> 2)) * kVRow + 4 * (s_ & 3);
 #pragma unroll
   for (int db = 0; db < kD / 16; db++) {
-    const _Float16* vrow = vt + (16 * db + (lane & 15)) * kVRow;
-    const u2_t lo = *(const u2_t*)(vrow + 4 * c);
-    const u2_t hi = *(const u2_t*)(vrow + 16 + 4 * c);
-    const u4_t va = {lo.x, lo.y, hi.x, hi.y};
+    typedef short s4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4_t lds_s4;
+    const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vsrc + 16 * db));
+    const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vsrc + 16 * kVRow + 16 * db));
+    const u2_t l2 = __builtin_bit_cast(u2_t, lo), h2 = __builtin_bit_cast(u2_t, hi);
+    const u4_t va = {l2.x, l2.y, h2.x, h2.y};
     acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, va), pf, acc[db], 0, 0, 0);
   }
 }
