@@ -47,12 +47,19 @@ qgemm_status check(const qgemm_attn_slot* slots, int nslots, int kv) {
     if (!aligned(s.Q, 16) || !aligned(s.K, 16) || !aligned(s.V, 16) || !aligned(s.O, 16))
       return QGEMM_ERR_INVALID_ARG;
     if (s.W < 1 || s.W > qa::kMaxW || s.L < s.W || s.L > kMaxL) return QGEMM_ERR_INVALID_ARG;
-    const size_t nq = (size_t)s.W * qa::kHq * qa::kD;
-    const size_t nkv = (size_t)s.L * qa::kHkv * qa::kD * esz;
-    if (overlaps(s.O, nq * 4, s.Q, nq * 2) || overlaps(s.O, nq * 4, s.K, nkv) || overlaps(s.O, nq * 4, s.V, nkv))
-      return QGEMM_ERR_INVALID_ARG;
-    for (int j = 0; j < i; j++)
-      if (overlaps(s.O, nq * 4, slots[j].O, (size_t)slots[j].W * qa::kHq * qa::kD * 4)) return QGEMM_ERR_INVALID_ARG;
+  }
+  // an output may not overlap any slot's inputs or another output
+  for (int i = 0; i < nslots; i++) {
+    const qgemm_attn_slot& s = slots[i];
+    const size_t no = (size_t)s.W * qa::kHq * qa::kD * 4;
+    for (int j = 0; j < nslots; j++) {
+      const qgemm_attn_slot& t = slots[j];
+      const size_t nq = (size_t)t.W * qa::kHq * qa::kD * 2;
+      const size_t nkv = (size_t)t.L * qa::kHkv * qa::kD * esz;
+      if (overlaps(s.O, no, t.Q, nq) || overlaps(s.O, no, t.K, nkv) || overlaps(s.O, no, t.V, nkv))
+        return QGEMM_ERR_INVALID_ARG;
+      if (j != i && overlaps(s.O, no, t.O, (size_t)t.W * qa::kHq * qa::kD * 4)) return QGEMM_ERR_INVALID_ARG;
+    }
   }
   return QGEMM_OK;
 }

@@ -213,6 +213,10 @@ def test_attn_validation_rejects_before_any_launch():
                                0x50000000, 1 << 30, None) == qgemm.ERR_INVALID_ARG
     two = arr(slot(), slot(O=0x40000000 + 1024))                     # outputs overlap
     assert L.qgemm_attn_verify(two, 2, 0, 0.0625, 0x50000000, 1 << 30, None) == qgemm.ERR_INVALID_ARG
+    cross = arr(slot(), slot(Q=0x40000000 + 4096, O=0x48000000))        # an output over another slot's Q
+    assert L.qgemm_attn_verify(cross, 2, 0, 0.0625, 0x50000000, 1 << 30, None) == qgemm.ERR_INVALID_ARG
+    ok2 = arr(slot(), slot(O=0x48000000))
+    assert qgemm.attn_workspace_bytes(ok2, qgemm.KV_FP16) > 0
     assert L.qgemm_attn_verify(good, 1, 0, float("nan"), 0x50000000, 1 << 30, None) == qgemm.ERR_INVALID_ARG
     assert L.qgemm_attn_verify(good, 1, 0, 0.0625, 0x50000008, 1 << 30, None) == qgemm.ERR_INVALID_ARG
     assert L.qgemm_attn_verify(good, 1, 0, 0.0625, 0x50000000, ws - 256, None) == qgemm.ERR_INVALID_ARG
