@@ -119,7 +119,8 @@ typedef enum {
  *   X      : binary16 [M][ldx], 16-byte aligned, ldx % 8 == 0, K <= ldx <= 2^24
  *   Y      : fp32 [M][ldy], 16-byte aligned, ldy % 4 == 0, ldy >= N
  *   M      : 1 .. QGEMM_MAX_M
- * Y must not overlap X, any packed buffer or another job's Y. */
+ * Y must not overlap any job's X, any packed buffer or another job's Y
+ * (checked: QGEMM_ERR_INVALID_ARG); inputs may be shared between jobs. */
 typedef struct {
   const void* packed;
   const uint16_t* X;

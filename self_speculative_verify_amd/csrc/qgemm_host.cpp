@@ -52,6 +52,37 @@ int path_of(int path, int M) {
 }
 
 // y_optional: the verify head, whose Y may be null (no outputs written)
+// No job's Y overlaps any job's X, packed weights or another Y (reads may
+// share memory).  Intervals sorted by start; an interval overlaps an earlier
+// one iff that one ends after it starts, so it suffices to track the largest
+// end so far over all intervals and over the written ones.
+bool overlap_free(const qgemm_job* jobs, int njobs) {
+  struct Span {
+    uintptr_t a, b;
+    bool write;
+  };
+  std::vector<Span> v;
+  v.reserve((size_t)njobs * 3);
+  for (int i = 0; i < njobs; i++) {
+    const qgemm_job& j = jobs[i];
+    const uintptr_t x0 = (uintptr_t)j.X, p0 = (uintptr_t)j.packed;
+    v.push_back({x0, x0 + (uintptr_t)(((j.M - 1) * j.ldx + j.K) * sizeof(uint16_t)), false});
+    v.push_back({p0, p0 + (uintptr_t)(nrb_of(j.N) * nkt_of(j.K) * qg::tile_bytes(j.bits)), false});
+    if (j.Y) {
+      const uintptr_t y0 = (uintptr_t)j.Y;
+      v.push_back({y0, y0 + (uintptr_t)(((j.M - 1) * j.ldy + j.N) * sizeof(float)), true});
+    }
+  }
+  std::sort(v.begin(), v.end(), [](const Span& p, const Span& q) { return p.a < q.a; });
+  uintptr_t end_any = 0, end_write = 0;
+  for (const Span& s : v) {
+    if ((s.write ? end_any : end_write) > s.a) return false;
+    end_any = std::max(end_any, s.b);
+    if (s.write) end_write = std::max(end_write, s.b);
+  }
+  return true;
+}
+
 qgemm_status validate(const qgemm_job* jobs, int njobs, int path, bool y_optional = false) {
   if (njobs < 1 || jobs == nullptr) return QGEMM_ERR_INVALID_ARG;
   if (path != QGEMM_PATH_AUTO && path != QGEMM_PATH_GEMV && path != QGEMM_PATH_MFMA)
@@ -70,17 +101,8 @@ qgemm_status validate(const qgemm_job* jobs, int njobs, int path, bool y_optiona
     }
     if (!aligned(j.Y, 16)) return QGEMM_ERR_INVALID_ARG;
     if (j.ldy < j.N || j.ldy % 4 != 0) return QGEMM_ERR_INVALID_ARG;
-    // Y must not overlap X or the packed weights of this job
-    const uintptr_t y0 = (uintptr_t)j.Y;
-    const uintptr_t y1 = y0 + (uintptr_t)(((j.M - 1) * j.ldy + j.N) * sizeof(float));
-    const uintptr_t x0 = (uintptr_t)j.X;
-    const uintptr_t x1 = x0 + (uintptr_t)(((j.M - 1) * j.ldx + j.K) * sizeof(uint16_t));
-    const uintptr_t p0 = (uintptr_t)j.packed;
-    const uintptr_t p1 = p0 + (uintptr_t)(nrb_of(j.N) * nkt_of(j.K) * qg::tile_bytes(j.bits));
-    if (y0 < x1 && x0 < y1) return QGEMM_ERR_INVALID_ARG;
-    if (y0 < p1 && p0 < y1) return QGEMM_ERR_INVALID_ARG;
   }
-  return QGEMM_OK;
+  return overlap_free(jobs, njobs) ? QGEMM_OK : QGEMM_ERR_INVALID_ARG;
 }
 
 // ---------------------------------------------------------------------------

@@ -81,6 +81,20 @@ def test_validation_rejects(kw):
     assert qgemm.workspace_bytes(jobs) == 0
 
 
+def test_validation_rejects_overlaps_across_jobs():
+    a = _job()
+    cases = [
+        [a, _job(Y=0x10000000 + 128)],                  # two outputs overlap
+        [a, _job(Y=0x20000000, X=0x10000000 + 64)],     # a job reads another's output
+        [a, _job(Y=0x20000000, packed=0x10000000)],     # weights under another's output
+    ]
+    for jobs in cases:
+        assert qgemm.validate(jobs, qgemm.PATH_AUTO, 0x40000000, 1 << 30) == qgemm.ERR_INVALID_ARG
+    # shared inputs are fine
+    ok = [a, _job(Y=0x20000000)]
+    assert qgemm.validate(ok, qgemm.PATH_AUTO, 0x40000000, 1 << 30) == qgemm.OK
+
+
 def test_validation_accepts_and_sizes_workspace():
     jobs = [_job(), _job(Y=0x20000000, M=33, bits=5, N=17, K=416, ldx=416, ldy=20),
             _job(Y=0x30000000, bits=0x104, K=448, ldx=448), _job(Y=0x38000000, bits=0x204, M=20)]
