@@ -119,20 +119,37 @@ struct Row {
 };
 
 // One step of 32 positions from the LDS tiles: scores, online softmax, and
-// the value product into acc.
+// the value product into acc.  kH splits the dims of the score product into
+// kH independent accumulation chains per position block (more chains hide
+// the MFMA dependency latency at the cost of registers).
+template <int kH>
 __device__ __forceinline__ void step(Row& st_, f4_t (&acc)[kD / 16], const h8_t (&qf)[kD / 32], const _Float16* ks,
                                      const _Float16* vt, int pb, int lim, int lane, float scale_log2e) {
   const int c = lane >> 4;
-  // S^T for positions pb .. pb + 15 and pb + 16 .. pb + 31 (the two
-  // accumulation chains interleaved)
-  f4_t st[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // S^T for positions pb .. pb + 15 and pb + 16 .. pb + 31: 2 kH chains
+  // (two position blocks x kH parts of the dims), interleaved, then the parts
+  // added
+  f4_t sh[2][kH];
 #pragma unroll
-  for (int s = 0; s < kD / 32; s++)
+  for (int sb = 0; sb < 2; sb++)
 #pragma unroll
-    for (int sb = 0; sb < 2; sb++) {
-      const h8_t kf = *(const h8_t*)(ks + (16 * sb + (lane & 15)) * kKRow + 32 * s + 8 * c);
-      st[sb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[s], st[sb], 0, 0, 0);
-    }
+    for (int h = 0; h < kH; h++) sh[sb][h] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kD / 32 / kH; s++)
+#pragma unroll
+    for (int h = 0; h < kH; h++)
+#pragma unroll
+      for (int sb = 0; sb < 2; sb++) {
+        const int ds = h * (kD / 32 / kH) + s;
+        const h8_t kf = *(const h8_t*)(ks + (16 * sb + (lane & 15)) * kKRow + 32 * ds + 8 * c);
+        sh[sb][h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ds], sh[sb][h], 0, 0, 0);
+      }
+  f4_t st[2] = {sh[0][0], sh[1][0]};
+#pragma unroll
+  for (int h = 1; h < kH; h++) {
+    st[0] += sh[0][h];
+    st[1] += sh[1][h];
+  }
   // element j of this lane: position pb + (j < 4 ? 4c + j : 16 + 4c + j - 4)
   float x[8];
   float mx = -__builtin_inff();
@@ -220,6 +237,9 @@ __global__ void __launch_bounds__(kThreads) attn_partial(AttnArgs a) {
   // b + 1 is stored into the other buffer while step b is computed (the
   // barrier ending step b - 1 freed it).  Loads run two steps ahead in two
   // register sets: the set just stored is reloaded with step b + 3.
+  // E4M3 tiles leave registers for four score chains; fp16 tiles measured
+  // no better with four than with two
+  constexpr int kChainParts = kFp8 ? 2 : 1;
   Tile<kFp8> t0, t1;
   t0.load(S.K, S.V, g, p0, S.L, tid);
   if (nblk > 1) t1.load(S.K, S.V, g, p0 + kBlk, S.L, tid);
@@ -234,7 +254,7 @@ __global__ void __launch_bounds__(kThreads) attn_partial(AttnArgs a) {
       if (b + 3 < nblk) t1.load(S.K, S.V, g, p0 + (b + 3) * kBlk, S.L, tid);
     }
     if (active)
-      step(r_state, acc, qf, (const _Float16*)lds, (const _Float16*)(lds + kKBytes), p0 + b * kBlk, lim, lane,
+      step<kChainParts>(r_state, acc, qf, (const _Float16*)lds, (const _Float16*)(lds + kKBytes), p0 + b * kBlk, lim, lane,
            a.scale_log2e);
     __syncthreads();
     if (b + 1 >= nblk) break;
@@ -244,7 +264,7 @@ __global__ void __launch_bounds__(kThreads) attn_partial(AttnArgs a) {
       if (b + 4 < nblk) t0.load(S.K, S.V, g, p0 + (b + 4) * kBlk, S.L, tid);
     }
     if (active)
-      step(r_state, acc, qf, (const _Float16*)(lds + kBufBytes), (const _Float16*)(lds + kBufBytes + kKBytes),
+      step<kChainParts>(r_state, acc, qf, (const _Float16*)(lds + kBufBytes), (const _Float16*)(lds + kBufBytes + kKBytes),
            p0 + (b + 1) * kBlk, lim, lane, a.scale_log2e);
     __syncthreads();
   }
