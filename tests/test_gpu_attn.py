@@ -1,8 +1,9 @@
 """GPU parity of the shared-KV attention verify against the CPU oracle,
 through the C boundary: fp16 and E4M3 caches, single and multi-chunk
 positions, ragged W and L, several slots per call, repeat determinism, and
-the long-context workload the benchmark times (checked on every query row
-of a sampled set of heads)."""
+both workloads the benchmark times: one slot over 32768 positions (checked
+on every query row of a sampled set of heads) and eight slots over 8192
+each (checked on every row)."""
 import numpy as np
 import pytest
 
@@ -113,6 +114,18 @@ def test_attn_long_context_workload(kv):
         Qs[:, hs] = Q[:, hs]
         Oref = oracle.attn_verify(Qs, Kv, Vv, W, SCALE)
         _check(O[:, hs], Oref[:, hs], Vv, f"L=32768 kv head {g}")
+
+
+@pytest.mark.parametrize("kv", [qgemm.KV_FP16, qgemm.KV_FP8])
+def test_attn_eight_slot_workload(kv):
+    """The benchmark's many-slot shape: 8 slots of W = 6 over L = 8192 each,
+    in one call, every slot checked on all its query rows."""
+    W, L, n = 6, 8192, 8
+    cases = [_case(5000 + 10 * i, W, L, kv) for i in range(n)]
+    outs, _ = _run(cases, kv)
+    for i, (case, O) in enumerate(zip(cases, outs)):
+        Q, _, _, Kv, Vv = case
+        _check(O, oracle.attn_verify(Q, Kv, Vv, W, SCALE), Vv, f"slot {i}")
 
 
 @pytest.mark.parametrize("kv", [qgemm.KV_FP16, qgemm.KV_FP8])
