@@ -7,7 +7,6 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
-#include <map>
 #include <mutex>
 #include <vector>
 
@@ -157,76 +156,13 @@ int class_of(int kind, int M) {
 
 int cu_count();
 
-// Wave range boundaries that fall inside a row group (after its first step
-// and at or before its last): each one costs a partial-sum exchange.
-int64_t cut_row_groups(const std::vector<JobDesc>& descs, int64_t T, int64_t W) {
-  const int64_t q = T / W, rem = T % W;
-  int64_t cuts = 0;
-  size_t j = 0;
-  for (int64_t w = 1; w < W; w++) {
-    const int64_t f = w * q + std::min(w, rem);  // start of wave w (as in the kernel)
-    while (f >= descs[j].uend) j++;
-    const int64_t wt = qg::unit_weight(descs[j].fmt), span = (int64_t)descs[j].nkt * wt;
-    const int64_t r = (f - descs[j].ubeg) % span;
-    if (r > 0 && r <= span - wt) cuts++;
-  }
-  return cuts;
-}
-
-// Waves of a stream launch.  Every wave must hold at least one step
-// (contributor counts rely on it), which kMaxUnitWeight units per wave
-// guarantee, so W <= T / kMaxUnitWeight.  Otherwise W is kStreamWaves
-// (enough to fill the chip), unless a count in [kStreamMinWaves,
-// kStreamWaves] that gives every wave a whole number of one job's row groups
-// cuts fewer row groups; ties go to the most waves.  Depends on the shapes
-// only, never on M.
-int64_t stream_waves_uncached(const std::vector<JobDesc>& descs, int64_t T) {
-  const int64_t wmax = std::max<int64_t>(1, T / qg::kMaxUnitWeight);
-  if (wmax <= qg::kStreamMinWaves) return wmax;
-  std::vector<int64_t> cand = {std::min<int64_t>(qg::kStreamWaves, wmax)};
-  for (const auto& d : descs)
-    for (int64_t k = 1; k <= 8; k++) {
-      const int64_t per = k * d.nkt * qg::unit_weight(d.fmt);
-      if (T % per == 0) cand.push_back(T / per);
-    }
-  int64_t best = -1, best_cuts = 0;
-  for (int64_t W : cand) {
-    if (W < qg::kStreamMinWaves || W > qg::kStreamWaves || W > wmax) continue;
-    const int64_t cuts = cut_row_groups(descs, T, W);
-    if (best < 0 || cuts < best_cuts || (cuts == best_cuts && W > best)) {
-      best = W;
-      best_cuts = cuts;
-    }
-  }
-  return best < 0 ? std::min<int64_t>(wmax, qg::kStreamWaves) : best;
-}
-
-// The choice above walks up to kStreamWaves boundaries per candidate, which
-// is too slow to repeat on every sweep call; it is a pure function of the
-// launch's row-group shapes, so it is memoized per shape signature (a bounded
-// cache; shapes only, never pointers or M).
-int64_t stream_waves(const std::vector<JobDesc>& descs, int64_t T) {
-  if (T / qg::kMaxUnitWeight <= qg::kStreamMinWaves) return std::max<int64_t>(1, T / qg::kMaxUnitWeight);
-  std::vector<int64_t> key;
-  key.reserve(2 * descs.size() + 1);
-  key.push_back(T);
-  for (const auto& d : descs) {
-    key.push_back(d.nkt);
-    key.push_back(d.nrg);
-    key.push_back(d.fmt);
-  }
-  static std::mutex mu;
-  static std::map<std::vector<int64_t>, int64_t> cache;
-  {
-    std::lock_guard<std::mutex> g(mu);
-    auto it = cache.find(key);
-    if (it != cache.end()) return it->second;
-  }
-  const int64_t W = stream_waves_uncached(descs, T);
-  std::lock_guard<std::mutex> g(mu);
-  if (cache.size() >= 256) cache.clear();
-  cache.emplace(std::move(key), W);
-  return W;
+// Waves of a stream launch: kStreamWaves, or kStreamWavesBig for a launch of
+// at least kStreamBigUnits units, but never more than T / kMaxUnitWeight, so
+// that every wave holds at least one step (contributor counts rely on it).
+// Depends on the shapes only, never on M.
+int64_t stream_waves(int64_t T) {
+  const int64_t base = T >= qg::kStreamBigUnits ? qg::kStreamWavesBig : qg::kStreamWaves;
+  return std::max<int64_t>(1, std::min<int64_t>(base, T / qg::kMaxUnitWeight));
 }
 
 Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* keys = nullptr) {
@@ -312,7 +248,7 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* k
       off = round_up(off + l.descs.size() * sizeof(JobDesc) + l.index.size() * sizeof(int32_t), 256);
     }
     if (l.kind != kGroupMfma) {
-      l.nwaves = (int)stream_waves(l.descs, l.total);
+      l.nwaves = (int)stream_waves(l.total);
       l.counters_off = coff;
       coff = round_up(coff + (size_t)l.rgs * sizeof(int), 256);
       l.slots_off = soff;

@@ -32,12 +32,16 @@ constexpr int kMaxInline = 12;       // jobs passed by value in the kernel argum
 constexpr int kXRowBytes = 272;      // LDS row stride of a staged X chunk (256 + 16 pad)
 
 // stream kernel (panels of at most 16 rows): waves per workgroup, and the
-// range of waves in the grid.  The count is chosen from the shapes alone --
-// never from the device or M -- so the K split of every row group, and with it
-// every output bit, is reproducible.
+// waves in the grid.  The count is chosen from the shapes alone -- never from
+// the device or M -- so the K split of every row group, and with it every
+// output bit, is reproducible.  Launches of at least kStreamBigUnits units
+// (2 GiB of weights) take twice as many waves: two per SIMD keep more loads
+// in flight over a long stream, while a shorter launch loses more to the
+// extra waves' start-up and exchange than it gains.
 constexpr int kStreamWavesPerBlock = 4;
-constexpr int kStreamMinWaves = 1024;
 constexpr int kStreamWaves = 1024;
+constexpr int kStreamWavesBig = 2048;
+constexpr int64_t kStreamBigUnits = (int64_t)1 << 24;
 // group kernel (17..64 rows): waves per workgroup (three per SIMD where the
 // registers allow it: padded rows 32 and 48), 16-row blocks per wave
 constexpr int group_waves(int mpad) { return mpad >= 64 ? 8 : 12; }
