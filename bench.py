@@ -391,8 +391,9 @@ def main():
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the sweep shards "
-              "along N with no collective; see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the sweep shards "
+              "along N with no collective, so one GPU's share at its real shape is what it times",
+              file=sys.stderr)
         sys.exit(2)
 
     import __graft_entry__
