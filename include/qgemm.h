@@ -87,7 +87,7 @@ extern "C" {
 typedef enum {
   QGEMM_OK = 0,
   QGEMM_ERR_INVALID_ARG = 1,  /* an argument fails the rules below; nothing enqueued */
-  QGEMM_ERR_UNSUPPORTED = 2,  /* valid arguments this build cannot run (e.g. path) */
+  QGEMM_ERR_UNSUPPORTED = 2,  /* valid arguments the library cannot run (e.g. path) */
   QGEMM_ERR_NONFINITE = 3,    /* pack: NaN/Inf weight or a scale that overflows fp16 */
   QGEMM_ERR_HIP = 4           /* a HIP runtime call or launch failed */
 } qgemm_status;

@@ -1,7 +1,7 @@
 // Host-only stand-ins for the HIP runtime calls and the kernel launchers that
 // the library's host code (qgemm_host.cpp, attn_host.cpp) makes, for building
 // that code under AddressSanitizer and UndefinedBehaviorSanitizer on a machine
-// without a GPU.  Every "device" buffer in this build is host memory, so each
+// without a GPU.  Every "device" buffer is then host memory, so each
 // launcher stand-in touches the memory its kernel would touch -- the first
 // and last element of every region the kernel reads or writes, as the kernel
 // computes it from its arguments -- and checks the arguments' invariants.  A
