@@ -340,13 +340,16 @@ __device__ __forceinline__ const QG_CONST JobDesc* job_table(const SweepArgs& a)
 // on another wave.  The slots and counters are accessed with system-scope
 // atomics, which bypass the per-XCD L2 caches (not coherent with each other).
 //
-// MFMA: v_mfma_f32_16x16x32_f16 with A = X (16 rows m x 32 k of one group)
-// and B = codes (32 k x 16 rows n): lane l supplies A row m = l%16 and B
-// column n = l%16, both for k chunk l/16 -- exactly the lane's 16 code bytes
-// -- and holds D for (m = 4(l/16) + i, n = l%16).  The group's scale (one per
-// lane) multiplies D before it is added to the accumulators; only the kA rows
-// that can hold m < M are kept.  X rows m >= M read row M-1 and feed only
-// output rows that are never stored (MFMA rows are independent).
+// MFMA: v_mfma_f32_16x16x32_f16 with A = X (16 rows x 32 k of one group)
+// and B = codes (32 k x 16 rows n): lane l supplies A row l%16 and B column
+// n = l%16, both for k chunk l/16 -- exactly the lane's 16 code bytes -- and
+// holds D rows 4(l/16) + i of column n.  X row m is placed at A row
+// 4(m%4) + m/4, so it comes out in lane group g = m%4, accumulator i = m/4
+// (m = g + 4i): a panel of at most 4 kA rows keeps kA = ceil(class / 4)
+// accumulators per lane, and the group's scale (one per lane) multiplies only
+// those.  A rows whose m >= M read X row M-1 and feed outputs that are never
+// stored (MFMA rows are independent).  The placement is the same for every
+// class, so a row's arithmetic does not depend on the panel height.
 // GEMV: lane l = r + 16c forms, for row n = r and each m, four v_dot2_f32_f16
 // over its 8 codes of a group, scaled by the group's scale; the four k chunks
 // of a row (lanes r, r+16, r+32, r+48) are summed when the row group is
@@ -356,7 +359,11 @@ __device__ __forceinline__ const QG_CONST JobDesc* job_table(const SweepArgs& a)
 template <bool kMfma, int kCap>
 struct Stream {
   static constexpr int kR = stream_rows(kMfma ? 1 : 0, kCap);        // row blocks per step
-  static constexpr int kA = kMfma ? (kCap < 4 ? kCap : 4) : kCap;    // accumulators per row block
+  static constexpr int kA = kMfma ? (kCap + 3) / 4 : kCap;           // accumulators per row block
+  // Partial-sum slots hold a row group's rows at positions 0 .. class - 1,
+  // a lane's accumulators side by side: position kA g + i is row g + 4 i
+  // (MFMA), position m row m (GEMV).
+  static __device__ __forceinline__ int slot_row(int p) { return kMfma ? p / kA + 4 * (p % kA) : p; }
   static constexpr int kXP = kMfma ? 4 : (kCap * 16 + 63) / 64;      // X loads per lane per step
   // steps in flight per wave: about 8 tiles (9-11 KB) per wave
   static constexpr int kDepth = 4;
@@ -460,7 +467,7 @@ struct Stream {
     const int last = first + (nkt - 1) * wt;       // ... and of its last step
     const int nn = lane & 15;
     // row m held by this lane in accumulator i (MFMA), or m = i (GEMV, lanes < 16)
-    auto row_of = [&](int i) { return kMfma ? 4 * (lane >> 4) + i : i; };
+    auto row_of = [&](int i) { return kMfma ? (lane >> 4) + 4 * i : i; };
     const bool holder = kMfma || lane < 16;
     if (first >= cx.a && last < cx.b) {
       const bool keys = D[j].keys != nullptr;
@@ -489,11 +496,12 @@ struct Stream {
     const uint32_t sbase = (uint32_t)((cx.gw * 2 + kind) * srows * kR * kTileRows) * 4u;
     const __amdgpu_buffer_rsrc_t sr = slot_rsrc(cx);
     if constexpr (kMfma) {
-      const int m0 = 4 * (lane >> 4);
-      if (m0 < srows) {
+      // this lane's rows go to slot positions kA g .. kA g + kA - 1
+      const int p0 = kA * (lane >> 4);
+      if (p0 < srows) {
 #pragma unroll
         for (int r = 0; r < kR; r++) {
-          const uint32_t o = sbase + (uint32_t)(((r * kTileRows + nn) * srows + m0) * 4);
+          const uint32_t o = sbase + (uint32_t)(((r * kTileRows + nn) * srows + p0) * 4);
           if constexpr (kA == 4) {
             const f4_t v = {acc[r][0], acc[r][1], acc[r][2], acc[r][3]};
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, v), sr, o, 0, kCoherent);
@@ -594,7 +602,7 @@ struct Stream {
           for (int c = 0; c < kChunksPerLane; c++)
             if (w + t <= wl) v[c] += p[t][c];
       }
-      // verify head: element t of every chunk of this lane is row
+      // verify head: element t of every chunk of this lane is slot position
       // (4 lane + t) mod srows (64 chunks of 4 elements span whole columns)
       unsigned long long kb[4] = {0ull, 0ull, 0ull, 0ull};
       const bool keys = D[j].keys != nullptr;
@@ -604,7 +612,7 @@ struct Stream {
         if (q >= nchunks) continue;
 #pragma unroll
         for (int t = 0; t < 4; t++) {
-          const int e = 4 * q + t, col = e / srows, m = e - col * srows;
+          const int e = 4 * q + t, col = e / srows, m = slot_row(e - col * srows);
           const int n = rg * cols + col;
           if (m < M && n < N) {
             if (Y) Y[(int64_t)m * ldy + n] = v[c][t];
@@ -613,13 +621,13 @@ struct Stream {
         }
       }
       if (keys) {
-        // lanes l and l' hold the same rows when l = l' mod max(srows / 4, 1)
+        // lanes l and l' hold the same positions when l = l' mod max(srows / 4, 1)
         const int per = srows >= 4 ? srows / 4 : 1;
 #pragma unroll
         for (int t = 0; t < 4; t++) {
           unsigned long long k = kb[t];
           for (int msk = per; msk < 64; msk <<= 1) k = umax64(k, __shfl_xor(k, msk));
-          const int m = (4 * lane + t) % srows;
+          const int m = slot_row((4 * lane + t) % srows);
           if (lane < per && m < M && k != 0ull) key_max(D[j].keys + (cx.gw % kKeyCopies) * kKeyRows + m, k);
         }
       }
@@ -801,7 +809,9 @@ struct Stream {
     // lane byte offsets into X (fit 32 bits: host check)
     uint32_t xlane[kXP];
     if constexpr (kMfma) {
-      const int m = (lane & 15) < M ? (lane & 15) : M - 1;
+      // A row r = l % 16 carries X row (r / 4) + 4 (r % 4)
+      const int ar = lane & 15, mr = (ar >> 2) + 4 * (ar & 3);
+      const int m = mr < M ? mr : M - 1;
       xlane[0] = 2u * (uint32_t)(m * ldx + 8 * (lane >> 4));
     } else {
 #pragma unroll
@@ -882,7 +892,7 @@ struct Stream {
 #pragma unroll
     for (int i = 0; i < kA; i++) {
       const unsigned long long k = lanes_max<1, 16>(cx.best[i]);
-      const int m = kMfma ? 4 * (lane >> 4) + i : i;
+      const int m = kMfma ? (lane >> 4) + 4 * i : i;
       if ((lane & 15) == 0 && (kMfma || lane == 0) && m < M && k != 0ull) key_max(keys + m, k);
       cx.best[i] = 0ull;
     }
