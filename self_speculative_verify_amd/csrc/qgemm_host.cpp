@@ -18,7 +18,7 @@ hipError_t launch_pack(const float* W, int64_t ldw, int N, int K, int bits, void
                        unsigned* flag, hipStream_t stream);
 hipError_t launch_fill_zero(void* p, int64_t words, hipStream_t stream);
 int sweep_blocks_per_cu(int kind, int cls, bool all);
-hipError_t launch_sweep(int kind, int cls, bool all, const SweepArgs& args, int grid, hipStream_t stream);
+hipError_t launch_sweep(int kind, int cls, bool all, bool big, const SweepArgs& args, int grid, hipStream_t stream);
 hipError_t launch_accept(const AcceptArgs& a, unsigned long long* keys, const int32_t* drafts, int32_t* argmax,
                          float* maxval, int32_t* accepted, hipStream_t stream);
 }  // namespace qg
@@ -115,6 +115,8 @@ struct Launch {
   int kind;
   int cls;
   bool all = false;           // some job uses a format beyond the 4/5-bit group-32 ones
+  bool big = false;           // stream: at least kStreamBigBytes of weights
+  int64_t bytes = 0;          // weight bytes of its jobs
   std::vector<JobDesc> descs;
   int64_t total = 0;          // stream: flat units; group: row-block groups
   int64_t rgs = 0;            // stream: row groups (arrival counters)
@@ -156,12 +158,12 @@ int class_of(int kind, int M) {
 
 int cu_count();
 
-// Waves of a stream launch: kStreamWaves, or kStreamWavesBig for a launch of
-// at least kStreamBigUnits units, but never more than T / kMaxUnitWeight, so
-// that every wave holds at least one step (contributor counts rely on it).
-// Depends on the shapes only, never on M.
-int64_t stream_waves(int64_t T) {
-  const int64_t base = T >= qg::kStreamBigUnits ? qg::kStreamWavesBig : qg::kStreamWaves;
+// Waves of a stream launch: kStreamWaves, or kStreamWavesBig for a big one,
+// but never more than T / kMaxUnitWeight, so that every wave holds at least
+// one step (contributor counts rely on it).  Depends on the shapes only,
+// never on M.
+int64_t stream_waves(int64_t T, bool big) {
+  const int64_t base = big ? qg::kStreamWavesBig : qg::kStreamWaves;
   return std::max<int64_t>(1, std::min<int64_t>(base, T / qg::kMaxUnitWeight));
 }
 
@@ -177,19 +179,31 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* k
     if (ga != gb) return gb;  // stream jobs first, in order
     return ga && jobs[a].K > jobs[b].K;
   });
+  // each job's launch (kind, class), and every launch's weight bytes, which
+  // decide its step shape before any job is laid out
+  std::vector<int> dst_of(njobs);
   for (int i : order) {
     const qgemm_job& j = jobs[i];
     const int kind = kind_of(path, j.M);
     const int cls = class_of(kind, j.M);
-    Launch* dst = nullptr;
-    for (auto& l : P.launches)
-      if (l.kind == kind && l.cls == cls) dst = &l;
-    if (!dst) {
+    int li = -1;
+    for (size_t k = 0; k < P.launches.size(); k++)
+      if (P.launches[k].kind == kind && P.launches[k].cls == cls) li = (int)k;
+    if (li < 0) {
       P.launches.push_back(Launch{});
-      dst = &P.launches.back();
-      dst->kind = kind;
-      dst->cls = cls;
+      li = (int)P.launches.size() - 1;
+      P.launches[li].kind = kind;
+      P.launches[li].cls = cls;
     }
+    dst_of[i] = li;
+    P.launches[li].bytes += nrb_of(j.N) * nkt_of(j.K) * qg::tile_bytes(j.bits);
+  }
+  // the MFMA stream kernel has the eight-block step shape for big launches
+  for (auto& l : P.launches) l.big = l.bytes >= qg::kStreamBigBytes;
+  for (int i : order) {
+    const qgemm_job& j = jobs[i];
+    Launch* dst = &P.launches[dst_of[i]];
+    const int kind = dst->kind, cls = dst->cls;
     if (j.bits != qg::kFmtQ4 && j.bits != qg::kFmtQ5) dst->all = true;
     JobDesc d;
     std::memset(&d, 0, sizeof(d));
@@ -213,7 +227,7 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* k
       dst->total += groups;
       d.grp_end = (int32_t)std::min(dst->total, kMaxSteps);
     } else {
-      const int R = qg::stream_rows(kind, cls);
+      const int R = qg::stream_rows(dst->big && kind == kStreamMfma);
       d.nrg = (d.nrb + R - 1) / R;
       d.ubeg = (int32_t)std::min(dst->total, kMaxSteps);
       dst->total += (int64_t)d.nrg * d.nkt * qg::unit_weight(d.fmt);
@@ -248,11 +262,11 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* k
       off = round_up(off + l.descs.size() * sizeof(JobDesc) + l.index.size() * sizeof(int32_t), 256);
     }
     if (l.kind != kGroupMfma) {
-      l.nwaves = (int)stream_waves(l.total);
+      l.nwaves = (int)stream_waves(l.total, l.big);
       l.counters_off = coff;
       coff = round_up(coff + (size_t)l.rgs * sizeof(int), 256);
       l.slots_off = soff;
-      const size_t slot_floats = (size_t)l.cls * qg::stream_rows(l.kind, l.cls) * qg::kTileRows;
+      const size_t slot_floats = (size_t)l.cls * qg::stream_rows(l.big && l.kind == kStreamMfma) * qg::kTileRows;
       soff = round_up(soff + (size_t)2 * l.nwaves * slot_floats * sizeof(float), 256);
     }
   }
@@ -620,7 +634,8 @@ qgemm_status launch_plan(const Plan& P, uint8_t* tables, uint8_t* counters, uint
       args.rem = (int32_t)(l.total % l.nwaves);
       args.slot_rows = l.cls;
     }
-    if (qg::launch_sweep(l.kind, l.cls, l.all, args, grid_of(l), s) != hipSuccess) return QGEMM_ERR_HIP;
+    if (qg::launch_sweep(l.kind, l.cls, l.all, l.big && l.kind == kStreamMfma, args, grid_of(l), s) != hipSuccess)
+      return QGEMM_ERR_HIP;
   }
   return QGEMM_OK;
 }

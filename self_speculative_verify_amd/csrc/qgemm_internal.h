@@ -34,24 +34,25 @@ constexpr int kXRowBytes = 272;      // LDS row stride of a staged X chunk (256 
 // stream kernel (panels of at most 16 rows): waves per workgroup, and the
 // waves in the grid.  The count is chosen from the shapes alone -- never from
 // the device or M -- so the K split of every row group, and with it every
-// output bit, is reproducible.  Launches of at least kStreamBigUnits units
-// (2 GiB of weights) take twice as many waves: two per SIMD keep more loads
-// in flight over a long stream, while a shorter launch loses more to the
-// extra waves' start-up and exchange than it gains.
+// output bit, is reproducible.  A launch of at least kStreamBigBytes of
+// weights is "big": twice the waves (two per SIMD keep more loads in flight
+// over a long stream, while a shorter launch loses more to the extra waves'
+// start-up and exchange than it gains) and, on the MFMA path, steps of twice
+// the row blocks (one X chunk serves eight weight tiles instead of four),
+// two of them in flight instead of four.
 constexpr int kStreamWavesPerBlock = 4;
 constexpr int kStreamWaves = 1024;
 constexpr int kStreamWavesBig = 2048;
-constexpr int64_t kStreamBigUnits = (int64_t)1 << 24;
+constexpr int64_t kStreamBigBytes = (int64_t)4 << 30;
 // group kernel (17..64 rows): waves per workgroup (three per SIMD where the
 // registers allow it: padded rows 32 and 48), 16-row blocks per wave
 constexpr int group_waves(int mpad) { return mpad >= 64 ? 8 : 12; }
 constexpr int kGroupRows = 2;
 
-// Stream kernels walk "steps": one k tile of a row group of kStreamRows
+// Stream kernels walk "steps": one k tile of a row group of stream_rows(big)
 // consecutive 16-row blocks.  The same for every class of a path, so the K
 // split of a row -- and with it every output bit -- does not depend on M.
-constexpr int kStreamRows = 4;
-constexpr int stream_rows(int kind, int cls) { return (void)kind, (void)cls, kStreamRows; }
+constexpr int stream_rows(bool big) { return big ? 8 : 4; }
 
 inline __host__ __device__ constexpr int tile_bytes(int f) {
   return f == kFmtQ5 ? kTile5 : f == kFmtG64 ? kTileG64 : f == kFmtZP ? kTileZP : kTile4;
@@ -82,7 +83,7 @@ struct JobDesc {
   int32_t nkt;           // ceil(K / 128)
   int32_t ngroups;       // K / 32
   int32_t nrb;           // ceil(N / 16)
-  int32_t nrg;           // stream kernel: row groups, ceil(nrb / stream_rows)
+  int32_t nrg;           // stream kernel: row groups, ceil(nrb / stream_rows(big))
   int32_t rg_begin;      // stream kernel: first arrival counter of this job
   int32_t grp_begin;     // group kernel: first row-block group of this job
   int32_t grp_end;

@@ -356,17 +356,17 @@ __device__ __forceinline__ const QG_CONST JobDesc* job_table(const SweepArgs& a)
 // written.  X chunks go through a small wave-private LDS buffer.
 // Padding groups (beyond K) have codes q = 0 and scale +0, and their X reads
 // are clamped into the row, so they add exact zeros: no tile needs a branch.
-template <bool kMfma, int kCap>
+template <bool kMfma, int kCap, bool kBig>
 struct Stream {
-  static constexpr int kR = stream_rows(kMfma ? 1 : 0, kCap);        // row blocks per step
+  static constexpr int kR = stream_rows(kBig);                        // row blocks per step
   static constexpr int kA = kMfma ? (kCap + 3) / 4 : kCap;           // accumulators per row block
   // Partial-sum slots hold a row group's rows at positions 0 .. class - 1,
   // a lane's accumulators side by side: position kA g + i is row g + 4 i
   // (MFMA), position m row m (GEMV).
   static __device__ __forceinline__ int slot_row(int p) { return kMfma ? p / kA + 4 * (p % kA) : p; }
   static constexpr int kXP = kMfma ? 4 : (kCap * 16 + 63) / 64;      // X loads per lane per step
-  // steps in flight per wave: about 8 tiles (9-11 KB) per wave
-  static constexpr int kDepth = 4;
+  // steps in flight per wave: 16 tiles (17-23 KB) per wave either way
+  static constexpr int kDepth = kBig ? 2 : 4;
 
   // one step's loads: codes, scales (group 64: the pair of word s.x), the
   // side word (5-bit high bits or zero points) and the X chunk
@@ -958,9 +958,9 @@ struct Stream {
   }
 };
 
-template <bool kMfma, int kCap, bool kAll>
+template <bool kMfma, int kCap, bool kAll, bool kBig>
 __global__ void __launch_bounds__(64 * kStreamWavesPerBlock) stream_kernel(SweepArgs args) {
-  using S = Stream<kMfma, kCap>;
+  using S = Stream<kMfma, kCap, kBig>;
   __shared__ __attribute__((aligned(16))) uint8_t xs[kStreamWavesPerBlock][kMfma ? 16 : kCap * kXRowBytes];
   S::template run<kAll>(args, xs[threadIdx.x >> 6]);
 }
@@ -1373,22 +1373,22 @@ typedef void (*sweep_fn)(SweepArgs);
 // kind: 0 = stream GEMV (cls = rows 1, 2, 4, 8), 1 = stream MFMA (cls 1, 2, 4, 8, 16),
 //       2 = group MFMA (cls = padded rows 32, 48, 64); all: some job uses a
 //       format other than the 4- and 5-bit group-32 ones
-template <bool kAll>
+template <bool kAll, bool kBig>
 static sweep_fn pick_set(int kind, int cls) {
   if (kind == 0) {
     switch (cls) {
-      case 1: return stream_kernel<false, 1, kAll>;
-      case 2: return stream_kernel<false, 2, kAll>;
-      case 4: return stream_kernel<false, 4, kAll>;
-      case 8: return stream_kernel<false, 8, kAll>;
+      case 1: return stream_kernel<false, 1, kAll, false>;
+      case 2: return stream_kernel<false, 2, kAll, false>;
+      case 4: return stream_kernel<false, 4, kAll, false>;
+      case 8: return stream_kernel<false, 8, kAll, false>;
     }
   } else if (kind == 1) {
     switch (cls) {
-      case 1: return stream_kernel<true, 1, kAll>;
-      case 2: return stream_kernel<true, 2, kAll>;
-      case 4: return stream_kernel<true, 4, kAll>;
-      case 8: return stream_kernel<true, 8, kAll>;
-      case 16: return stream_kernel<true, 16, kAll>;
+      case 1: return stream_kernel<true, 1, kAll, kBig>;
+      case 2: return stream_kernel<true, 2, kAll, kBig>;
+      case 4: return stream_kernel<true, 4, kAll, kBig>;
+      case 8: return stream_kernel<true, 8, kAll, kBig>;
+      case 16: return stream_kernel<true, 16, kAll, kBig>;
     }
   } else {
     switch (cls) {
@@ -1399,12 +1399,17 @@ static sweep_fn pick_set(int kind, int cls) {
   }
   return nullptr;
 }
-static sweep_fn pick(int kind, int cls, bool all) { return all ? pick_set<true>(kind, cls) : pick_set<false>(kind, cls); }
+// big: the MFMA stream kernel with eight-block steps (GEMV and group kernels
+// have one step shape)
+static sweep_fn pick(int kind, int cls, bool all, bool big) {
+  if (big) return all ? pick_set<true, true>(kind, cls) : pick_set<false, true>(kind, cls);
+  return all ? pick_set<true, false>(kind, cls) : pick_set<false, false>(kind, cls);
+}
 
 int sweep_threads(int kind, int cls) { return kind == 2 ? 64 * group_waves(cls) : 64 * kStreamWavesPerBlock; }
 
 int sweep_blocks_per_cu(int kind, int cls, bool all) {
-  sweep_fn f = pick(kind, cls, all);
+  sweep_fn f = pick(kind, cls, all, false);
   if (!f) return 0;
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void*)f, sweep_threads(kind, cls), 0) != hipSuccess)
@@ -1412,8 +1417,9 @@ int sweep_blocks_per_cu(int kind, int cls, bool all) {
   return nb;
 }
 
-hipError_t launch_sweep(int kind, int cls, bool all, const SweepArgs& args, int grid, hipStream_t stream) {
-  sweep_fn f = pick(kind, cls, all);
+hipError_t launch_sweep(int kind, int cls, bool all, bool big, const SweepArgs& args, int grid, hipStream_t stream) {
+  if (big && kind != 1) return hipErrorInvalidValue;
+  sweep_fn f = pick(kind, cls, all, big);
   if (!f) return hipErrorInvalidValue;
   hipLaunchKernelGGL(f, dim3(grid), dim3(sweep_threads(kind, cls)), 0, stream, args);
   return hipGetLastError();

@@ -67,7 +67,7 @@ void run_or_record(hipStream_t s, std::function<void()> f) {
 int64_t tiles_bytes(const qg::JobDesc& d) { return (int64_t)d.nrb * d.nkt * qg::tile_bytes(d.fmt); }
 
 // What one sweep launch touches, from its arguments alone.
-void sweep_footprint(int kind, int cls, const qg::SweepArgs a, int grid) {
+void sweep_footprint(int kind, int cls, bool big, const qg::SweepArgs a, int grid) {
   CHECK(a.njobs >= 1 && a.total >= 1 && grid >= 1);
   std::vector<qg::JobDesc> D(a.njobs);
   if (a.table) {
@@ -79,6 +79,8 @@ void sweep_footprint(int kind, int cls, const qg::SweepArgs a, int grid) {
     for (int j = 0; j < a.njobs; j++) D[j] = a.inl[j];
   }
   const bool stream = kind != 2;
+  CHECK(!big || kind == 1);
+  const int R = qg::stream_rows(big);
   int64_t rgs = 0;
   for (int j = 0; j < a.njobs; j++) {
     const qg::JobDesc& d = D[j];
@@ -93,7 +95,7 @@ void sweep_footprint(int kind, int cls, const qg::SweepArgs a, int grid) {
       // units of the jobs tile [0, total) in order
       CHECK(d.ubeg == (j == 0 ? 0 : D[j - 1].uend));
       CHECK(d.uend - d.ubeg == (int64_t)d.nrg * d.nkt * qg::unit_weight(d.fmt));
-      CHECK(d.nrg == (d.nrb + qg::kStreamRows - 1) / qg::kStreamRows);
+      CHECK(d.nrg == (d.nrb + R - 1) / R);
       CHECK(d.rg_begin == rgs);
       rgs += d.nrg;
     } else {
@@ -110,7 +112,7 @@ void sweep_footprint(int kind, int cls, const qg::SweepArgs a, int grid) {
     CHECK(a.q >= qg::kMaxUnitWeight || a.nwaves == 1);  // every wave holds at least one step
     CHECK(a.slot_rows == cls);
     span_w(a.counters, (size_t)rgs * sizeof(int));
-    span_w(a.slots, (size_t)2 * a.nwaves * a.slot_rows * qg::kStreamRows * qg::kTileRows * sizeof(float));
+    span_w(a.slots, (size_t)2 * a.nwaves * a.slot_rows * R * qg::kTileRows * sizeof(float));
     if (a.index) {
       // uend of every job, then the job holding the first unit of each bucket
       const int64_t nb = ((int64_t)a.total >> a.bshift) + 1;
@@ -155,11 +157,12 @@ hipError_t launch_fill_zero(void* p, int64_t words, hipStream_t stream) {
   return hipSuccess;
 }
 
-hipError_t launch_sweep(int kind, int cls, bool all, const SweepArgs& args, int grid, hipStream_t stream) {
+hipError_t launch_sweep(int kind, int cls, bool all, bool big, const SweepArgs& args, int grid,
+                        hipStream_t stream) {
   (void)all;
   CHECK(kind >= 0 && kind <= 2);
   const SweepArgs a = args;  // by value, as a kernel argument
-  run_or_record(stream, [=] { sweep_footprint(kind, cls, a, grid); });
+  run_or_record(stream, [=] { sweep_footprint(kind, cls, big, a, grid); });
   return hipSuccess;
 }
 
