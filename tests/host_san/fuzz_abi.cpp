@@ -15,6 +15,7 @@
 #include "qgemm.h"
 
 extern long g_launches;
+extern long g_big_launches;
 
 #define EXPECT(c)                                                                         \
   do {                                                                                    \
@@ -133,6 +134,40 @@ void sweep_case() {
     EXPECT(qgemm_sweep_path(bad.data(), (int)bad.size(), path, ws, wsb, nullptr) == QGEMM_ERR_INVALID_ARG);
   }
   broken_sweep(jobs, path, ws, wsb);
+}
+
+// A launch of at least 4 GiB of weights (the stream kernel's big step
+// shape): one or several large jobs, M within the stream classes.  Only the
+// ends of each buffer are touched, so the allocations stay virtual.
+void big_case() {
+  const int M = (int)rnd(1, 16), path = rnd(0, 1) ? QGEMM_PATH_AUTO : QGEMM_PATH_MFMA;
+  const int n = rnd(0, 1) ? 1 : (int)rnd(13, 16);
+  std::vector<qgemm_job> jobs;
+  int64_t bytes = 0;
+  for (int i = 0; i < n; i++) {
+    qgemm_job j;
+    std::memset(&j, 0, sizeof(j));
+    j.bits = kFmts[rnd(0, 3)];
+    j.K = n == 1 ? 65536 : 16384;
+    j.N = n == 1 ? rnd(140000, 200000) : rnd(40000, 50000);
+    j.M = M;
+    j.ldx = j.K;
+    j.ldy = round_up(j.N, 4);
+    const size_t pb = qgemm_packed_bytes(j.bits, j.N, j.K);
+    bytes += (int64_t)pb;
+    j.packed = alloc(pb);
+    j.X = (const uint16_t*)alloc((size_t)((M - 1) * j.ldx + j.K) * 2);
+    j.Y = (float*)alloc((size_t)((M - 1) * j.ldy + j.N) * 4);
+    jobs.push_back(j);
+  }
+  EXPECT(bytes >= ((int64_t)4 << 30));
+  const size_t wsb = qgemm_workspace_bytes(jobs.data(), n, path);
+  void* ws = workspace(wsb);
+  g_calls++;
+  const long big0 = g_big_launches;
+  EXPECT(qgemm_sweep_path(jobs.data(), n, path, ws, wsb, nullptr) == QGEMM_OK);
+  EXPECT(g_big_launches == big0 + 1);
+  EXPECT(qgemm_sweep_path(jobs.data(), n, path, ws, wsb - 256, nullptr) == QGEMM_ERR_INVALID_ARG);
 }
 
 qgemm_job make_head(int M) {
@@ -279,6 +314,11 @@ int main(int argc, char** argv) {
   rng.seed(std::strtoull(argv[1], nullptr, 10));
   const long iters = std::strtol(argv[2], nullptr, 10);
   for (g_iter = 0; g_iter < iters; g_iter++) {
+    if (g_iter % 50 == 49) {
+      big_case();
+      free_all();
+      continue;
+    }
     switch (rnd(0, 5)) {
       case 0: case 1: sweep_case(); break;
       case 2: verify_case(); break;

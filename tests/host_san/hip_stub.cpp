@@ -21,7 +21,8 @@
 #include "qgemm.h"
 #include "qgemm_internal.h"
 
-long g_launches = 0;  // kernels run or recorded, for the fuzz driver
+long g_launches = 0;      // kernels run or recorded, for the fuzz driver
+long g_big_launches = 0;  // of which sweeps with the big step shape
 
 #define CHECK(c)                                                                    \
   do {                                                                              \
@@ -162,6 +163,7 @@ hipError_t launch_sweep(int kind, int cls, bool all, bool big, const SweepArgs& 
   (void)all;
   CHECK(kind >= 0 && kind <= 2);
   const SweepArgs a = args;  // by value, as a kernel argument
+  if (big) g_big_launches++;
   run_or_record(stream, [=] { sweep_footprint(kind, cls, big, a, grid); });
   return hipSuccess;
 }

@@ -3,7 +3,9 @@ UndefinedBehaviorSanitizer (CPU only).
 
 tests/host_san/ holds two randomized drivers:
   * fuzz_abi: the C boundary (sweeps of 1..40 jobs of every format and path,
-    the verify head, round replay, attention verify, pack) built from the
+    launches of more than 4 GiB of weights, which take the stream kernel's
+    big step shape, the verify head, round replay, attention verify, pack)
+    built from the
     library's own host sources, with the HIP runtime and the kernel launchers
     replaced by host stand-ins that touch every region each kernel would
     touch.  Valid calls get buffers and workspaces of exactly the documented
