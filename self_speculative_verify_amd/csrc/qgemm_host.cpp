@@ -17,8 +17,8 @@ namespace qg {
 hipError_t launch_pack(const float* W, int64_t ldw, int N, int K, int bits, void* packed,
                        unsigned* flag, hipStream_t stream);
 hipError_t launch_fill_zero(void* p, int64_t words, hipStream_t stream);
-int sweep_blocks_per_cu(int kind, int cls, bool all);
-hipError_t launch_sweep(int kind, int cls, bool all, bool big, const SweepArgs& args, int grid, hipStream_t stream);
+int sweep_blocks_per_cu(int kind, int cls, int fs, int rows);
+hipError_t launch_sweep(int kind, int cls, int fs, int rows, const SweepArgs& args, int grid, hipStream_t stream);
 hipError_t launch_accept(const AcceptArgs& a, unsigned long long* keys, const int32_t* drafts, int32_t* argmax,
                          float* maxval, int32_t* accepted, hipStream_t stream);
 }  // namespace qg
@@ -50,18 +50,21 @@ int path_of(int path, int M) {
   return path;
 }
 
-// y_optional: the verify head, whose Y may be null (no outputs written)
-// No job's Y overlaps any job's X, packed weights or another Y (reads may
+// A byte range [a, b) a call reads or writes.
+struct Span {
+  uintptr_t a, b;
+  bool write;
+};
+Span written(const void* p, size_t bytes) { return {(uintptr_t)p, (uintptr_t)p + bytes, true}; }
+
+// No buffer a call writes (each job's Y, and the `extra` spans: workspace,
+// verify outputs) overlaps any other buffer it reads or writes (reads may
 // share memory).  Intervals sorted by start; an interval overlaps an earlier
 // one iff that one ends after it starts, so it suffices to track the largest
 // end so far over all intervals and over the written ones.
-bool overlap_free(const qgemm_job* jobs, int njobs) {
-  struct Span {
-    uintptr_t a, b;
-    bool write;
-  };
-  std::vector<Span> v;
-  v.reserve((size_t)njobs * 3);
+bool overlap_free(const qgemm_job* jobs, int njobs, const std::vector<Span>& extra) {
+  std::vector<Span> v(extra);
+  v.reserve(extra.size() + (size_t)njobs * 3);
   for (int i = 0; i < njobs; i++) {
     const qgemm_job& j = jobs[i];
     const uintptr_t x0 = (uintptr_t)j.X, p0 = (uintptr_t)j.packed;
@@ -82,7 +85,10 @@ bool overlap_free(const qgemm_job* jobs, int njobs) {
   return true;
 }
 
-qgemm_status validate(const qgemm_job* jobs, int njobs, int path, bool y_optional = false) {
+// y_optional: the verify head, whose Y may be null (no outputs written);
+// extra: further buffers the call writes
+qgemm_status validate(const qgemm_job* jobs, int njobs, int path, bool y_optional = false,
+                      const std::vector<Span>& extra = {}) {
   if (njobs < 1 || jobs == nullptr) return QGEMM_ERR_INVALID_ARG;
   if (path != QGEMM_PATH_AUTO && path != QGEMM_PATH_GEMV && path != QGEMM_PATH_MFMA)
     return QGEMM_ERR_INVALID_ARG;
@@ -101,46 +107,45 @@ qgemm_status validate(const qgemm_job* jobs, int njobs, int path, bool y_optiona
     if (!aligned(j.Y, 16)) return QGEMM_ERR_INVALID_ARG;
     if (j.ldy < j.N || j.ldy % 4 != 0) return QGEMM_ERR_INVALID_ARG;
   }
-  return overlap_free(jobs, njobs) ? QGEMM_OK : QGEMM_ERR_INVALID_ARG;
+  return overlap_free(jobs, njobs, extra) ? QGEMM_OK : QGEMM_ERR_INVALID_ARG;
 }
 
 // ---------------------------------------------------------------------------
 // planning: jobs are grouped by kernel (kind, class); the workspace holds the
-// job tables of launches with many jobs, the stream kernels' arrival counters
-// and partial-sum slots (each region 256-byte aligned)
+// job tables of launches with many jobs and the stream kernels' partial-sum
+// slots (each region 256-byte aligned)
 // ---------------------------------------------------------------------------
 enum Kind { kStreamGemv = 0, kStreamMfma = 1, kGroupMfma = 2 };
 
 struct Launch {
   int kind;
   int cls;
-  bool all = false;           // some job uses a format beyond the 4/5-bit group-32 ones
+  int fs = 0;                 // formats of its jobs (bit 0: 4-bit, 1: 5-bit, 2: group-64, 3: zero-point)
   bool big = false;           // stream: at least kStreamBigBytes of weights
+  int rows = 4;               // stream: row blocks per step
   int64_t bytes = 0;          // weight bytes of its jobs
   std::vector<JobDesc> descs;
   int64_t total = 0;          // stream: flat units; group: row-block groups
-  int64_t rgs = 0;            // stream: row groups (arrival counters)
-  size_t table_off = 0, counters_off = 0, slots_off = 0;
+  size_t table_off = 0, slots_off = 0;
   int nwaves = 0;
   int bshift = 0;             // stream with a table: log2 of the units per bucket
   std::vector<int32_t> index; // stream with a table: uend per job, first job per bucket
 };
 
+int fmt_bit(int f) { return f == qg::kFmtQ4 ? 1 : f == qg::kFmtQ5 ? 2 : f == qg::kFmtG64 ? 4 : 8; }
+
 // Flat units and row-block groups are 32-bit in the kernels.
 constexpr int64_t kMaxSteps = ((int64_t)1 << 31) - 1;
 
-// Workspace of a plan: the job tables of its launches, then their arrival
-// counters, then their partial-sum slots (three regions, each a 256-byte
-// multiple).  A completed sweep leaves its counters at zero and its slots
-// holding stale sums, so sweeps that run one after another may share the
-// counter and slot regions as long as no counter ever lands on another
-// plan's slots or table: counters need a region of their own.
+// Workspace of a plan: the job tables of its launches, then the stream
+// kernels' partial-sum slots (two regions, each a 256-byte multiple).  Every
+// completed sweep leaves its slots at zero, so sweeps that run one after
+// another may share one slot region whatever their jobs.
 struct Plan {
   std::vector<Launch> launches;
   size_t table_bytes = 0;
-  size_t counter_bytes = 0;
   size_t slot_bytes = 0;
-  size_t total = 0;           // the three regions, at least 256
+  size_t total = 0;           // both regions, at least 256
   bool ok = true;             // false: a launch exceeds the 32-bit unit range
 };
 
@@ -199,12 +204,15 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* k
     P.launches[li].bytes += nrb_of(j.N) * nkt_of(j.K) * qg::tile_bytes(j.bits);
   }
   // the MFMA stream kernel has the eight-block step shape for big launches
-  for (auto& l : P.launches) l.big = l.bytes >= qg::kStreamBigBytes;
+  for (auto& l : P.launches) {
+    l.big = l.bytes >= qg::kStreamBigBytes;
+    l.rows = qg::stream_rows(l.big && l.kind == kStreamMfma);
+  }
   for (int i : order) {
     const qgemm_job& j = jobs[i];
     Launch* dst = &P.launches[dst_of[i]];
     const int kind = dst->kind, cls = dst->cls;
-    if (j.bits != qg::kFmtQ4 && j.bits != qg::kFmtQ5) dst->all = true;
+    dst->fs |= fmt_bit(j.bits);
     JobDesc d;
     std::memset(&d, 0, sizeof(d));
     d.packed = (const uint8_t*)j.packed;
@@ -227,17 +235,15 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* k
       dst->total += groups;
       d.grp_end = (int32_t)std::min(dst->total, kMaxSteps);
     } else {
-      const int R = qg::stream_rows(dst->big && kind == kStreamMfma);
+      const int R = dst->rows;
       d.nrg = (d.nrb + R - 1) / R;
       d.ubeg = (int32_t)std::min(dst->total, kMaxSteps);
       dst->total += (int64_t)d.nrg * d.nkt * qg::unit_weight(d.fmt);
       d.uend = (int32_t)std::min(dst->total, kMaxSteps);
-      d.rg_begin = (int32_t)dst->rgs;
-      dst->rgs += d.nrg;
     }
     dst->descs.push_back(d);
   }
-  size_t off = 0, coff = 0, soff = 0;
+  size_t off = 0, soff = 0;
   for (auto& l : P.launches) {
     if (l.total > kMaxSteps) {
       P.ok = false;
@@ -263,27 +269,23 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* k
     }
     if (l.kind != kGroupMfma) {
       l.nwaves = (int)stream_waves(l.total, l.big);
-      l.counters_off = coff;
-      coff = round_up(coff + (size_t)l.rgs * sizeof(int), 256);
       l.slots_off = soff;
-      const size_t slot_floats = (size_t)l.cls * qg::stream_rows(l.big && l.kind == kStreamMfma) * qg::kTileRows;
-      soff = round_up(soff + (size_t)2 * l.nwaves * slot_floats * sizeof(float), 256);
+      soff = round_up(soff + (size_t)qg::stream_slot_bytes(l.nwaves, l.rows, l.kind == kStreamMfma, l.cls), 256);
     }
   }
   P.table_bytes = off;
-  P.counter_bytes = coff;
   P.slot_bytes = soff;
-  P.total = std::max<size_t>(off + coff + soff, 256);
+  P.total = std::max<size_t>(off + soff, 256);
   return P;
 }
 
-int blocks_per_cu(int kind, int cls, bool all) {
+int blocks_per_cu(int kind, int cls, int fs, int rows) {
   static std::mutex mu;
-  static int cache[2][3][65] = {};
+  static int cache[16][2][3][65] = {};
   std::lock_guard<std::mutex> g(mu);
-  int& c = cache[all ? 1 : 0][kind][cls];
+  int& c = cache[fs & 15][rows == 8 ? 1 : 0][kind][cls];
   if (c == 0) {
-    c = qg::sweep_blocks_per_cu(kind, cls, all);
+    c = qg::sweep_blocks_per_cu(kind, cls, fs, rows);
     if (c <= 0) c = 1;
   }
   return c;
@@ -303,7 +305,7 @@ int cu_count() {
 
 qgemm_status run_plan(Plan& P, void* workspace, void* stream);
 qgemm_status upload_tables(const Plan& P, uint8_t* tables, hipStream_t s);
-qgemm_status launch_plan(const Plan& P, uint8_t* tables, uint8_t* counters, uint8_t* slots, hipStream_t s);
+qgemm_status launch_plan(const Plan& P, uint8_t* tables, uint8_t* slots, hipStream_t s);
 int grid_of(const Launch& l);
 
 }  // namespace
@@ -351,7 +353,7 @@ qgemm_status qgemm_workspace_init(void* workspace, size_t ws_bytes, void* stream
 
 qgemm_status qgemm_validate(const qgemm_job* jobs, int njobs, int path, void* workspace,
                             size_t ws_bytes) {
-  qgemm_status st = validate(jobs, njobs, path);
+  qgemm_status st = validate(jobs, njobs, path, false, {written(workspace, ws_bytes)});
   if (st != QGEMM_OK) return st;
   if (!workspace || !aligned(workspace, 256)) return QGEMM_ERR_INVALID_ARG;
   const Plan P = make_plan(jobs, njobs, path);
@@ -362,12 +364,9 @@ qgemm_status qgemm_validate(const qgemm_job* jobs, int njobs, int path, void* wo
 
 qgemm_status qgemm_sweep_path(const qgemm_job* jobs, int njobs, int path, void* workspace,
                               size_t ws_bytes, void* stream) {
-  qgemm_status st = validate(jobs, njobs, path);
+  qgemm_status st = qgemm_validate(jobs, njobs, path, workspace, ws_bytes);
   if (st != QGEMM_OK) return st;
-  if (!workspace || !aligned(workspace, 256)) return QGEMM_ERR_INVALID_ARG;
   Plan P = make_plan(jobs, njobs, path);
-  if (!P.ok) return QGEMM_ERR_UNSUPPORTED;
-  if (ws_bytes < P.total) return QGEMM_ERR_INVALID_ARG;
   return run_plan(P, workspace, stream);
 }
 
@@ -389,12 +388,20 @@ namespace {
 
 // Checks of a verify head call (host only) and the acceptance kernel's
 // arguments.
+// The outputs argmax [M], maxlogit [M] (optional) and accepted [nslots] and
+// the workspace are written spans: none may overlap another or the job's
+// buffers.
 qgemm_status head_args(const qgemm_job* head, const int32_t* drafts, const qgemm_slot* slots, int nslots,
-                       const int32_t* argmax, const int32_t* accepted, qg::AcceptArgs& a) {
-  qgemm_status st = validate(head, 1, QGEMM_PATH_AUTO, true);
-  if (st != QGEMM_OK) return st;
-  if (!argmax || !accepted) return QGEMM_ERR_INVALID_ARG;
+                       const int32_t* argmax, const float* maxlogit, const int32_t* accepted,
+                       const void* workspace, size_t ws_bytes, qg::AcceptArgs& a) {
+  if (!head || !argmax || !accepted) return QGEMM_ERR_INVALID_ARG;
   if (!slots || nslots < 1 || nslots > qg::kMaxSlots) return QGEMM_ERR_INVALID_ARG;
+  if (head->M < 1 || head->M > QGEMM_MAX_M) return QGEMM_ERR_INVALID_ARG;
+  std::vector<Span> outs = {written(argmax, (size_t)head->M * 4), written(accepted, (size_t)nslots * 4),
+                            written(workspace, ws_bytes)};
+  if (maxlogit) outs.push_back(written(maxlogit, (size_t)head->M * 4));
+  qgemm_status st = validate(head, 1, QGEMM_PATH_AUTO, true, outs);
+  if (st != QGEMM_OK) return st;
   std::memset(&a, 0, sizeof(a));
   a.nslots = nslots;
   a.M = head->M;
@@ -420,7 +427,7 @@ qgemm_status qgemm_verify_head(const qgemm_job* head, const int32_t* drafts, con
                                int32_t* argmax, float* maxlogit, int32_t* accepted, void* workspace,
                                size_t ws_bytes, void* stream) {
   qg::AcceptArgs a;
-  qgemm_status st = head_args(head, drafts, slots, nslots, argmax, accepted, a);
+  qgemm_status st = head_args(head, drafts, slots, nslots, argmax, maxlogit, accepted, workspace, ws_bytes, a);
   if (st != QGEMM_OK) return st;
   if (!workspace || !aligned(workspace, 256)) return QGEMM_ERR_INVALID_ARG;
   const Plan P0 = make_plan(head, 1, QGEMM_PATH_AUTO);
@@ -449,29 +456,31 @@ struct qgemm_round_s {
 namespace {
 
 // Plans of a round and its workspace layout: every sweep's tables one after
-// another, then one counter region and one slot region that all sweeps share
-// (they run in order; each region as large as the largest sweep's), then the
-// head's argmax keys.
+// another, then one slot region that all sweeps share (they run in order and
+// each leaves it at zero; as large as the largest sweep's), then the head's
+// argmax keys.
 struct RoundPlan {
   std::vector<Plan> sweeps;
   Plan head;
   bool has_head = false;
   std::vector<size_t> table_off;
-  size_t head_table_off = 0, counters_off = 0, slots_off = 0, keys_off = 0, total = 0;
+  size_t head_table_off = 0, slots_off = 0, keys_off = 0, total = 0;
 };
 
+// keys_base: the workspace (null when only sizing), ws_bytes its size; the
+// workspace may overlap no sweep's buffers
 qgemm_status round_plan(const qgemm_round_sweep* sweeps, int nsweeps, const qgemm_job* head, RoundPlan& R,
-                        unsigned long long* keys_base) {
+                        unsigned long long* keys_base, size_t ws_bytes = 0) {
+  const std::vector<Span> ws_span = keys_base ? std::vector<Span>{written(keys_base, ws_bytes)} : std::vector<Span>{};
   if (nsweeps < 0 || (nsweeps > 0 && !sweeps) || (nsweeps == 0 && !head)) return QGEMM_ERR_INVALID_ARG;
-  size_t tables = 0, counters = 0, slots = 0;
+  size_t tables = 0, slots = 0;
   for (int i = 0; i < nsweeps; i++) {
-    const qgemm_status st = validate(sweeps[i].jobs, sweeps[i].njobs, sweeps[i].path);
+    const qgemm_status st = validate(sweeps[i].jobs, sweeps[i].njobs, sweeps[i].path, false, ws_span);
     if (st != QGEMM_OK) return st;
     R.sweeps.push_back(make_plan(sweeps[i].jobs, sweeps[i].njobs, sweeps[i].path));
     if (!R.sweeps.back().ok) return QGEMM_ERR_UNSUPPORTED;
     R.table_off.push_back(tables);
     tables += R.sweeps.back().table_bytes;
-    counters = std::max(counters, R.sweeps.back().counter_bytes);
     slots = std::max(slots, R.sweeps.back().slot_bytes);
   }
   if (head) {
@@ -482,12 +491,10 @@ qgemm_status round_plan(const qgemm_round_sweep* sweeps, int nsweeps, const qgem
     R.head = make_plan(head, 1, QGEMM_PATH_AUTO);
     if (!R.head.ok) return QGEMM_ERR_UNSUPPORTED;
     tables += R.head.table_bytes;
-    counters = std::max(counters, R.head.counter_bytes);
     slots = std::max(slots, R.head.slot_bytes);
   }
-  R.counters_off = tables;
-  R.slots_off = tables + counters;
-  R.keys_off = round_up(tables + counters + slots, 256);
+  R.slots_off = tables;
+  R.keys_off = round_up(tables + slots, 256);
   R.total = std::max<size_t>(R.keys_off + (head ? kKeyBytes : 0), 256);
   if (head && keys_base) {
     // the head's jobs carry the key pointer
@@ -514,11 +521,12 @@ qgemm_status qgemm_round_create(const qgemm_round_sweep* sweeps, int nsweeps, co
   if (!workspace || !aligned(workspace, 256)) return QGEMM_ERR_INVALID_ARG;
   qg::AcceptArgs a;
   if (head) {
-    const qgemm_status st = head_args(head, drafts, slots, nslots, argmax, accepted, a);
+    const qgemm_status st = head_args(head, drafts, slots, nslots, argmax, maxlogit, accepted, workspace,
+                                      ws_bytes, a);
     if (st != QGEMM_OK) return st;
   }
   RoundPlan R;
-  qgemm_status st = round_plan(sweeps, nsweeps, head, R, (unsigned long long*)workspace);
+  qgemm_status st = round_plan(sweeps, nsweeps, head, R, (unsigned long long*)workspace, ws_bytes);
   if (st != QGEMM_OK) return st;
   if (ws_bytes < R.total) return QGEMM_ERR_INVALID_ARG;
   uint8_t* ws = (uint8_t*)workspace;
@@ -539,11 +547,11 @@ qgemm_status qgemm_round_create(const qgemm_round_sweep* sweeps, int nsweeps, co
   bool ok = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) == hipSuccess;
   bool capturing = ok;
   for (size_t i = 0; ok && i < R.sweeps.size(); i++) {
-    ok = launch_plan(R.sweeps[i], ws + R.table_off[i], ws + R.counters_off, ws + R.slots_off, cs) == QGEMM_OK;
+    ok = launch_plan(R.sweeps[i], ws + R.table_off[i], ws + R.slots_off, cs) == QGEMM_OK;
     r->kernels += (int)R.sweeps[i].launches.size();
   }
   if (ok && R.has_head) {
-    ok = launch_plan(R.head, ws + R.head_table_off, ws + R.counters_off, ws + R.slots_off, cs) == QGEMM_OK &&
+    ok = launch_plan(R.head, ws + R.head_table_off, ws + R.slots_off, cs) == QGEMM_OK &&
          qg::launch_accept(a, (unsigned long long*)(ws + R.keys_off), drafts, argmax, maxlogit, accepted, cs) ==
              hipSuccess;
     r->kernels += (int)R.head.launches.size() + 1;
@@ -582,7 +590,7 @@ qgemm_status run_plan(Plan& P, void* workspace, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const qgemm_status st = upload_tables(P, ws, s);
   if (st != QGEMM_OK) return st;
-  return launch_plan(P, ws, ws + P.table_bytes, ws + P.table_bytes + P.counter_bytes, s);
+  return launch_plan(P, ws, ws + P.table_bytes, s);
 }
 
 // One copy per launch with more than kMaxInline jobs: its job table, then
@@ -604,13 +612,13 @@ qgemm_status upload_tables(const Plan& P, uint8_t* tables, hipStream_t s) {
 // graph recording calls this for every launch before it starts).
 int grid_of(const Launch& l) {
   if (l.kind == kGroupMfma)
-    return (int)std::max<int64_t>(1, std::min<int64_t>(l.total, (int64_t)cu_count() * blocks_per_cu(l.kind, l.cls, l.all)));
+    return (int)std::max<int64_t>(1, std::min<int64_t>(l.total, (int64_t)cu_count() * blocks_per_cu(l.kind, l.cls, l.fs, l.rows)));
   return (l.nwaves + qg::kStreamWavesPerBlock - 1) / qg::kStreamWavesPerBlock;
 }
 
 // The kernels of a plan whose tables are in place: nothing but launches, so
 // it can be recorded into a graph.
-qgemm_status launch_plan(const Plan& P, uint8_t* tables, uint8_t* counters, uint8_t* slots, hipStream_t s) {
+qgemm_status launch_plan(const Plan& P, uint8_t* tables, uint8_t* slots, hipStream_t s) {
   for (const auto& l : P.launches) {
     qg::SweepArgs args;
     std::memset(&args, 0, sizeof(args));
@@ -627,14 +635,14 @@ qgemm_status launch_plan(const Plan& P, uint8_t* tables, uint8_t* counters, uint
       args.index = nullptr;
     }
     if (l.kind != kGroupMfma) {
-      args.counters = (int*)(counters + l.counters_off);
       args.slots = (float*)(slots + l.slots_off);
+      args.slot_bytes = qg::stream_slot_bytes(l.nwaves, l.rows, l.kind == kStreamMfma, l.cls);
+      args.spin_limit = qg::kSpinLimit;
       args.nwaves = l.nwaves;
       args.q = (int32_t)(l.total / l.nwaves);
       args.rem = (int32_t)(l.total % l.nwaves);
-      args.slot_rows = l.cls;
     }
-    if (qg::launch_sweep(l.kind, l.cls, l.all, l.big && l.kind == kStreamMfma, args, grid_of(l), s) != hipSuccess)
+    if (qg::launch_sweep(l.kind, l.cls, l.fs, l.rows, args, grid_of(l), s) != hipSuccess)
       return QGEMM_ERR_HIP;
   }
   return QGEMM_OK;

@@ -83,8 +83,7 @@ struct JobDesc {
   int32_t nkt;           // ceil(K / 128)
   int32_t ngroups;       // K / 32
   int32_t nrb;           // ceil(N / 16)
-  int32_t nrg;           // stream kernel: row groups, ceil(nrb / stream_rows(big))
-  int32_t rg_begin;      // stream kernel: first arrival counter of this job
+  int32_t nrg;           // stream kernel: row groups, ceil(nrb / rows per step)
   int32_t grp_begin;     // group kernel: first row-block group of this job
   int32_t grp_end;
 };
@@ -123,14 +122,25 @@ struct SweepArgs {
   int32_t nwaves;        // stream kernel: waves in the grid (fixes the K split)
   int32_t q, rem;        // stream kernel: wave w takes q units, one more if w < rem
   int32_t njobs;
-  int32_t slot_rows;     // stream kernel: rows m per slot (the class)
   int32_t bshift;        // stream kernel with a table: log2 of the units per bucket
+  int32_t spin_limit;    // stream kernel: polls a reader makes before it gives up on a slot
   int32_t pad_;
+  int64_t slot_bytes;    // stream kernel: bytes of the slot region
   const JobDesc* table;  // device copy of all jobs (when njobs > kMaxInline), else null
   const int32_t* index;  // with a table: uend of every job, then the first job of every bucket
-  int* counters;         // stream kernel: arrival counter per row group (zero between calls)
-  float* slots;          // stream kernel: two partial-sum slots per wave
+  float* slots;          // stream kernel: two partial-sum slots per wave (all zero between calls)
   JobDesc inl[kMaxInline];
 };
+
+// Stream kernel slots: per wave two slots (its head piece, its tail piece),
+// each 64 lanes x rows * acc floats; acc = accumulators per row block (MFMA:
+// ceil(class / 4), GEMV: class).
+inline __host__ __device__ constexpr int stream_acc(bool mfma, int cls) { return mfma ? (cls + 3) / 4 : cls; }
+inline __host__ __device__ constexpr int64_t stream_slot_bytes(int nwaves, int rows, bool mfma, int cls) {
+  return (int64_t)nwaves * 2 * 64 * rows * stream_acc(mfma, cls) * 4;
+}
+// a reader's polls of one slot before it gives up (the wait ends long before
+// in any sweep; the bound only guarantees that every wave exits)
+constexpr int kSpinLimit = 1 << 20;
 
 }  // namespace qg

@@ -1,0 +1,539 @@
+// gfx950 stream kernels of the quantized weight sweep: panels of at most 16
+// rows (GEMV, or MFMA with one m block).
+//
+// The method (Quasar/q27 wiki): decode streams every quantized linear weight
+// once per step ("decode physics" paragraph: decode is bound by weight reads)
+// and one weight read serves all draft positions of all slots (intro bullets
+// on the fused verify sweep).  These kernels are the decode-sized end of that
+// sweep: a single weight read per tile, the activation panel M <= 16 rows.
+//
+// Work is a flat sequence of steps (job, row group, k tile); a row group is
+// kR consecutive 16-row blocks, and one step reads the kR tiles of its row
+// group at one k tile.  Units of weight bytes (a step weighs its tile bytes /
+// 128) are cut into `nwaves` equal contiguous ranges, one per wave; a wave
+// owns the steps whose first unit lies in its range.  The cut depends on the
+// shapes only, so every output bit is the same for every M of a class.
+//
+// A row group whose steps fall into several ranges ("split") is summed
+// without counters or waits on the critical path:
+//   * its first contributor (the wave holding its first step) and every
+//     contributor after the second are writers: they store their partial
+//     sums into a slot of their own;
+//   * the second contributor is its reader: it adds the partials in wave
+//     order (k order) to its own, writes Y and clears the slots.
+// A wave processes the pieces it writes first and the piece it reads last, so
+// a reader normally finds every partial long written.  Slots hold the fp32
+// bits of the partials with +0 stored as -0; an all-zero word means "not yet
+// written" and a workspace of zeros is empty, which every completed sweep
+// leaves behind.  The reader polls (bounded) until every word of its
+// sources is non-zero.  Readers only ever wait for waves of lower index,
+// which are dispatched no later than themselves (look-back), and writers
+// wait for nothing, so the waits end.  Accumulators start at +0 and fp32
+// round-to-nearest never turns +0 into -0, so no partial is -0 itself; the
+// reader's sum with a stored -0 is bitwise the sum with +0.
+//
+// Per step the X chunk (class rows x 128 k: 16 bytes per lane and load, one
+// load for up to four rows) goes through a wave-private LDS buffer, from
+// which the MFMA A fragments (or the GEMV operands) are read: one global load
+// instruction per four panel rows and step instead of one per MFMA group.
+//
+// MFMA: v_mfma_f32_16x16x32_f16 with A = X (16 rows x 32 k of one group)
+// and B = codes (32 k x 16 rows n): lane l supplies A row l%16 and B column
+// n = l%16, both for k chunk l/16 -- exactly the lane's 16 code bytes -- and
+// holds D rows 4(l/16) + i of column n.  X row m is placed at A row
+// 4(m%4) + m/4, so it comes out in lane group g = m%4, accumulator i = m/4:
+// a panel of at most 4 kA rows keeps kA = ceil(class / 4) accumulators per
+// lane, and the group's scale multiplies only those.
+// GEMV: lane l = r + 16c forms, for row n = r and each m, four
+// v_dot2_f32_f16 over its 8 codes of a group, scaled by the group's scale;
+// the four k chunks of a row (lanes r, r+16, r+32, r+48) are summed when the
+// row group is written.
+// Padding groups (beyond K) have codes q = 0 and scale +0, and their X reads
+// are clamped into the row, so they add exact zeros: no tile needs a branch.
+#pragma once
+
+#include <utility>
+
+#include "sweep_device.h"
+
+namespace qg {
+
+// format sets of a launch (bit i: format class i present)
+constexpr int kSetQ4 = 1, kSetQ5 = 2, kSetG64 = 4, kSetZP = 8;
+
+template <bool kMfma, int kCap, int kR, int kFS>
+struct Stream {
+  static constexpr int kA = kMfma ? (kCap + 3) / 4 : kCap;      // accumulators per row block
+  static constexpr int kAcc = kR * kA;                         // partial-sum floats per lane
+  static constexpr int kXP = (kCap * 16 + 63) / 64;            // 16-byte X pieces per lane and step
+  static constexpr int kDepth = kR >= 8 ? 2 : 4;               // steps in flight
+  static constexpr bool kSide = (kFS & (kSetQ5 | kSetZP)) != 0;
+  static constexpr int kOnly = kFS == kSetQ4 ? kFmtQ4 : kFS == kSetQ5 ? kFmtQ5 : kFS == kSetG64 ? kFmtG64
+                               : kFS == kSetZP ? kFmtZP : 0;   // the one format, or 0
+
+  struct Step {
+    u4_t c[kR];
+    u2_t s[kR];
+    uint32_t h[kSide ? kR : 1];
+    u4_t x[kXP];
+  };
+
+  using Phases = StreamPhases;
+  using Pos = StreamPos;
+
+  // ---------------------------------------------------------------- loads
+  // kR weight tiles (non-temporal: streamed once), their scales and side
+  // words, and the X chunk of k tile kt: lane l, piece p holds X[row][k0 +
+  // 8 col ..] for row = 4p + l/16 (rows past M read row M-1) and col = l%16;
+  // k is clamped into the row (padding groups multiply it by zero codes).
+  template <int F>
+  static __device__ __forceinline__ void load_tiles(Step& t, const uint8_t* wp, const uint32_t (&roff)[kR],
+                                                    bool spill, int lane) {
+#pragma unroll
+    for (int r = 0; r < kR; r++) {
+      const uint8_t* tp = wp + (spill ? 0u : roff[r]);
+      t.c[r] = __builtin_nontemporal_load(gload_ptr<u4_t>(tp + 16 * lane));
+      if constexpr (F == kFmtG64) {
+        t.s[r].x = __builtin_nontemporal_load(gload_ptr<uint32_t>(tp + kScaleOff + 4 * (lane & 15)));
+        t.s[r].y = 0u;
+      } else {
+        t.s[r] = __builtin_nontemporal_load(gload_ptr<u2_t>(tp + kScaleOff + 8 * (lane & 15)));
+      }
+      if constexpr (kSide) {
+        if constexpr (F == kFmtQ5) t.h[r] = __builtin_nontemporal_load(gload_ptr<uint32_t>(tp + kHiOff + 4 * lane));
+        else if constexpr (F == kFmtZP)
+          t.h[r] = __builtin_nontemporal_load(gload_ptr<uint16_t>(tp + kZeroOff + 2 * (lane & 15)));
+        else t.h[r] = 0u;
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void load_x(Step& t, const JobDesc& d, int kt, int lane) {
+    const uint8_t* xb = (const uint8_t*)d.X;
+    const int col = lane & 15;
+    int k = kt * kTileK + 8 * col;
+    k = k < d.K - 8 ? k : d.K - 8;
+#pragma unroll
+    for (int p = 0; p < kXP; p++) {
+      const int row = 4 * p + (lane >> 4);
+      const int m = row < d.M ? row : d.M - 1;
+      t.x[p] = *gload_ptr<u4_t>(xb + 2 * ((int64_t)m * d.ldx + k));
+    }
+  }
+
+  // Loads of the step at c.  Past the wave's last step (spill != null) the
+  // same loads (so the wait counts stay exact) go to `spill`: the X panel of
+  // the cursor's job when it holds at least a 5-bit tile's bytes (every wave
+  // reads X, so it stays cached), else that job's first tile, read in the
+  // job's own format.  Tile r of the step sits roff[r] bytes after tile
+  // (rg * kR, kt); blocks past the job's last re-read its last one (their
+  // sums are never stored).
+  static __device__ __forceinline__ void load(Step& t, const Pos& c, const QG_CONST JobDesc* D,
+                                              const uint8_t* spill, int lane) {
+    const int tb = tile_bytes(kOnly ? kOnly : c.fmt);
+    const uint32_t rstride = (uint32_t)(c.nkt * tb);
+    const int left = c.nrb - 1 - c.rg * kR;
+    uint32_t roff[kR];
+#pragma unroll
+    for (int r = 0; r < kR; r++) roff[r] = (uint32_t)(r < left ? r : left) * rstride;
+    const uint8_t* wp = spill ? spill : c.packed + ((int64_t)c.rg * kR * c.nkt + c.kt) * tb;
+    const bool sp = spill != nullptr;
+    if constexpr (kOnly) {
+      load_tiles<kOnly>(t, wp, roff, sp, lane);
+    } else {
+      if ((kFS & kSetQ4) && c.fmt == kFmtQ4) load_tiles<kFmtQ4>(t, wp, roff, sp, lane);
+      else if ((kFS & kSetQ5) && c.fmt == kFmtQ5) load_tiles<kFmtQ5>(t, wp, roff, sp, lane);
+      else if ((kFS & kSetG64) && c.fmt == kFmtG64) load_tiles<kFmtG64>(t, wp, roff, sp, lane);
+      else load_tiles<kFmtZP>(t, wp, roff, sp, lane);
+    }
+    load_x(t, D[c.j], c.kt, lane);
+  }
+
+  static __device__ __forceinline__ const uint8_t* spill_of(const JobDesc& d) {
+    return 2 * ((int64_t)(d.M - 1) * d.ldx + d.K) >= kTile5 ? (const uint8_t*)d.X : d.packed;
+  }
+
+  // -------------------------------------------------------------- compute
+  // The step's X chunk into the wave's LDS buffer (rows < class), then the
+  // contraction of its kR tiles.
+  static __device__ __forceinline__ void stage_x(const Step& t, uint8_t* xs, int lane) {
+#pragma unroll
+    for (int p = 0; p < kXP; p++) {
+      const int row = 4 * p + (lane >> 4);
+      if (row < kCap) *(u4_t*)(xs + row * kXRowBytes + 16 * (lane & 15)) = t.x[p];
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // LDS writes stay before the reads
+  }
+
+  template <int F>
+  static __device__ __forceinline__ void compute(float (&acc)[kR][kA], const Step& t, const uint8_t* xs,
+                                                 int lane) {
+    if constexpr (kMfma) {
+      const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+      // A row ar = l % 16 carries X row (ar / 4) + 4 (ar % 4); rows past the
+      // class read the last one (their outputs are never stored)
+      const int ar = lane & 15, c = lane >> 4;
+      int mr = (ar >> 2) + 4 * (ar & 3);
+      mr = mr < kCap ? mr : kCap - 1;
+      h8_t a[4];
+#pragma unroll
+      for (int j = 0; j < 4; j++) a[j] = lds_h8(xs + mr * kXRowBytes + 64 * j + 16 * c);
+#pragma unroll
+      for (int r = 0; r < kR; r++) {
+        const uint32_t side = side_word<F>(t.h[kSide ? r : 0]);
+        f4_t p[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const h8_t q = unpack_chunk<F>(t.c[r][j], side, j);
+          // group 64: the second half of a group accumulates onto the first
+          const f4_t c0 = (F == kFmtG64 && (j & 1)) ? p[j ^ 1] : zero;
+          p[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], q, c0, 0, 0, 0);
+        }
+        const h2_t s01 = scale_pair(t.s[r].x), s23 = scale_pair(t.s[r].y);
+        const _Float16 sh[4] = {s01.x, s01.y, s23.x, s23.y};
+        if constexpr (F == kFmtG64) {
+#pragma unroll
+          for (int h = 0; h < 2; h++)
+#pragma unroll
+            for (int i = 0; i < kA; i++) acc[r][i] = __builtin_fmaf((float)sh[h], p[2 * h + 1][i], acc[r][i]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int i = 0; i < kA; i++) acc[r][i] = __builtin_fmaf((float)sh[j], p[j][i], acc[r][i]);
+        }
+      }
+    } else {
+      const int c = lane >> 4;
+#pragma unroll
+      for (int r = 0; r < kR; r++) {
+        const h2_t s01 = scale_pair(t.s[r].x), s23 = scale_pair(t.s[r].y);
+        const _Float16 sh[4] = {s01.x, s01.y, s23.x, s23.y};
+        const uint32_t side = side_word<F>(t.h[kSide ? r : 0]);
+        float dp[kCap];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          h2_t q[4];
+          unpack8<F>(t.c[r][j], side, j, q);
+          // group 64: the dot products of both halves, then one scale
+          const float sj = (float)sh[F == kFmtG64 ? j >> 1 : j];
+          const bool first = F != kFmtG64 || !(j & 1), last = F != kFmtG64 || (j & 1);
+#pragma unroll
+          for (int m = 0; m < kCap; m++) {
+            const h8_t x = lds_h8(xs + m * kXRowBytes + 64 * j + 16 * c);
+            const h2_t x0 = {x[0], x[1]}, x1 = {x[2], x[3]}, x2 = {x[4], x[5]}, x3 = {x[6], x[7]};
+            float d = __builtin_amdgcn_fdot2(q[0], x0, first ? 0.f : dp[m], false);
+            d = __builtin_amdgcn_fdot2(q[1], x1, d, false);
+            d = __builtin_amdgcn_fdot2(q[2], x2, d, false);
+            d = __builtin_amdgcn_fdot2(q[3], x3, d, false);
+            dp[m] = d;
+            if (last) acc[r][m] = __builtin_fmaf(sj, d, acc[r][m]);
+          }
+        }
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void compute_any(float (&acc)[kR][kA], const Step& t, int fmt,
+                                                     uint8_t* xs, int lane) {
+    stage_x(t, xs, lane);
+    if constexpr (kOnly) {
+      compute<kOnly>(acc, t, xs, lane);
+    } else {
+      if ((kFS & kSetQ4) && fmt == kFmtQ4) compute<kFmtQ4>(acc, t, xs, lane);
+      else if ((kFS & kSetQ5) && fmt == kFmtQ5) compute<kFmtQ5>(acc, t, xs, lane);
+      else if ((kFS & kSetG64) && fmt == kFmtG64) compute<kFmtG64>(acc, t, xs, lane);
+      else compute<kFmtZP>(acc, t, xs, lane);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the next step's LDS writes stay after these reads
+  }
+
+  static __device__ __forceinline__ void zero(float (&acc)[kR][kA]) {
+#pragma unroll
+    for (int r = 0; r < kR; r++)
+#pragma unroll
+      for (int i = 0; i < kA; i++) acc[r][i] = 0.f;
+  }
+
+  // ------------------------------------------------------------- epilogue
+  struct Ctx {
+    const QG_CONST JobDesc* D;
+    float* slots;
+    uint32_t slot_bytes;      // bytes of the slot region
+    int q, rem;               // partition of the units over the waves
+    int gw, lane;
+    int spin_limit;
+    // verify head: best argmax key of this lane's rows over the columns it
+    // finished (accumulator i's row), published at the end of the range
+    unsigned long long best[kA];
+  };
+
+  // slot (wave w, kind k) of the lane: kAcc floats at this byte offset
+  static __device__ __forceinline__ uint32_t slot_off(int w, int k, int lane) {
+    return (uint32_t)(((w * 2 + k) * 64 + lane) * kAcc) * 4u;
+  }
+  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const Ctx& cx) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)cx.slots, (short)0, (int)cx.slot_bytes, kBufWord3);
+  }
+
+  // Lanes' row m of accumulator i (MFMA), or m = i (GEMV)
+  static __device__ __forceinline__ int row_of(int lane, int i) { return kMfma ? (lane >> 4) + 4 * i : i; }
+
+  // GEMV: the four k chunks of each row summed across lanes (lanes < 16 hold
+  // the totals)
+  static __device__ __forceinline__ void lanes_sum(float (&acc)[kR][kA]) {
+    if constexpr (!kMfma) {
+#pragma unroll
+      for (int r = 0; r < kR; r++)
+#pragma unroll
+        for (int m = 0; m < kA; m++) {
+          float v = acc[r][m];
+          v += __shfl_xor(v, 16);
+          v += __shfl_xor(v, 32);
+          acc[r][m] = v;
+        }
+    }
+  }
+
+  // Final sums of row group rg of job j to Y (and the argmax keys).
+  static __device__ __forceinline__ void store_y(float (&acc)[kR][kA], Ctx& cx, int j, int rg) {
+    const QG_CONST JobDesc* D = cx.D;
+    const int lane = cx.lane;
+    lanes_sum(acc);
+    const int M = D[j].M, N = D[j].N;
+    const int64_t ldy = D[j].ldy;
+    QG_GLOBAL float* Y = (QG_GLOBAL float*)D[j].Y;
+    const bool keys = D[j].keys != nullptr;
+    const bool holder = kMfma || lane < 16;
+#pragma unroll
+    for (int r = 0; r < kR; r++) {
+      const int n = (rg * kR + r) * kTileRows + (lane & 15);
+      if (holder && n < N) {
+#pragma unroll
+        for (int i = 0; i < kA; i++) {
+          const int m = row_of(lane, i);
+          if (m < M) {
+            if (Y) Y[(int64_t)m * ldy + n] = acc[r][i];
+            if (keys) cx.best[i] = umax64(cx.best[i], logit_key(acc[r][i], n));
+          }
+        }
+      }
+    }
+  }
+
+  // Writer: this lane's partials, +0 stored as -0, into slot (gw, k).
+  static __device__ __forceinline__ void store_partial(const float (&acc)[kR][kA], const Ctx& cx, int k) {
+    const __amdgpu_buffer_rsrc_t sr = slot_rsrc(cx);
+    const uint32_t o = slot_off(cx.gw, k, cx.lane);
+    uint32_t w[kAcc];
+#pragma unroll
+    for (int r = 0; r < kR; r++)
+#pragma unroll
+      for (int i = 0; i < kA; i++) {
+        const uint32_t b = __builtin_bit_cast(uint32_t, acc[r][i]);
+        w[r * kA + i] = b ? b : 0x80000000u;
+      }
+    if constexpr (kAcc % 4 == 0) {
+#pragma unroll
+      for (int e = 0; e < kAcc; e += 4)
+        __builtin_amdgcn_raw_buffer_store_b128(u4_t{w[e], w[e + 1], w[e + 2], w[e + 3]}, sr, o + 4u * e, 0,
+                                               kCoherent);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kAcc; e += 2)
+        __builtin_amdgcn_raw_buffer_store_b64(u2_t{w[e], w[e + 1]}, sr, o + 4u * e, 0, kCoherent);
+    }
+  }
+
+  // Reader: the partial of slot (w, k) once every word of it is written
+  // (bounded wait; on timeout the words read are used as they are), then
+  // the slot cleared for the next sweep.
+  static __device__ __forceinline__ void take_partial(uint32_t (&w)[kAcc], const Ctx& cx, int wsrc, int k) {
+    const __amdgpu_buffer_rsrc_t sr = slot_rsrc(cx);
+    const uint32_t o = slot_off(wsrc, k, cx.lane);
+    for (int spin = 0;; spin++) {
+      bool ready = true;
+      if constexpr (kAcc % 4 == 0) {
+#pragma unroll
+        for (int e = 0; e < kAcc; e += 4) {
+          const u4_t v = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(sr, o + 4u * e, 0, kCoherent));
+          w[e] = v.x;
+          w[e + 1] = v.y;
+          w[e + 2] = v.z;
+          w[e + 3] = v.w;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < kAcc; e += 2) {
+          const u2_t v = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(sr, o + 4u * e, 0, kCoherent));
+          w[e] = v.x;
+          w[e + 1] = v.y;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < kAcc; e++) ready = ready && w[e] != 0u;
+      if (__builtin_amdgcn_read_exec() == __ballot(ready) || spin >= cx.spin_limit) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if constexpr (kAcc % 4 == 0) {
+#pragma unroll
+      for (int e = 0; e < kAcc; e += 4)
+        __builtin_amdgcn_raw_buffer_store_b128(u4_t{0u, 0u, 0u, 0u}, sr, o + 4u * e, 0, kCoherent);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kAcc; e += 2)
+        __builtin_amdgcn_raw_buffer_store_b64(u2_t{0u, 0u}, sr, o + 4u * e, 0, kCoherent);
+    }
+  }
+
+  // Reader of row group rg of job j: partials of its contributors wf .. wl
+  // in wave order with its own (wave wf + 1) in second place, then Y.
+  static __device__ __forceinline__ void read_split(float (&acc)[kR][kA], Ctx& cx, int j, int rg) {
+    int wf, wl;
+    stream_contributors(cx.q, cx.rem, cx.D, j, rg, wf, wl);
+    uint32_t w[kAcc];
+    take_partial(w, cx, wf, 1);
+#pragma unroll
+    for (int r = 0; r < kR; r++)
+#pragma unroll
+      for (int i = 0; i < kA; i++) acc[r][i] = __builtin_bit_cast(float, w[r * kA + i]) + acc[r][i];
+    for (int src = wf + 2; src <= wl; src++) {
+      take_partial(w, cx, src, 0);
+#pragma unroll
+      for (int r = 0; r < kR; r++)
+#pragma unroll
+        for (int i = 0; i < kA; i++) acc[r][i] += __builtin_bit_cast(float, w[r * kA + i]);
+    }
+    store_y(acc, cx, j, rg);
+  }
+
+  // Verify head: the range's best key per row, over the 16 lanes holding the
+  // row's columns, into the job's keys (one atomic per row and wave).
+  static __device__ __forceinline__ void publish(Ctx& cx, unsigned long long* keys, int M) {
+    const int lane = cx.lane;
+#pragma unroll
+    for (int i = 0; i < kA; i++) {
+      const unsigned long long k = lanes_max<1, 16>(cx.best[i]);
+      const int m = row_of(lane, i);
+      if ((lane & 15) == 0 && (kMfma || lane == 0) && m < M && k != 0ull) key_max(keys + m, k);
+      cx.best[i] = 0ull;
+    }
+  }
+
+  // ----------------------------------------------------------------- main
+  template <typename F, int... P>
+  static __device__ __forceinline__ void each_slot(F& f, std::integer_sequence<int, P...>) {
+    (f(std::integral_constant<int, P>{}), ...);
+  }
+
+  // Inlined into the kernel on purpose: the job table pointer below is the
+  // address of the kernel argument in the constant (kernarg) address space,
+  // which a by-reference copy on the stack would not be.
+  static __device__ __forceinline__ void run(const SweepArgs& args, uint8_t* xs) {
+    Ctx cx;
+    const QG_CONST JobDesc* D = job_table(args);
+    cx.D = D;
+    cx.slots = args.slots;
+    cx.slot_bytes = (uint32_t)args.slot_bytes;
+    cx.q = args.q;
+    cx.rem = args.rem;
+    cx.spin_limit = args.spin_limit;
+    cx.lane = threadIdx.x & 63;
+    const int lane = cx.lane;
+    // wave-uniform by construction; readfirstlane lets the compiler know it
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    cx.gw = (int)blockIdx.x * kStreamWavesPerBlock + wave;
+    if (cx.gw >= args.nwaves) return;
+#pragma unroll
+    for (int i = 0; i < kA; i++) cx.best[i] = 0ull;
+    const int a = stream_start_of(cx.gw, cx.q, cx.rem);
+    const int b = a + cx.q + (cx.gw < cx.rem ? 1 : 0);
+    Phases P;
+    stream_plan(P, args, D, cx.gw, a, b);
+
+    Pos pc, cc;
+    stream_start(pc, D, P);
+    cc = pc;
+    const int njobs = args.njobs;
+    const uint8_t* spill = nullptr;
+    Step buf[kDepth];
+#pragma unroll
+    for (int p = 0; p < kDepth; p++) {
+      load(buf[p], pc, D, spill, lane);
+      if (!spill) {
+        stream_advance(pc, D, P, njobs);
+        if (pc.ph == 4) {
+          if (pc.j >= njobs) stream_load_job(pc, D, njobs - 1);
+          spill = spill_of(D[pc.j]);
+        }
+      }
+    }
+    float acc[kR][kA];
+    zero(acc);
+    bool done = false;
+    // one pipeline slot: consume buffer p (while steps are left), then refill
+    // it kDepth steps ahead; p is a constant in every instance, so the
+    // buffers stay in registers
+    auto slot = [&](auto pc_) {
+      constexpr int p = decltype(pc_)::value;
+      if (!done) {
+        compute_any(acc, buf[p], cc.fmt, xs, lane);
+        const int j = cc.j, rg = cc.rg, ph = cc.ph;
+        const bool rg_end = cc.kt == cc.nkt - 1;
+        stream_advance(cc, D, P, njobs);
+        if (rg_end || cc.ph != ph) {
+          if (ph == 2) store_y(acc, cx, j, rg);
+          else if (ph == 3) read_split(acc, cx, j, rg);
+          else store_partial(acc, cx, ph == 0 ? 1 : 0);
+          zero(acc);
+        }
+        done = cc.ph == 4;
+      }
+      load(buf[p], pc, D, spill, lane);
+      if (!spill) {
+        stream_advance(pc, D, P, njobs);
+        if (pc.ph == 4) {
+          if (pc.j >= njobs) stream_load_job(pc, D, njobs - 1);
+          spill = spill_of(D[pc.j]);
+        }
+      }
+    };
+    while (!done) each_slot(slot, std::make_integer_sequence<int, kDepth>{});
+    const QG_CONST JobDesc& dk = D[0];
+    if (dk.keys) publish(cx, dk.keys + (cx.gw % kKeyCopies) * kKeyRows, dk.M);
+  }
+};
+
+template <bool kMfma, int kCap, int kR, int kFS>
+__global__ void __launch_bounds__(64 * kStreamWavesPerBlock) stream_kernel(SweepArgs args) {
+  using S = Stream<kMfma, kCap, kR, kFS>;
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kStreamWavesPerBlock][kCap * kXRowBytes];
+  S::run(args, xs[threadIdx.x >> 6]);
+}
+
+typedef void (*sweep_fn)(SweepArgs);
+
+template <bool kMfma, int kR, int kFS>
+static sweep_fn pick_cls(int cls) {
+  switch (cls) {
+    case 1: return stream_kernel<kMfma, 1, kR, kFS>;
+    case 2: return stream_kernel<kMfma, 2, kR, kFS>;
+    case 4: return stream_kernel<kMfma, 4, kR, kFS>;
+    case 8: return stream_kernel<kMfma, 8, kR, kFS>;
+  }
+  if constexpr (kMfma)
+    if (cls == 16) return stream_kernel<kMfma, 16, kR, kFS>;
+  return nullptr;
+}
+
+// The stream kernels of one format set: GEMV (four row blocks per step) and
+// MFMA (four or eight).
+template <int kFS>
+static sweep_fn pick_set(bool mfma, int cls, int rows) {
+  if (!mfma) return rows == 4 ? pick_cls<false, 4, kFS>(cls) : nullptr;
+  if (rows == 8) return pick_cls<true, 8, kFS>(cls);
+  if (rows == 4) return pick_cls<true, 4, kFS>(cls);
+  return nullptr;
+}
+
+}  // namespace qg

@@ -14,12 +14,14 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <functional>
 #include <vector>
 
 #include "attn_internal.h"
 #include "qgemm.h"
 #include "qgemm_internal.h"
+#include "stream_plan.h"
 
 long g_launches = 0;      // kernels run or recorded, for the fuzz driver
 long g_big_launches = 0;  // of which sweeps with the big step shape
@@ -67,8 +69,84 @@ void run_or_record(hipStream_t s, std::function<void()> f) {
 
 int64_t tiles_bytes(const qg::JobDesc& d) { return (int64_t)d.nrb * d.nkt * qg::tile_bytes(d.fmt); }
 
+// Every wave of a stream launch through the kernels' own planning code
+// (stream_plan.h): each step is taken by exactly one wave, each row group's
+// sums reach Y exactly once -- directly when one wave holds all its steps,
+// else by its second contributor, which reads the partials of all other
+// contributors (slot 1 of the first, slot 0 of the later ones), each written
+// exactly once -- and no wave writes a slot twice.
+void stream_schedule_check(const qg::SweepArgs& a, const std::vector<qg::JobDesc>& D) {
+  std::vector<int64_t> first(a.njobs + 1, 0);
+  for (int j = 0; j < a.njobs; j++) first[j + 1] = first[j] + (int64_t)D[j].nrg * D[j].nkt;
+  std::vector<uint8_t> taken((size_t)first[a.njobs], 0);
+  // per row group: [Y writes, reads, reader wave]; per (wave, slot): row group written
+  std::vector<int64_t> rgbase(a.njobs + 1, 0);
+  for (int j = 0; j < a.njobs; j++) rgbase[j + 1] = rgbase[j] + D[j].nrg;
+  std::vector<int> ywrites((size_t)rgbase[a.njobs], 0), reader((size_t)rgbase[a.njobs], -1);
+  std::vector<int64_t> slot_rg((size_t)a.nwaves * 2, -1);
+  for (int w = 0; w < a.nwaves; w++) {
+    const int u0 = qg::stream_start_of(w, a.q, a.rem), u1 = u0 + a.q + (w < a.rem ? 1 : 0);
+    qg::StreamPhases P;
+    qg::stream_plan(P, a, D.data(), w, u0, u1);
+    CHECK((P.mask & 15) != 0);
+    qg::StreamPos c;
+    qg::stream_start(c, D.data(), P);
+    int steps = 0;
+    while (c.ph < 4) {
+      CHECK(c.j >= 0 && c.j < a.njobs && c.rg >= 0 && c.rg < D[c.j].nrg && c.kt >= 0 && c.kt < D[c.j].nkt);
+      const qg::JobDesc& d = D[c.j];
+      const int64_t s = (int64_t)c.rg * d.nkt + c.kt;
+      // the step's first unit lies in the wave's range
+      const int64_t fu = d.ubeg + s * qg::unit_weight(d.fmt);
+      CHECK(fu >= u0 && fu < u1);
+      CHECK(taken[first[c.j] + s]++ == 0);
+      steps++;
+      const int j = c.j, rg = c.rg, ph = c.ph;
+      const bool rg_end = c.kt == d.nkt - 1;
+      qg::stream_advance(c, D.data(), P, a.njobs);
+      if (rg_end || c.ph != ph) {
+        const int64_t r = rgbase[j] + rg;
+        if (ph == 2) {
+          ywrites[r]++;
+        } else if (ph == 3) {
+          ywrites[r]++;
+          CHECK(reader[r] == -1);
+          reader[r] = w;
+        } else {
+          const int slot = ph == 0 ? 1 : 0;
+          CHECK(slot_rg[2 * w + slot] == -1);
+          slot_rg[2 * w + slot] = r;
+        }
+      }
+    }
+    CHECK(steps >= 1);
+  }
+  for (size_t i = 0; i < taken.size(); i++) CHECK(taken[i] == 1);
+  std::vector<int> reads(a.nwaves * 2, 0);
+  for (int j = 0; j < a.njobs; j++)
+    for (int rg = 0; rg < D[j].nrg; rg++) {
+      const int64_t r = rgbase[j] + rg;
+      CHECK(ywrites[r] == 1);
+      int wf, wl;
+      qg::stream_contributors(a.q, a.rem, D.data(), j, rg, wf, wl);
+      if (wf == wl) {
+        CHECK(reader[r] == -1);
+        continue;
+      }
+      CHECK(reader[r] == wf + 1);
+      CHECK(slot_rg[2 * wf + 1] == r);
+      reads[2 * wf + 1]++;
+      for (int src = wf + 2; src <= wl; src++) {
+        CHECK(slot_rg[2 * src] == r);
+        reads[2 * src]++;
+      }
+    }
+  // every written slot is read exactly once (and so left empty)
+  for (int i = 0; i < a.nwaves * 2; i++) CHECK((slot_rg[i] >= 0) == (reads[i] == 1) && reads[i] <= 1);
+}
+
 // What one sweep launch touches, from its arguments alone.
-void sweep_footprint(int kind, int cls, bool big, const qg::SweepArgs a, int grid) {
+void sweep_footprint(int kind, int cls, int fs, int rows, const qg::SweepArgs a, int grid) {
   CHECK(a.njobs >= 1 && a.total >= 1 && grid >= 1);
   std::vector<qg::JobDesc> D(a.njobs);
   if (a.table) {
@@ -80,13 +158,14 @@ void sweep_footprint(int kind, int cls, bool big, const qg::SweepArgs a, int gri
     for (int j = 0; j < a.njobs; j++) D[j] = a.inl[j];
   }
   const bool stream = kind != 2;
-  CHECK(!big || kind == 1);
-  const int R = qg::stream_rows(big);
-  int64_t rgs = 0;
+  CHECK(rows == 4 || (rows == 8 && kind == 1));
+  const int R = rows;
+  int seen = 0;
   for (int j = 0; j < a.njobs; j++) {
     const qg::JobDesc& d = D[j];
     CHECK(qg::valid_fmt(d.fmt) && d.M >= 1 && d.M <= QGEMM_MAX_M && d.N >= 1 && d.K >= 32);
     CHECK(d.nkt == (d.K + qg::kTileK - 1) / qg::kTileK && d.nrb == (d.N + qg::kTileRows - 1) / qg::kTileRows);
+    seen |= d.fmt == qg::kFmtQ4 ? 1 : d.fmt == qg::kFmtQ5 ? 2 : d.fmt == qg::kFmtG64 ? 4 : 8;
     span_r(d.packed, (size_t)tiles_bytes(d));
     span_r(d.X, (size_t)((int64_t)(d.M - 1) * d.ldx + d.K) * 2);
     if (d.Y) span_w(d.Y, (size_t)((int64_t)(d.M - 1) * d.ldy + d.N) * 4);
@@ -97,8 +176,6 @@ void sweep_footprint(int kind, int cls, bool big, const qg::SweepArgs a, int gri
       CHECK(d.ubeg == (j == 0 ? 0 : D[j - 1].uend));
       CHECK(d.uend - d.ubeg == (int64_t)d.nrg * d.nkt * qg::unit_weight(d.fmt));
       CHECK(d.nrg == (d.nrb + R - 1) / R);
-      CHECK(d.rg_begin == rgs);
-      rgs += d.nrg;
     } else {
       CHECK(d.M <= cls && cls >= 17 && cls <= 64);
       CHECK(d.grp_begin == (j == 0 ? 0 : D[j - 1].grp_end));
@@ -106,14 +183,15 @@ void sweep_footprint(int kind, int cls, bool big, const qg::SweepArgs a, int gri
       CHECK(d.grp_end - d.grp_begin == (d.nrb + per - 1) / per);
     }
   }
+  CHECK(seen == fs);
   if (stream) {
     CHECK(D[a.njobs - 1].uend == a.total);
     CHECK(a.nwaves >= 1 && (int64_t)grid * qg::kStreamWavesPerBlock >= a.nwaves);
     CHECK(a.q == a.total / a.nwaves && a.rem == a.total % a.nwaves);
     CHECK(a.q >= qg::kMaxUnitWeight || a.nwaves == 1);  // every wave holds at least one step
-    CHECK(a.slot_rows == cls);
-    span_w(a.counters, (size_t)rgs * sizeof(int));
-    span_w(a.slots, (size_t)2 * a.nwaves * a.slot_rows * R * qg::kTileRows * sizeof(float));
+    CHECK(a.spin_limit > 0);
+    CHECK(a.slot_bytes == qg::stream_slot_bytes(a.nwaves, R, kind == 1, cls));
+    span_w(a.slots, (size_t)a.slot_bytes);
     if (a.index) {
       // uend of every job, then the job holding the first unit of each bucket
       const int64_t nb = ((int64_t)a.total >> a.bshift) + 1;
@@ -125,6 +203,7 @@ void sweep_footprint(int kind, int cls, bool big, const qg::SweepArgs a, int gri
         CHECK(j >= 0 && j < a.njobs && D[j].ubeg <= f && f < D[j].uend);
       }
     }
+    stream_schedule_check(a, D);
   } else {
     CHECK(D[a.njobs - 1].grp_end == a.total);
     CHECK(a.table == nullptr || a.index == nullptr);
@@ -158,13 +237,12 @@ hipError_t launch_fill_zero(void* p, int64_t words, hipStream_t stream) {
   return hipSuccess;
 }
 
-hipError_t launch_sweep(int kind, int cls, bool all, bool big, const SweepArgs& args, int grid,
+hipError_t launch_sweep(int kind, int cls, int fs, int rows, const SweepArgs& args, int grid,
                         hipStream_t stream) {
-  (void)all;
-  CHECK(kind >= 0 && kind <= 2);
+  CHECK(kind >= 0 && kind <= 2 && fs >= 1 && fs <= 15);
   const SweepArgs a = args;  // by value, as a kernel argument
-  if (big) g_big_launches++;
-  run_or_record(stream, [=] { sweep_footprint(kind, cls, big, a, grid); });
+  if (rows == 8) g_big_launches++;
+  run_or_record(stream, [=] { sweep_footprint(kind, cls, fs, rows, a, grid); });
   return hipSuccess;
 }
 
@@ -185,7 +263,7 @@ hipError_t launch_accept(const AcceptArgs& args, unsigned long long* keys, const
   return hipSuccess;
 }
 
-int sweep_blocks_per_cu(int kind, int cls, bool all) { return (void)kind, (void)cls, (void)all, 2; }
+int sweep_blocks_per_cu(int kind, int cls, int fs, int rows) { return (void)kind, (void)cls, (void)fs, (void)rows, 2; }
 
 }  // namespace qg
 

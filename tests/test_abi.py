@@ -111,13 +111,25 @@ def test_validation_accepts_and_sizes_workspace():
     assert qgemm.validate([], qgemm.PATH_AUTO, 0x40000000, 1 << 30) == qgemm.ERR_INVALID_ARG
 
 
-def test_workspace_does_not_depend_on_M_split():
-    """K slicing depends on shapes only: the workspace grows linearly in M."""
-    a = qgemm.workspace_bytes([_job(N=34816, K=5120, M=1, Y=0x100000000, ldy=34816,
-                                    packed=0x200000000, X=0x300000000, ldx=5120)])
-    b = qgemm.workspace_bytes([_job(N=34816, K=5120, M=2, Y=0x100000000, ldy=34816,
-                                    packed=0x200000000, X=0x300000000, ldx=5120)])
-    assert b > a > 0
+def test_workspace_sized_by_accumulators():
+    """The split-K slots hold each lane's accumulators: one per row block up to
+    four panel rows on the MFMA path (M = 1..4 share a size), more above; the
+    K split itself depends on the shapes only."""
+    def ws(M, path=qgemm.PATH_AUTO):
+        return qgemm.workspace_bytes([_job(N=34816, K=5120, M=M, Y=0x100000000, ldy=34816,
+                                           packed=0x200000000, X=0x300000000, ldx=5120)], path)
+    assert ws(1) == ws(4) > 0
+    assert ws(8) == ws(5) > ws(4)
+    assert ws(16) > ws(8)
+    assert ws(2, qgemm.PATH_GEMV) > ws(1, qgemm.PATH_GEMV) > 0
+
+
+def test_validation_rejects_workspace_overlap():
+    """The workspace is written: it may overlap no job's X, weights or Y."""
+    a = _job()
+    for w in (0x100000, 0x200000 - 256, 0x10000000):     # packed, X (its start inside), Y
+        assert qgemm.validate([a], qgemm.PATH_AUTO, w, 1 << 20) == qgemm.ERR_INVALID_ARG, hex(w)
+    assert qgemm.validate([a], qgemm.PATH_AUTO, 0x40000000, 1 << 20) == qgemm.OK
 
 
 def test_status_strings():
@@ -160,6 +172,12 @@ def test_verify_head_validation_rejects_before_any_launch():
     assert call(w=0) == qgemm.ERR_INVALID_ARG
     assert call(w=wsp + 8) == qgemm.ERR_INVALID_ARG
     assert call(nb=ws - 8) == qgemm.ERR_INVALID_ARG
+    # outputs and workspace are written: no overlap among them or with the job
+    assert call(a=acc) == qgemm.ERR_INVALID_ARG             # argmax over accepted
+    assert call(a=mx + 8) == qgemm.ERR_INVALID_ARG          # argmax over maxlogit
+    assert call(c=wsp + 256) == qgemm.ERR_INVALID_ARG       # accepted inside the workspace
+    assert call(a=0x200000) == qgemm.ERR_INVALID_ARG        # argmax over the head's X
+    assert call(w=0x100000) == qgemm.ERR_INVALID_ARG        # workspace over the weights
 
 
 def test_round_validation_rejects_before_any_launch():

@@ -269,8 +269,10 @@ def test_many_jobs_one_sweep():
                f"N={N} K={K}")
 
 
-def test_workspace_counters_return_to_zero():
-    """Split-K counters are left at zero, so the workspace is reusable."""
+def test_workspace_slots_return_to_zero():
+    """Every split-K slot a sweep writes is read and cleared by the same
+    sweep: after each call the workspace of a one-matrix sweep (slots only)
+    is all zero again, so it serves any later set of jobs without a refill."""
     import torch
 
     say("workspace reuse")
@@ -280,13 +282,30 @@ def test_workspace_counters_return_to_zero():
     packed = packed_dev(ref_packed)
     X = synth.x_fp16(7, M, K)
     Xd, Y = x_dev(X), y_dev(M, N)
-    s = Sweep([qgemm.make_job(packed, bits, N, K, Xd, Y, M)])
+    job_a = qgemm.make_job(packed, bits, N, K, Xd, Y, M)
+    # a second set of different shapes, path and panel height
+    N2, K2, bits2, M2 = 5120, 17408, 5, 6
+    W2 = _weights(2_000_001, N2, K2)
+    ref2 = oracle.quantize_pack(W2, bits2)
+    packed2 = packed_dev(ref2)
+    X2 = synth.x_fp16(8, M2, K2)
+    Xd2, Y2 = x_dev(X2), y_dev(M2, N2)
+    job_b = qgemm.make_job(packed2, bits2, N2, K2, Xd2, Y2, M2)
+    ws = qgemm.Workspace(max(qgemm.workspace_bytes([job_a]), qgemm.workspace_bytes([job_b]),
+                             qgemm.workspace_bytes([job_a], qgemm.PATH_GEMV)), device=device())
     outs = []
-    for _ in range(3):
+    for path in (qgemm.PATH_AUTO, qgemm.PATH_AUTO, qgemm.PATH_GEMV, qgemm.PATH_AUTO):
         Y.fill_(float("nan"))
-        s()
+        qgemm.sweep([job_a], ws, path)
         torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws.buf)) == 0, "slots left non-zero"
         outs.append(Y.cpu().numpy())
-    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+        qgemm.sweep([job_b], ws)
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws.buf)) == 0, "slots left non-zero"
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[3])
     Yref = oracle.sweep(ref_packed, N, K, bits, X)
-    _check(outs[0], Yref, X, oracle.max_scale(ref_packed, N, K, bits), "reuse")
+    for o in outs:
+        _check(o, Yref, X, oracle.max_scale(ref_packed, N, K, bits), "reuse")
+    Yref2 = oracle.sweep(ref2, N2, K2, bits2, X2)
+    _check(Y2[:, :N2].cpu().numpy(), Yref2, X2, oracle.max_scale(ref2, N2, K2, bits2), "reuse, second set")
