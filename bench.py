@@ -349,6 +349,61 @@ def attn_bench(args):
             torch.cuda.empty_cache()
 
 
+def timeline(args):
+    """Per-wave timeline of the stream kernel (a build of the library with
+    s_memrealtime stamps): workloads 2 (M = 1) and 3 (M = 6), the last of
+    `steps` back-to-back sweeps.  Prints one JSON line per workload with
+    percentiles (us) of each wave's start (after the first wave's), first
+    step computed, streaming span and end."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import __graft_entry__
+    from self_speculative_verify_amd import qgemm
+
+    __graft_entry__.ensure_built("qgemm_timeline")
+    qgemm.LIB_PATH = __graft_entry__.LIBS["qgemm_timeline"]
+    L = qgemm.lib()
+    L.qgemm_timeline_set.argtypes = [ctypes.c_void_p]
+    L.qgemm_timeline_set.restype = None
+    words = 8
+    tr = torch.zeros(4096 * words, dtype=torch.int64, device="cuda")
+    L.qgemm_timeline_set(tr.data_ptr())
+    for cfg in (2, 3):
+        b = Bench(cfg)
+        tr.zero_()
+        ms, _ = b.run(args.steps, args.warmup)
+        torch.cuda.synchronize()
+        t = tr.cpu().numpy().reshape(-1, words)
+        t = t[t[:, 0] > 0]
+        base = t[:, 0].min()
+        us = lambda a: (a / 100.0)  # 100 MHz
+        pct = lambda a: [round(float(x), 2) for x in np.percentile(a, [0, 10, 50, 90, 100])]
+        readers = t[:, 5] & 8 != 0
+        out = {
+            "workload": b.wl.name, "M": b.M, "waves": int(len(t)), "ms_per_sweep": round(ms, 5),
+            "percentiles": [0, 10, 50, 90, 100],
+            "start_us": pct(us(t[:, 0] - base)),
+            "first_step_us": pct(us(t[:, 1] - t[:, 0])),
+            "stream_span_us": pct(us(t[:, 2] - t[:, 1])),
+            "after_last_step_us": pct(us(t[:, 3] - t[:, 2])),
+            "end_us": pct(us(t[:, 3] - base)),
+            "kernel_span_us": round(float(us(t[:, 3].max() - base)), 2),
+            "readers": int(readers.sum()),
+            "wait_us": pct(us(t[:, 4])),
+            "compute_us": pct(us(t[:, 7])),
+            "plan_us": pct(us(t[:, 6] - t[:, 0])),
+        }
+        print(json.dumps(out), flush=True)
+        if args.timeline_dump:
+            np.save(os.path.join(args.timeline_dump, f"timeline_cfg{cfg}.npy"), t)
+        del b
+        torch.cuda.empty_cache()
+    L.qgemm_timeline_set(None)
+
+
 def cpu_baseline():
     """The oracle, untuned, on the host cores: the full M = 1 sweep of the
     34816 x 5120 4-bit gate+up matrix (generation and packing untimed)."""
@@ -389,6 +444,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--stack-layers", type=int, default=64)
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB")
+    ap.add_argument("--timeline-dump", default="", metavar="DIR",
+                    help="with --timeline: also save the raw stamps (numpy) under DIR")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-wave stamps of the stream kernel on workloads 2 and 3 (diagnostic build)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the sweep shards "
@@ -415,6 +474,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
+        return
+
+    if args.timeline:
+        timeline(args)
         return
 
     if args.only == 6:

@@ -297,10 +297,11 @@ struct Group {
 
 template <int kMPad, bool kAll>
 __global__ void __launch_bounds__(64 * group_waves(kMPad)) __attribute__((amdgpu_waves_per_eu(kMPad >= 64 ? 2 : 3)))
-group_kernel(SweepArgs args) {
+group_kernel(SweepArgs) {
   using S = Group<kMPad>;
   __shared__ __attribute__((aligned(1024))) uint8_t xs[S::kLdsBytes];
   const uint32_t xs_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)xs;
+  const QG_CONST SweepArgs& args = kernel_args();
   const QG_CONST JobDesc* D = job_table(args);
   const int tid = threadIdx.x;
   // argmax keys of the verify head start at 0 (the first unit's barriers

@@ -23,6 +23,12 @@ hipError_t launch_accept(const AcceptArgs& a, unsigned long long* keys, const in
                          float* maxval, int32_t* accepted, hipStream_t stream);
 }  // namespace qg
 
+#ifdef QG_TIMELINE
+// Timeline build only: the stamp buffer every stream launch writes (null: none).
+static unsigned long long* g_trace = nullptr;
+extern "C" void qgemm_timeline_set(void* trace) { g_trace = (unsigned long long*)trace; }
+#endif
+
 namespace {
 
 using qg::JobDesc;
@@ -163,13 +169,11 @@ int class_of(int kind, int M) {
 
 int cu_count();
 
-// Waves of a stream launch: kStreamWaves, or kStreamWavesBig for a big one,
-// but never more than T / kMaxUnitWeight, so that every wave holds at least
-// one step (contributor counts rely on it).  Depends on the shapes only,
-// never on M.
-int64_t stream_waves(int64_t T, bool big) {
-  const int64_t base = big ? qg::kStreamWavesBig : qg::kStreamWaves;
-  return std::max<int64_t>(1, std::min<int64_t>(base, T / qg::kMaxUnitWeight));
+// Waves of a stream launch: kStreamWaves, but never more than
+// T / kMaxUnitWeight, so that every wave holds at least one step.  Depends on
+// the shapes only, never on M.
+int64_t stream_waves(int64_t T) {
+  return std::max<int64_t>(1, std::min<int64_t>(qg::kStreamWaves, T / qg::kMaxUnitWeight));
 }
 
 Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* keys = nullptr) {
@@ -268,7 +272,7 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* k
       off = round_up(off + l.descs.size() * sizeof(JobDesc) + l.index.size() * sizeof(int32_t), 256);
     }
     if (l.kind != kGroupMfma) {
-      l.nwaves = (int)stream_waves(l.total, l.big);
+      l.nwaves = (int)stream_waves(l.total);
       l.slots_off = soff;
       soff = round_up(soff + (size_t)qg::stream_slot_bytes(l.nwaves, l.rows, l.kind == kStreamMfma, l.cls), 256);
     }
@@ -636,6 +640,9 @@ qgemm_status launch_plan(const Plan& P, uint8_t* tables, uint8_t* slots, hipStre
     }
     if (l.kind != kGroupMfma) {
       args.slots = (float*)(slots + l.slots_off);
+#ifdef QG_TIMELINE
+      args.trace = g_trace;
+#endif
       args.slot_bytes = qg::stream_slot_bytes(l.nwaves, l.rows, l.kind == kStreamMfma, l.cls);
       args.spin_limit = qg::kSpinLimit;
       args.nwaves = l.nwaves;

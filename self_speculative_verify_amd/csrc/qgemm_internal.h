@@ -34,15 +34,12 @@ constexpr int kXRowBytes = 272;      // LDS row stride of a staged X chunk (256 
 // stream kernel (panels of at most 16 rows): waves per workgroup, and the
 // waves in the grid.  The count is chosen from the shapes alone -- never from
 // the device or M -- so the K split of every row group, and with it every
-// output bit, is reproducible.  A launch of at least kStreamBigBytes of
-// weights is "big": twice the waves (two per SIMD keep more loads in flight
-// over a long stream, while a shorter launch loses more to the extra waves'
-// start-up and exchange than it gains) and, on the MFMA path, steps of twice
-// the row blocks (one X chunk serves eight weight tiles instead of four),
-// two of them in flight instead of four.
+// output bit, is reproducible.  Two waves per SIMD: while one computes a step
+// (the unpack is VALU-bound) the other's loads are in flight.  A launch of at
+// least kStreamBigBytes of weights is "big": on the MFMA path its steps span
+// twice the row blocks (one X chunk serves eight weight tiles instead of four).
 constexpr int kStreamWavesPerBlock = 4;
-constexpr int kStreamWaves = 1024;
-constexpr int kStreamWavesBig = 2048;
+constexpr int kStreamWaves = 2048;
 constexpr int64_t kStreamBigBytes = (int64_t)4 << 30;
 // group kernel (17..64 rows): waves per workgroup (three per SIMD where the
 // registers allow it: padded rows 32 and 48), 16-row blocks per wave
@@ -129,8 +126,20 @@ struct SweepArgs {
   const JobDesc* table;  // device copy of all jobs (when njobs > kMaxInline), else null
   const int32_t* index;  // with a table: uend of every job, then the first job of every bucket
   float* slots;          // stream kernel: two partial-sum slots per wave (all zero between calls)
+#ifdef QG_TIMELINE
+  unsigned long long* trace;  // timeline build only: kTraceWords stamps per stream wave
+#endif
   JobDesc inl[kMaxInline];
 };
+
+#ifdef QG_TIMELINE
+// Timeline build (a diagnostic variant of the library): per stream wave,
+//   [0] start, [1] first step computed, [2] last step computed, [3] end
+//   (s_memrealtime, 100 MHz), [4] time waiting for step data after the
+//   first step, [5] phase mask, [6] plan complete (the first tile's address
+//   known), [7] time computing steps (MFMA path).
+constexpr int kTraceWords = 8;
+#endif
 
 // Stream kernel slots: per wave two slots (its head piece, its tail piece),
 // each 64 lanes x rows * acc floats; acc = accumulators per row block (MFMA:

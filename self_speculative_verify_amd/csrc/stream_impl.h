@@ -15,22 +15,18 @@
 // shapes only, so every output bit is the same for every M of a class.
 //
 // A row group whose steps fall into several ranges ("split") is summed
-// without counters or waits on the critical path:
-//   * its first contributor (the wave holding its first step) and every
-//     contributor after the second are writers: they store their partial
-//     sums into a slot of their own;
-//   * the second contributor is its reader: it adds the partials in wave
-//     order (k order) to its own, writes Y and clears the slots.
-// A wave processes the pieces it writes first and the piece it reads last, so
-// a reader normally finds every partial long written.  Slots hold the fp32
-// bits of the partials with +0 stored as -0; an all-zero word means "not yet
-// written" and a workspace of zeros is empty, which every completed sweep
-// leaves behind.  The reader polls (bounded) until every word of its
-// sources is non-zero.  Readers only ever wait for waves of lower index,
-// which are dispatched no later than themselves (look-back), and writers
-// wait for nothing, so the waits end.  Accumulators start at +0 and fp32
-// round-to-nearest never turns +0 into -0, so no partial is -0 itself; the
-// reader's sum with a stored -0 is bitwise the sum with +0.
+// without counters (stream_plan.h has the rules): every contributor but the
+// last stores its partial sums into a slot of its own, and the last one adds
+// them in wave order (k order), its own last, writes Y and clears the slots.
+// A wave takes the pieces it writes first and the piece it reads last, so a
+// reader normally finds the first contributor's partial long written.  Slots
+// hold the fp32 bits of the partials with +0 stored as -0; an all-zero word
+// means "not yet written" and a workspace of zeros is empty, which every
+// completed sweep leaves behind.  The reader polls (bounded) until every word
+// of its sources is non-zero; it only ever waits for waves of lower index.
+// Accumulators start at +0 and fp32 round-to-nearest never turns +0 into -0,
+// so no partial is -0 itself, and a sum with a stored -0 is bitwise the sum
+// with +0.
 //
 // Per step the X chunk (class rows x 128 k: 16 bytes per lane and load, one
 // load for up to four rows) goes through a wave-private LDS buffer, from
@@ -66,7 +62,7 @@ struct Stream {
   static constexpr int kA = kMfma ? (kCap + 3) / 4 : kCap;      // accumulators per row block
   static constexpr int kAcc = kR * kA;                         // partial-sum floats per lane
   static constexpr int kXP = (kCap * 16 + 63) / 64;            // 16-byte X pieces per lane and step
-  static constexpr int kDepth = kR >= 8 ? 2 : 4;               // steps in flight
+  static constexpr int kDepth = 2;                             // steps in flight
   static constexpr bool kSide = (kFS & (kSetQ5 | kSetZP)) != 0;
   static constexpr int kOnly = kFS == kSetQ4 ? kFmtQ4 : kFS == kSetQ5 ? kFmtQ5 : kFS == kSetG64 ? kFmtG64
                                : kFS == kSetZP ? kFmtZP : 0;   // the one format, or 0
@@ -86,38 +82,73 @@ struct Stream {
   // words, and the X chunk of k tile kt: lane l, piece p holds X[row][k0 +
   // 8 col ..] for row = 4p + l/16 (rows past M read row M-1) and col = l%16;
   // k is clamped into the row (padding groups multiply it by zero codes).
+  // Per-lane byte offsets of a tile's loads, and of the lane's X piece in
+  // its job's panel (row clamped to M - 1, k = 0), computed once per job: the
+  // loads then take a uniform 64-bit base plus an unsigned 32-bit lane offset
+  // (the global_load SGPR-base form), with no per-step address arithmetic.
+  struct Lane {
+    uint32_t code, scale, scale64, hi, zp;
+    uint32_t x[kXP];
+    uint32_t xcol;
+  };
+  static __device__ __forceinline__ void lane_offsets(Lane& o, int lane) {
+    o.code = 16u * lane;
+    o.scale = kScaleOff + 8u * (lane & 15);
+    o.scale64 = kScaleOff + 4u * (lane & 15);
+    o.hi = kHiOff + 4u * lane;
+    o.zp = kZeroOff + 2u * (lane & 15);
+    o.xcol = 16u * (lane & 15);
+  }
+  static __device__ __forceinline__ void x_offsets(Lane& o, const Pos& c, int lane) {
+#pragma unroll
+    for (int p = 0; p < kXP; p++) {
+      const int row = 4 * p + (lane >> 4);
+      const int m = row < c.M ? row : c.M - 1;
+      o.x[p] = 2u * (uint32_t)(m * c.ldx) + o.xcol;
+    }
+  }
+  template <typename T>
+  static __device__ __forceinline__ T ldnt(const uint8_t* base, uint32_t off) {
+    return __builtin_nontemporal_load((const QG_GLOBAL T*)((const QG_GLOBAL uint8_t*)base + off));
+  }
+
   template <int F>
   static __device__ __forceinline__ void load_tiles(Step& t, const uint8_t* wp, const uint32_t (&roff)[kR],
-                                                    bool spill, int lane) {
+                                                    bool spill, const Lane& o) {
 #pragma unroll
     for (int r = 0; r < kR; r++) {
       const uint8_t* tp = wp + (spill ? 0u : roff[r]);
-      t.c[r] = __builtin_nontemporal_load(gload_ptr<u4_t>(tp + 16 * lane));
+      t.c[r] = ldnt<u4_t>(tp, o.code);
       if constexpr (F == kFmtG64) {
-        t.s[r].x = __builtin_nontemporal_load(gload_ptr<uint32_t>(tp + kScaleOff + 4 * (lane & 15)));
+        t.s[r].x = ldnt<uint32_t>(tp, o.scale64);
         t.s[r].y = 0u;
       } else {
-        t.s[r] = __builtin_nontemporal_load(gload_ptr<u2_t>(tp + kScaleOff + 8 * (lane & 15)));
+        t.s[r] = ldnt<u2_t>(tp, o.scale);
       }
       if constexpr (kSide) {
-        if constexpr (F == kFmtQ5) t.h[r] = __builtin_nontemporal_load(gload_ptr<uint32_t>(tp + kHiOff + 4 * lane));
-        else if constexpr (F == kFmtZP)
-          t.h[r] = __builtin_nontemporal_load(gload_ptr<uint16_t>(tp + kZeroOff + 2 * (lane & 15)));
+        if constexpr (F == kFmtQ5) t.h[r] = ldnt<uint32_t>(tp, o.hi);
+        else if constexpr (F == kFmtZP) t.h[r] = ldnt<uint16_t>(tp, o.zp);
         else t.h[r] = 0u;
       }
     }
   }
 
-  static __device__ __forceinline__ void load_x(Step& t, const JobDesc& d, int kt, int lane) {
-    const uint8_t* xb = (const uint8_t*)d.X;
-    const int col = lane & 15;
-    int k = kt * kTileK + 8 * col;
-    k = k < d.K - 8 ? k : d.K - 8;
+  // X chunk of k tile kt: lane l, piece p holds X[row][k0 + 8 col ..] for
+  // row = 4p + l/16 (rows past M read row M-1) and col = l%16; in a k tile
+  // past K's end, k is clamped into the row (padding groups multiply it by
+  // zero codes).
+  static __device__ __forceinline__ void load_x(Step& t, const Pos& c, const Lane& o, int lane) {
+    const uint8_t* xb = (const uint8_t*)c.X;
+    if ((c.kt + 1) * kTileK <= c.K) {
+      const uint8_t* xk = xb + 2u * (uint32_t)(c.kt * kTileK);
 #pragma unroll
-    for (int p = 0; p < kXP; p++) {
-      const int row = 4 * p + (lane >> 4);
-      const int m = row < d.M ? row : d.M - 1;
-      t.x[p] = *gload_ptr<u4_t>(xb + 2 * ((int64_t)m * d.ldx + k));
+      for (int p = 0; p < kXP; p++) t.x[p] = *(const QG_GLOBAL u4_t*)((const QG_GLOBAL uint8_t*)xk + o.x[p]);
+    } else {
+      int k = c.kt * kTileK + 8 * (lane & 15);
+      k = k < c.K - 8 ? k : c.K - 8;
+#pragma unroll
+      for (int p = 0; p < kXP; p++)
+        t.x[p] = *(const QG_GLOBAL u4_t*)((const QG_GLOBAL uint8_t*)xb + (o.x[p] - o.xcol + 2u * (uint32_t)k));
     }
   }
 
@@ -128,8 +159,8 @@ struct Stream {
   // job's own format.  Tile r of the step sits roff[r] bytes after tile
   // (rg * kR, kt); blocks past the job's last re-read its last one (their
   // sums are never stored).
-  static __device__ __forceinline__ void load(Step& t, const Pos& c, const QG_CONST JobDesc* D,
-                                              const uint8_t* spill, int lane) {
+  static __device__ __forceinline__ void load(Step& t, const Pos& c, const uint8_t* spill, const Lane& o,
+                                              int lane) {
     const int tb = tile_bytes(kOnly ? kOnly : c.fmt);
     const uint32_t rstride = (uint32_t)(c.nkt * tb);
     const int left = c.nrb - 1 - c.rg * kR;
@@ -139,14 +170,14 @@ struct Stream {
     const uint8_t* wp = spill ? spill : c.packed + ((int64_t)c.rg * kR * c.nkt + c.kt) * tb;
     const bool sp = spill != nullptr;
     if constexpr (kOnly) {
-      load_tiles<kOnly>(t, wp, roff, sp, lane);
+      load_tiles<kOnly>(t, wp, roff, sp, o);
     } else {
-      if ((kFS & kSetQ4) && c.fmt == kFmtQ4) load_tiles<kFmtQ4>(t, wp, roff, sp, lane);
-      else if ((kFS & kSetQ5) && c.fmt == kFmtQ5) load_tiles<kFmtQ5>(t, wp, roff, sp, lane);
-      else if ((kFS & kSetG64) && c.fmt == kFmtG64) load_tiles<kFmtG64>(t, wp, roff, sp, lane);
-      else load_tiles<kFmtZP>(t, wp, roff, sp, lane);
+      if ((kFS & kSetQ4) && c.fmt == kFmtQ4) load_tiles<kFmtQ4>(t, wp, roff, sp, o);
+      else if ((kFS & kSetQ5) && c.fmt == kFmtQ5) load_tiles<kFmtQ5>(t, wp, roff, sp, o);
+      else if ((kFS & kSetG64) && c.fmt == kFmtG64) load_tiles<kFmtG64>(t, wp, roff, sp, o);
+      else load_tiles<kFmtZP>(t, wp, roff, sp, o);
     }
-    load_x(t, D[c.j], c.kt, lane);
+    load_x(t, c, o, lane);
   }
 
   static __device__ __forceinline__ const uint8_t* spill_of(const JobDesc& d) {
@@ -189,18 +220,22 @@ struct Stream {
           const f4_t c0 = (F == kFmtG64 && (j & 1)) ? p[j ^ 1] : zero;
           p[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], q, c0, 0, 0, 0);
         }
-        const h2_t s01 = scale_pair(t.s[r].x), s23 = scale_pair(t.s[r].y);
-        const _Float16 sh[4] = {s01.x, s01.y, s23.x, s23.y};
+        // each scale converted by an instruction of its own (left to itself
+        // the compiler fuses the conversion into mixed-precision FMAs, which
+        // issue more slowly)
         if constexpr (F == kFmtG64) {
+          const float s0 = scale_f32<0>(t.s[r].x), s1 = scale_f32<1>(t.s[r].x);
 #pragma unroll
-          for (int h = 0; h < 2; h++)
+          for (int i = 0; i < kA; i++) acc[r][i] = __builtin_fmaf(s0, p[1][i], acc[r][i]);
 #pragma unroll
-            for (int i = 0; i < kA; i++) acc[r][i] = __builtin_fmaf((float)sh[h], p[2 * h + 1][i], acc[r][i]);
+          for (int i = 0; i < kA; i++) acc[r][i] = __builtin_fmaf(s1, p[3][i], acc[r][i]);
         } else {
+          const float sj[4] = {scale_f32<0>(t.s[r].x), scale_f32<1>(t.s[r].x), scale_f32<0>(t.s[r].y),
+                               scale_f32<1>(t.s[r].y)};
 #pragma unroll
           for (int j = 0; j < 4; j++)
 #pragma unroll
-            for (int i = 0; i < kA; i++) acc[r][i] = __builtin_fmaf((float)sh[j], p[j][i], acc[r][i]);
+            for (int i = 0; i < kA; i++) acc[r][i] = __builtin_fmaf(sj[j], p[j][i], acc[r][i]);
         }
       }
     } else {
@@ -386,24 +421,29 @@ struct Stream {
     }
   }
 
-  // Reader of row group rg of job j: partials of its contributors wf .. wl
-  // in wave order with its own (wave wf + 1) in second place, then Y.
+  // Reader of row group rg of job j (its last contributor, wave wl): the
+  // partials of contributors wf .. wl - 1 in wave order, then its own, to Y.
   static __device__ __forceinline__ void read_split(float (&acc)[kR][kA], Ctx& cx, int j, int rg) {
     int wf, wl;
     stream_contributors(cx.q, cx.rem, cx.D, j, rg, wf, wl);
     uint32_t w[kAcc];
     take_partial(w, cx, wf, 1);
+    float v[kR][kA];
 #pragma unroll
     for (int r = 0; r < kR; r++)
 #pragma unroll
-      for (int i = 0; i < kA; i++) acc[r][i] = __builtin_bit_cast(float, w[r * kA + i]) + acc[r][i];
-    for (int src = wf + 2; src <= wl; src++) {
+      for (int i = 0; i < kA; i++) v[r][i] = __builtin_bit_cast(float, w[r * kA + i]);
+    for (int src = wf + 1; src < wl; src++) {
       take_partial(w, cx, src, 0);
 #pragma unroll
       for (int r = 0; r < kR; r++)
 #pragma unroll
-        for (int i = 0; i < kA; i++) acc[r][i] += __builtin_bit_cast(float, w[r * kA + i]);
+        for (int i = 0; i < kA; i++) v[r][i] += __builtin_bit_cast(float, w[r * kA + i]);
     }
+#pragma unroll
+    for (int r = 0; r < kR; r++)
+#pragma unroll
+      for (int i = 0; i < kA; i++) acc[r][i] = v[r][i] + acc[r][i];
     store_y(acc, cx, j, rg);
   }
 
@@ -421,15 +461,24 @@ struct Stream {
   }
 
   // ----------------------------------------------------------------- main
+#ifdef QG_TIMELINE
+  // stamps on the MFMA path only (the GEMV kernels have no registers to spare)
+  static constexpr bool kTrace = kMfma;
+  // s_memrealtime after v is computed (the operand orders it after the work)
+  static __device__ __forceinline__ unsigned long long trace_stamp(float v) {
+    unsigned long long t;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_memrealtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(t) : "v"(v) : "memory");
+    return t;
+  }
+#endif
   template <typename F, int... P>
   static __device__ __forceinline__ void each_slot(F& f, std::integer_sequence<int, P...>) {
     (f(std::integral_constant<int, P>{}), ...);
   }
 
-  // Inlined into the kernel on purpose: the job table pointer below is the
-  // address of the kernel argument in the constant (kernarg) address space,
-  // which a by-reference copy on the stack would not be.
-  static __device__ __forceinline__ void run(const SweepArgs& args, uint8_t* xs) {
+  // args: the kernel's argument where it lies (kernarg segment); the job
+  // table pointer below may point into it.
+  static __device__ __forceinline__ void run(const QG_CONST SweepArgs& args, uint8_t* xs) {
     Ctx cx;
     const QG_CONST JobDesc* D = job_table(args);
     cx.D = D;
@@ -444,27 +493,49 @@ struct Stream {
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     cx.gw = (int)blockIdx.x * kStreamWavesPerBlock + wave;
     if (cx.gw >= args.nwaves) return;
+#ifdef QG_TIMELINE
+    const unsigned long long t0 = kTrace ? trace_stamp(0.f) : 0ull;
+    unsigned long long t1 = 0, t2 = 0, ta = 0, tb = 0, twait = 0, tcomp = 0;
+    int nsteps = 0;
+#endif
 #pragma unroll
     for (int i = 0; i < kA; i++) cx.best[i] = 0ull;
     const int a = stream_start_of(cx.gw, cx.q, cx.rem);
     const int b = a + cx.q + (cx.gw < cx.rem ? 1 : 0);
     Phases P;
-    stream_plan(P, args, D, cx.gw, a, b);
+    const StreamGrid grid = {args.index, args.njobs, args.bshift, cx.q, cx.rem};
+    stream_plan(P, grid, D, cx.gw, a, b);
 
     Pos pc, cc;
     stream_start(pc, D, P);
     cc = pc;
     const int njobs = args.njobs;
+    Lane lo;
+    lane_offsets(lo, lane);
+    x_offsets(lo, pc, lane);
+    int xjob = pc.j;  // the job lo.x was computed for
+#ifdef QG_TIMELINE
+    // the plan is complete once the first tile's address is known
+    unsigned long long tplan = 0;
+    if (kTrace) {
+      asm volatile("" ::"s"(pc.packed), "s"(pc.X));
+      tplan = trace_stamp(0.f);
+    }
+#endif
     const uint8_t* spill = nullptr;
     Step buf[kDepth];
 #pragma unroll
     for (int p = 0; p < kDepth; p++) {
-      load(buf[p], pc, D, spill, lane);
+      load(buf[p], pc, spill, lo, lane);
       if (!spill) {
         stream_advance(pc, D, P, njobs);
         if (pc.ph == 4) {
           if (pc.j >= njobs) stream_load_job(pc, D, njobs - 1);
           spill = spill_of(D[pc.j]);
+        }
+        if (pc.j != xjob) {
+          x_offsets(lo, pc, lane);
+          xjob = pc.j;
         }
       }
     }
@@ -477,7 +548,22 @@ struct Stream {
     auto slot = [&](auto pc_) {
       constexpr int p = decltype(pc_)::value;
       if (!done) {
+#ifdef QG_TIMELINE
+        if (kTrace) {
+          // every load of the step has landed: the time since the previous
+          // step's compute ended was spent waiting for it
+          asm volatile("" ::"v"(buf[p].c[kR - 1]), "v"(buf[p].s[kR - 1]), "v"(buf[p].x[kXP - 1]));
+          ta = trace_stamp(0.f);
+          if (nsteps) twait += ta - tb;
+        }
+#endif
         compute_any(acc, buf[p], cc.fmt, xs, lane);
+#ifdef QG_TIMELINE
+        if (kTrace) {
+          tb = trace_stamp(acc[kR - 1][kA - 1]);
+          tcomp += tb - ta;
+        }
+#endif
         const int j = cc.j, rg = cc.rg, ph = cc.ph;
         const bool rg_end = cc.kt == cc.nkt - 1;
         stream_advance(cc, D, P, njobs);
@@ -488,27 +574,50 @@ struct Stream {
           zero(acc);
         }
         done = cc.ph == 4;
+#ifdef QG_TIMELINE
+        if (kTrace && nsteps++ == 0) t1 = trace_stamp(acc[0][0]);
+        if (kTrace && done) t2 = trace_stamp(acc[0][0]);
+#endif
       }
-      load(buf[p], pc, D, spill, lane);
+      load(buf[p], pc, spill, lo, lane);
       if (!spill) {
         stream_advance(pc, D, P, njobs);
         if (pc.ph == 4) {
           if (pc.j >= njobs) stream_load_job(pc, D, njobs - 1);
           spill = spill_of(D[pc.j]);
         }
+        if (pc.j != xjob) {
+          x_offsets(lo, pc, lane);
+          xjob = pc.j;
+        }
       }
     };
     while (!done) each_slot(slot, std::make_integer_sequence<int, kDepth>{});
+#ifdef QG_TIMELINE
+    if (kTrace) __builtin_amdgcn_s_waitcnt(0);
+    const unsigned long long t3 = kTrace ? trace_stamp(0.f) : 0ull;
+    if (kTrace && args.trace && lane == 0) {
+      unsigned long long* tr = args.trace + (size_t)cx.gw * kTraceWords;
+      tr[0] = t0;
+      tr[1] = t1;
+      tr[2] = t2;
+      tr[3] = t3;
+      tr[4] = twait;
+      tr[6] = tplan;
+      tr[5] = (unsigned long long)P.mask;
+      tr[7] = tcomp;
+    }
+#endif
     const QG_CONST JobDesc& dk = D[0];
     if (dk.keys) publish(cx, dk.keys + (cx.gw % kKeyCopies) * kKeyRows, dk.M);
   }
 };
 
 template <bool kMfma, int kCap, int kR, int kFS>
-__global__ void __launch_bounds__(64 * kStreamWavesPerBlock) stream_kernel(SweepArgs args) {
+__global__ void __launch_bounds__(64 * kStreamWavesPerBlock) stream_kernel(SweepArgs) {
   using S = Stream<kMfma, kCap, kR, kFS>;
   __shared__ __attribute__((aligned(16))) uint8_t xs[kStreamWavesPerBlock][kCap * kXRowBytes];
-  S::run(args, xs[threadIdx.x >> 6]);
+  S::run(kernel_args(), xs[threadIdx.x >> 6]);
 }
 
 typedef void (*sweep_fn)(SweepArgs);

@@ -11,18 +11,21 @@
 // first rem waves); a wave owns the steps whose first unit lies in its range,
 // at least one (q >= the largest step weight).
 //
-// A row group whose steps fall into several ranges is "split".  Its first
-// contributor (the wave holding its first step) and every contributor after
-// the second store their partial sums into a slot of their own (slot 1 for
-// the first contributor, whose piece is its range's last row group; slot 0
-// for the others, whose piece is their first); the second contributor reads
-// them, adds them in wave order (k order) with its own in second place and
-// writes Y.  A wave takes its pieces in the order
+// A row group whose steps fall into several ranges is "split".  Its last
+// contributor (the wave holding its last step) reads it: every other
+// contributor stores its partial sums into a slot of its own (slot 1 for the
+// first contributor, whose piece is its range's last row group; slot 0 for
+// the middle ones, whose whole range lies in the row group), and the last one
+// adds them in wave order (k order) with its own last and writes Y.  A wave
+// takes its pieces in the order
 //   0: the tail piece it writes (its last row group, split past its range)
-//   1: the head piece it writes (its first row group, read by another wave)
+//   1: its whole range, when that lies inside one row group split at both ends
 //   2: its whole row groups (Y written directly)
-//   3: the head piece it reads
-// so that partials are written early and read late.
+//   3: the head piece it reads (its first row group, split before its range)
+// so that partials are written early and read late.  A reader waits only for
+// waves of lower index, which are dispatched no later than itself, and
+// writers wait for nothing: the waits always end, whatever part of the grid
+// is resident.
 #pragma once
 
 #include "qgemm_internal.h"
@@ -38,15 +41,32 @@
 #define QG_CONST
 #endif
 
+// Every function here is force-inlined: a call would need the kernel
+// argument in memory, and the compiler then copies the whole argument into
+// private memory.  They take scalars, never the argument struct itself.
+#define QG_PLAN __host__ __device__ __forceinline__
+
 namespace qg {
 
-inline __host__ __device__ const QG_CONST JobDesc* job_table(const SweepArgs& a) {
+// The kernels reach their argument only through the kernarg segment (a
+// pointer in the constant address space), never through the C++ parameter:
+// a reference to the parameter lets the compiler copy the whole argument into
+// private memory, and the inline job table must be read where it lies.
+QG_PLAN const QG_CONST JobDesc* job_table(const QG_CONST SweepArgs& a) {
   return a.table ? (const QG_CONST JobDesc*)a.table : (const QG_CONST JobDesc*)&a.inl[0];
 }
+#if defined(__HIP_DEVICE_COMPILE__)
+// the launch's SweepArgs: the kernels' only explicit argument, at offset 0
+__device__ __forceinline__ const QG_CONST SweepArgs& kernel_args() {
+  return *(const QG_CONST SweepArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+}
+#elif defined(__HIPCC__)
+__device__ const SweepArgs& kernel_args();  // host pass: declared, never emitted
+#endif
 
 // Wave w takes units [start(w), start(w + 1)); the wave holding unit f.
-inline __host__ __device__ int stream_start_of(int w, int q, int rem) { return w * q + (w < rem ? w : rem); }
-inline __host__ __device__ int stream_wave_of(int f, int q, int rem) {
+QG_PLAN int stream_start_of(int w, int q, int rem) { return w * q + (w < rem ? w : rem); }
+QG_PLAN int stream_wave_of(int f, int q, int rem) {
   const int edge = rem * (q + 1);
   return f < edge ? f / (q + 1) : rem + (f - edge) / q;
 }
@@ -63,28 +83,32 @@ struct StreamPhases {
   int jA, sA, jH, sH, jT, sT, jE, sE;
 };
 
-// Scalar cursor: phase (4: done), job, row group, k tile, and the job's shape.
+// Scalar cursor: phase (4: done), job, row group, k tile, and what the loads
+// of a step need of its job (kept in scalar registers rather than read from
+// the job table every step).
 struct StreamPos {
   int ph, j, rg, kt;
   int nkt, nrg, nrb, fmt;
   const uint8_t* packed;
+  const uint16_t* X;
+  int ldx, M, K;
 };
 
 // the first present phase after ph (4: none)
-inline __host__ __device__ int stream_next_phase(const StreamPhases& P, int ph) {
+QG_PLAN int stream_next_phase(const StreamPhases& P, int ph) {
   const unsigned m = ((unsigned)P.mask & 15u) >> (ph + 1);
   return m ? ph + 1 + __builtin_ctz(m) : 4;
 }
 // (values are selected, never references: a select between addresses would
 // keep the struct in memory on the device)
-inline __host__ __device__ void stream_phase_begin(const StreamPhases& P, int ph, int& j, int& s) {
+QG_PLAN void stream_phase_begin(const StreamPhases& P, int ph, int& j, int& s) {
   const bool h = (P.mask >> 4) & 1;
   const int jA = P.jA, sA = P.sA, jH = P.jH, sH = P.sH, jT = P.jT, sT = P.sT;
   const bool t0 = ph == 0, th = ph == 2 && h;
   j = t0 ? jT : th ? jH : jA;
   s = t0 ? sT : th ? sH : sA;
 }
-inline __host__ __device__ void stream_phase_end(const StreamPhases& P, int ph, int& j, int& s) {
+QG_PLAN void stream_phase_end(const StreamPhases& P, int ph, int& j, int& s) {
   const bool t = (P.mask >> 5) & 1;
   const int jH = P.jH, sH = P.sH, jT = P.jT, sT = P.sT, jE = P.jE, sE = P.sE;
   const bool e = ph == 0 || (ph == 2 && !t), h = ph == 1 || ph == 3;
@@ -92,20 +116,24 @@ inline __host__ __device__ void stream_phase_end(const StreamPhases& P, int ph, 
   s = e ? sE : h ? sH : sT;
 }
 
-inline __host__ __device__ void stream_load_job(StreamPos& c, const QG_CONST JobDesc* D, int j) {
+QG_PLAN void stream_load_job(StreamPos& c, const QG_CONST JobDesc* D, int j) {
   c.j = j;
   c.nkt = D[j].nkt;
   c.nrg = D[j].nrg;
   c.nrb = D[j].nrb;
   c.fmt = D[j].fmt;
   c.packed = D[j].packed;
+  c.X = D[j].X;
+  c.ldx = (int)D[j].ldx;  // <= 2^24 (host check)
+  c.M = D[j].M;
+  c.K = D[j].K;
 }
-inline __host__ __device__ void stream_seek(StreamPos& c, const QG_CONST JobDesc* D, int j, int s) {
+QG_PLAN void stream_seek(StreamPos& c, const QG_CONST JobDesc* D, int j, int s) {
   stream_load_job(c, D, j);
   c.rg = s / c.nkt;
   c.kt = s - c.rg * c.nkt;
 }
-inline __host__ __device__ void stream_start(StreamPos& c, const QG_CONST JobDesc* D, const StreamPhases& P) {
+QG_PLAN void stream_start(StreamPos& c, const QG_CONST JobDesc* D, const StreamPhases& P) {
   c.ph = stream_next_phase(P, -1);
   int j, s;
   stream_phase_begin(P, c.ph, j, s);
@@ -114,7 +142,7 @@ inline __host__ __device__ void stream_start(StreamPos& c, const QG_CONST JobDes
 
 // One step forward; at a phase end, on to the next phase (c.ph == 4: done,
 // with c.j possibly njobs).
-inline __host__ __device__ void stream_advance(StreamPos& c, const QG_CONST JobDesc* D, const StreamPhases& P,
+QG_PLAN void stream_advance(StreamPos& c, const QG_CONST JobDesc* D, const StreamPhases& P,
                                                int njobs) {
   if (++c.kt == c.nkt) {
     c.kt = 0;
@@ -136,13 +164,19 @@ inline __host__ __device__ void stream_advance(StreamPos& c, const QG_CONST JobD
   }
 }
 
+// The partition and job lookup of a launch (scalars of its arguments).
+struct StreamGrid {
+  const int32_t* index;  // with a job table: uend of every job, then the first job of every bucket
+  int njobs, bshift, q, rem;
+};
+
 // Job holding unit u: a bucket index into the uend list when the jobs come
 // from a table, else a scan of the (at most kMaxInline) inline jobs.
-inline __host__ __device__ int stream_job_of(const SweepArgs& args, const QG_CONST JobDesc* D, int u) {
+QG_PLAN int stream_job_of(const StreamGrid& g, const QG_CONST JobDesc* D, int u) {
   int j = 0;
-  if (args.index) {
-    const QG_CONST int32_t* ends = (const QG_CONST int32_t*)args.index;
-    j = ends[args.njobs + (u >> args.bshift)];
+  if (g.index) {
+    const QG_CONST int32_t* ends = (const QG_CONST int32_t*)g.index;
+    j = ends[g.njobs + (u >> g.bshift)];
     while (u >= ends[j]) j++;
   } else {
     while (u >= D[j].uend) j++;
@@ -151,10 +185,9 @@ inline __host__ __device__ int stream_job_of(const SweepArgs& args, const QG_CON
 }
 
 // The phases of wave gw's range [a, b) (a non-empty set of steps).
-inline __host__ __device__ void stream_plan(StreamPhases& P, const SweepArgs& args, const QG_CONST JobDesc* D,
-                                            int gw, int a, int b) {
+QG_PLAN void stream_plan(StreamPhases& P, const StreamGrid& g, const QG_CONST JobDesc* D, int gw, int a, int b) {
   // first step (jA, sA): the first step of job jA whose first unit is >= a
-  int jA = stream_job_of(args, D, a);
+  int jA = stream_job_of(g, D, a);
   const int wA = unit_weight(D[jA].fmt), dA = a - D[jA].ubeg;
   int sA = dA <= 0 ? 0 : (dA + wA - 1) / wA;
   if (sA == D[jA].nrg * D[jA].nkt) {
@@ -162,16 +195,14 @@ inline __host__ __device__ void stream_plan(StreamPhases& P, const SweepArgs& ar
     sA = 0;
   }
   // last step (jL, sL): the last step whose first unit is <= b - 1
-  const int jL = stream_job_of(args, D, b - 1);
+  const int jL = stream_job_of(g, D, b - 1);
   const int sL = (b - 1 - D[jL].ubeg) / unit_weight(D[jL].fmt);
   const int nktA = D[jA].nkt, nktL = D[jL].nkt;
   const int rgA = sA / nktA, rgL = sL / nktL;
   const bool head = sA != rgA * nktA;             // first row group began before a
   const bool tail = sL != rgL * nktL + nktL - 1;  // last row group runs past b
   const bool one = jA == jL && rgA == rgL;        // the range lies in one row group
-  // the second contributor of the first row group reads it
-  const int uA = D[jA].ubeg + rgA * nktA * unit_weight(D[jA].fmt);
-  const bool reader = head && stream_wave_of(uA, args.q, args.rem) == gw - 1;
+  (void)gw;
   P.jA = jA;
   P.sA = sA;
   // E: (jL, sL) + 1, normalized
@@ -196,11 +227,14 @@ inline __host__ __device__ void stream_plan(StreamPhases& P, const SweepArgs& ar
   P.sT = one ? sA : rgL * nktL;
   int m = (head ? 16 : 0) | (tail ? 32 : 0);
   if (one) {
-    // whole (body), or a piece of a split row group
-    m |= !head && !tail ? 4 : reader ? 8 : head ? 2 : 1;
+    // whole (body), or a piece of a split row group: the tail of the range
+    // continues it (the first contributor writes it, a middle one too), or
+    // the range holds its last step (read here)
+    m |= !head && !tail ? 4 : !tail ? 8 : head ? 2 : 1;
   } else {
+    // the first row group ends inside the range: its head piece is read here
     if (tail) m |= 1;
-    if (head) m |= reader ? 8 : 2;
+    if (head) m |= 8;
     // body: from the end of the head piece to the start of the tail piece
     const int jb0 = head ? P.jH : jA, sb0 = head ? P.sH : sA;
     const int jb1 = tail ? jL : P.jE, sb1 = tail ? P.sT : P.sE;
@@ -210,7 +244,7 @@ inline __host__ __device__ void stream_plan(StreamPhases& P, const SweepArgs& ar
 }
 
 // Contributors wf .. wl of row group rg of job j.
-inline __host__ __device__ void stream_contributors(int q, int rem, const QG_CONST JobDesc* D, int j, int rg,
+QG_PLAN void stream_contributors(int q, int rem, const QG_CONST JobDesc* D, int j, int rg,
                                                     int& wf, int& wl) {
   const int wt = unit_weight(D[j].fmt), nkt = D[j].nkt;
   const int u0 = D[j].ubeg + rg * nkt * wt;

@@ -72,8 +72,8 @@ int64_t tiles_bytes(const qg::JobDesc& d) { return (int64_t)d.nrb * d.nkt * qg::
 // Every wave of a stream launch through the kernels' own planning code
 // (stream_plan.h): each step is taken by exactly one wave, each row group's
 // sums reach Y exactly once -- directly when one wave holds all its steps,
-// else by its second contributor, which reads the partials of all other
-// contributors (slot 1 of the first, slot 0 of the later ones), each written
+// else by its last contributor, which reads the partials of all other
+// contributors (slot 1 of the first, slot 0 of the middle ones), each written
 // exactly once -- and no wave writes a slot twice.
 void stream_schedule_check(const qg::SweepArgs& a, const std::vector<qg::JobDesc>& D) {
   std::vector<int64_t> first(a.njobs + 1, 0);
@@ -87,7 +87,8 @@ void stream_schedule_check(const qg::SweepArgs& a, const std::vector<qg::JobDesc
   for (int w = 0; w < a.nwaves; w++) {
     const int u0 = qg::stream_start_of(w, a.q, a.rem), u1 = u0 + a.q + (w < a.rem ? 1 : 0);
     qg::StreamPhases P;
-    qg::stream_plan(P, a, D.data(), w, u0, u1);
+    const qg::StreamGrid g = {a.index, a.njobs, a.bshift, a.q, a.rem};
+    qg::stream_plan(P, g, D.data(), w, u0, u1);
     CHECK((P.mask & 15) != 0);
     qg::StreamPos c;
     qg::stream_start(c, D.data(), P);
@@ -133,10 +134,10 @@ void stream_schedule_check(const qg::SweepArgs& a, const std::vector<qg::JobDesc
         CHECK(reader[r] == -1);
         continue;
       }
-      CHECK(reader[r] == wf + 1);
+      CHECK(reader[r] == wl);
       CHECK(slot_rg[2 * wf + 1] == r);
       reads[2 * wf + 1]++;
-      for (int src = wf + 2; src <= wl; src++) {
+      for (int src = wf + 1; src < wl; src++) {
         CHECK(slot_rg[2 * src] == r);
         reads[2 * src]++;
       }
