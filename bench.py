@@ -381,7 +381,7 @@ def timeline(args):
         base = t[:, 0].min()
         us = lambda a: (a / 100.0)  # 100 MHz
         pct = lambda a: [round(float(x), 2) for x in np.percentile(a, [0, 10, 50, 90, 100])]
-        readers = t[:, 5] & 8 != 0
+        readers = (t[:, 5] & 8) != 0
         out = {
             "workload": b.wl.name, "M": b.M, "waves": int(len(t)), "ms_per_sweep": round(ms, 5),
             "percentiles": [0, 10, 50, 90, 100],

@@ -61,6 +61,7 @@ template <bool kMfma, int kCap, int kR, int kFS>
 struct Stream {
   static constexpr int kA = kMfma ? (kCap + 3) / 4 : kCap;      // accumulators per row block
   static constexpr int kAcc = kR * kA;                         // partial-sum floats per lane
+  static_assert(kAcc % 4 == 0, "slot words move in 16-byte stores");
   static constexpr int kXP = (kCap * 16 + 63) / 64;            // 16-byte X pieces per lane and step
   static constexpr int kDepth = 2;                             // steps in flight
   static constexpr bool kSide = (kFS & (kSetQ5 | kSetZP)) != 0;
@@ -368,16 +369,10 @@ struct Stream {
         const uint32_t b = __builtin_bit_cast(uint32_t, acc[r][i]);
         w[r * kA + i] = b ? b : 0x80000000u;
       }
-    if constexpr (kAcc % 4 == 0) {
 #pragma unroll
-      for (int e = 0; e < kAcc; e += 4)
-        __builtin_amdgcn_raw_buffer_store_b128(u4_t{w[e], w[e + 1], w[e + 2], w[e + 3]}, sr, o + 4u * e, 0,
-                                               kCoherent);
-    } else {
-#pragma unroll
-      for (int e = 0; e < kAcc; e += 2)
-        __builtin_amdgcn_raw_buffer_store_b64(u2_t{w[e], w[e + 1]}, sr, o + 4u * e, 0, kCoherent);
-    }
+    for (int e = 0; e < kAcc; e += 4)
+      __builtin_amdgcn_raw_buffer_store_b128(u4_t{w[e], w[e + 1], w[e + 2], w[e + 3]}, sr, o + 4u * e, 0,
+                                             kCoherent);
   }
 
   // Reader: the partial of slot (w, k) once every word of it is written
@@ -388,37 +383,22 @@ struct Stream {
     const uint32_t o = slot_off(wsrc, k, cx.lane);
     for (int spin = 0;; spin++) {
       bool ready = true;
-      if constexpr (kAcc % 4 == 0) {
 #pragma unroll
-        for (int e = 0; e < kAcc; e += 4) {
-          const u4_t v = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(sr, o + 4u * e, 0, kCoherent));
-          w[e] = v.x;
-          w[e + 1] = v.y;
-          w[e + 2] = v.z;
-          w[e + 3] = v.w;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < kAcc; e += 2) {
-          const u2_t v = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(sr, o + 4u * e, 0, kCoherent));
-          w[e] = v.x;
-          w[e + 1] = v.y;
-        }
+      for (int e = 0; e < kAcc; e += 4) {
+        const u4_t v = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(sr, o + 4u * e, 0, kCoherent));
+        w[e] = v.x;
+        w[e + 1] = v.y;
+        w[e + 2] = v.z;
+        w[e + 3] = v.w;
       }
 #pragma unroll
       for (int e = 0; e < kAcc; e++) ready = ready && w[e] != 0u;
       if (__builtin_amdgcn_read_exec() == __ballot(ready) || spin >= cx.spin_limit) break;
       __builtin_amdgcn_s_sleep(2);
     }
-    if constexpr (kAcc % 4 == 0) {
 #pragma unroll
-      for (int e = 0; e < kAcc; e += 4)
-        __builtin_amdgcn_raw_buffer_store_b128(u4_t{0u, 0u, 0u, 0u}, sr, o + 4u * e, 0, kCoherent);
-    } else {
-#pragma unroll
-      for (int e = 0; e < kAcc; e += 2)
-        __builtin_amdgcn_raw_buffer_store_b64(u2_t{0u, 0u}, sr, o + 4u * e, 0, kCoherent);
-    }
+    for (int e = 0; e < kAcc; e += 4)
+      __builtin_amdgcn_raw_buffer_store_b128(u4_t{0u, 0u, 0u, 0u}, sr, o + 4u * e, 0, kCoherent);
   }
 
   // Reader of row group rg of job j (its last contributor, wave wl): the
@@ -592,6 +572,11 @@ struct Stream {
         }
       }
     };
+    // Two waves share each SIMD.  The instruction arbiter favours the one in
+    // the lower wave slot, which would finish its range early while the other
+    // lags and delays the end of the sweep; the wave not in slot 0 runs at a
+    // raised priority instead (HW_ID bits 3:0 are the wave slot).
+    if (__builtin_amdgcn_s_getreg((4 << 0) | (0 << 6) | (3 << 11)) != 0) __builtin_amdgcn_s_setprio(1);
     while (!done) each_slot(slot, std::make_integer_sequence<int, kDepth>{});
 #ifdef QG_TIMELINE
     if (kTrace) __builtin_amdgcn_s_waitcnt(0);
