@@ -148,11 +148,11 @@ qgemm_status qgemm_pack(const float* W, int64_t ldw, int64_t N, int64_t K, int b
 
 /* Workspace bytes the sweep of these jobs on this path needs (a device buffer
  * the caller owns, 256-byte aligned); 0 when the jobs are invalid.  It holds
- * the job table (more than 12 jobs), split-K arrival counters and partial
- * sums.  The buffer must be zero-filled before its first use (for instance
- * with qgemm_workspace_init); every completed sweep leaves its counters at
- * zero again, so the same set of jobs (same shapes and path) may sweep on it
- * any number of times.  Its layout depends on those shapes: before a
+ * the job tables (launches of more than 12 jobs) and the split-K partial-sum
+ * slots.  The buffer must be zero-filled before its first use (for instance
+ * with qgemm_workspace_init); every completed sweep leaves its slots at zero
+ * again, so the same set of jobs (same shapes and path) may sweep on it any
+ * number of times.  Its layout depends on those shapes: before a
  * different set of jobs uses a workspace, zero-fill it again (or keep one
  * workspace per set of jobs, or record the sweeps as a round, below, whose
  * layout serves all of them).  A workspace serves one sweep at a time: sweeps
@@ -175,6 +175,24 @@ qgemm_status qgemm_sweep(const qgemm_job* jobs, int njobs, void* workspace, size
  * M > QGEMM_GEMV_MAX_M is QGEMM_ERR_INVALID_ARG. */
 qgemm_status qgemm_sweep_path(const qgemm_job* jobs, int njobs, int path, void* workspace,
                               size_t ws_bytes, void* stream);
+
+/* Allocation-free sweep, for callers that cannot allocate device memory
+ * (code that must not call hipMalloc: tight serving loops, harnesses that
+ * forbid it).  As qgemm_sweep_path, with the library's own scratch in place of
+ * the caller's workspace: one static device array of
+ * QGEMM_NOALLOC_SCRATCH_BYTES, which every GPU the library runs on holds until
+ * the process ends.  A job set whose qgemm_workspace_bytes exceeds that size
+ * is QGEMM_ERR_INVALID_ARG, as are the argument errors of qgemm_sweep_path.
+ * The call allocates no device memory; on `stream` it enqueues, in order: a
+ * fill kernel when the scratch region this sweep's split-K slots need may
+ * hold bytes an earlier call's job table left there, one copy per launch of
+ * more than 12 jobs (its job table, from host memory read during the call),
+ * and the sweep's launches.  Every call on one GPU shares that GPU's scratch:
+ * calls that overlap on one GPU (unordered streams or threads) race.  The
+ * outputs are bitwise those of qgemm_sweep_path for the same jobs and path. */
+#define QGEMM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+qgemm_status qgemm_sweep_noalloc(const qgemm_job* jobs, int njobs, int path, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Verify head (greedy acceptance).  In a self-speculative decode round the

@@ -17,6 +17,7 @@ namespace qg {
 hipError_t launch_pack(const float* W, int64_t ldw, int N, int K, int bits, void* packed,
                        unsigned* flag, hipStream_t stream);
 hipError_t launch_fill_zero(void* p, int64_t words, hipStream_t stream);
+hipError_t scratch_base(uint8_t** base, size_t* bytes);
 int sweep_blocks_per_cu(int kind, int cls, int fs, int rows);
 hipError_t launch_sweep(int kind, int cls, int fs, int rows, const SweepArgs& args, int grid, hipStream_t stream);
 hipError_t launch_accept(const AcceptArgs& a, unsigned long long* keys, const int32_t* drafts, int32_t* argmax,
@@ -372,6 +373,39 @@ qgemm_status qgemm_sweep_path(const qgemm_job* jobs, int njobs, int path, void* 
   if (st != QGEMM_OK) return st;
   Plan P = make_plan(jobs, njobs, path);
   return run_plan(P, workspace, stream);
+}
+
+// Allocation-free sweep: the current device's static scratch in place of a
+// workspace, split-K slots at its bottom and job tables at its top.  Per
+// device, [0, clean) is known to be zero: every completed sweep leaves its
+// slots zero, and only table copies (or the unknown contents before the
+// first call) can leave a byte non-zero.  A call whose slots reach past
+// `clean` clears [clean, slot end) first with the fill kernel.
+qgemm_status qgemm_sweep_noalloc(const qgemm_job* jobs, int njobs, int path, void* stream) {
+  qgemm_status st = validate(jobs, njobs, path, false, {});
+  if (st != QGEMM_OK) return st;
+  Plan P = make_plan(jobs, njobs, path);
+  if (!P.ok) return QGEMM_ERR_UNSUPPORTED;
+  if (P.total > QGEMM_NOALLOC_SCRATCH_BYTES) return QGEMM_ERR_INVALID_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= qg::kMaxDevices) return QGEMM_ERR_HIP;
+  uint8_t* base = nullptr;
+  size_t kScratch = 0;  // QGEMM_NOALLOC_SCRATCH_BYTES (less in host-only test builds)
+  if (qg::scratch_base(&base, &kScratch) != hipSuccess) return QGEMM_ERR_HIP;
+  if (P.total > kScratch) return QGEMM_ERR_INVALID_ARG;
+  static std::mutex mu;
+  static size_t clean[qg::kMaxDevices] = {};
+  std::lock_guard<std::mutex> g(mu);
+  hipStream_t s = (hipStream_t)stream;
+  size_t& c = clean[dev];
+  if (P.slot_bytes > c) {
+    if (qg::launch_fill_zero(base + c, (int64_t)((P.slot_bytes - c) / 4), s) != hipSuccess) return QGEMM_ERR_HIP;
+    c = P.slot_bytes;
+  }
+  uint8_t* tables = base + (kScratch - P.table_bytes);
+  c = std::min(c, kScratch - P.table_bytes);
+  if ((st = upload_tables(P, tables, s)) != QGEMM_OK) return st;
+  return launch_plan(P, tables, base, s);
 }
 
 // verify head workspace: the sweep's, then one argmax key per row

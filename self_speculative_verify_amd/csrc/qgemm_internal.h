@@ -29,6 +29,7 @@ inline __host__ __device__ constexpr bool valid_fmt(int f) {
 inline __host__ __device__ constexpr int fmt_group(int f) { return f == kFmtG64 ? 64 : kGroup; }
 
 constexpr int kMaxInline = 12;       // jobs passed by value in the kernel arguments
+constexpr int kMaxDevices = 64;      // devices the allocation-free sweep keeps a scratch address for
 constexpr int kXRowBytes = 272;      // LDS row stride of a staged X chunk (256 + 16 pad)
 
 // stream kernel (panels of at most 16 rows): waves per workgroup, and the

@@ -14,9 +14,40 @@
 // the mantissa of 1024.0 and subtracting 1024 + bias gives q exactly); every
 // product q * x is exact in fp32 and each group's partial sum is scaled by
 // its own fp32 scale.  Rounding a dequantized q*s to fp16 would not be exact.
+#include <mutex>
+
+#include "qgemm.h"
 #include "sweep_device.h"
 
 namespace qg {
+
+// Scratch of the allocation-free sweep: one static array, which every GPU
+// the library runs on holds (at its own address) until the process ends.  In
+// host code `scratch` names a host-side stand-in, not device memory: only the
+// address fetched per device below is ever passed to a kernel or a copy.
+static __device__ __align__(256) uint8_t scratch[QGEMM_NOALLOC_SCRATCH_BYTES];
+
+// The current device's copy of the scratch array (and its size): its
+// address is fetched once per device, with that device current, and kept.
+hipError_t scratch_base(uint8_t** base, size_t* bytes) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *base = (uint8_t*)addr[dev];
+  *bytes = sizeof(scratch);
+  return hipSuccess;
+}
 
 // --------------------------------------------------------------------------
 // pack

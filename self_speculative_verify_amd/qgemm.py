@@ -25,8 +25,9 @@ EXPORTS = (
     "qgemm_sweep", "qgemm_sweep_path", "qgemm_validate", "qgemm_auto_path",
     "qgemm_status_string", "qgemm_verify_workspace_bytes", "qgemm_verify_head",
     "qgemm_round_workspace_bytes", "qgemm_round_create", "qgemm_round_launch", "qgemm_round_kernels",
-    "qgemm_round_destroy", "qgemm_attn_workspace_bytes", "qgemm_attn_verify",
+    "qgemm_round_destroy", "qgemm_attn_workspace_bytes", "qgemm_attn_verify", "qgemm_sweep_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 64 << 20
 KV_FP16, KV_FP8 = 0, 1
 ATTN_HKV, ATTN_GROUP, ATTN_D, ATTN_MAX_W, ATTN_MAX_SLOTS = 4, 6, 256, 16, 16
 MAX_SLOTS = 64
@@ -92,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.qgemm_sweep.restype = ci
         L.qgemm_sweep_path.argtypes = [jp, ci, ci, vp, sz, vp]
         L.qgemm_sweep_path.restype = ci
+        L.qgemm_sweep_noalloc.argtypes = [jp, ci, ci, vp]
+        L.qgemm_sweep_noalloc.restype = ci
         L.qgemm_validate.argtypes = [jp, ci, ci, vp, sz]
         L.qgemm_validate.restype = ci
         L.qgemm_auto_path.argtypes = [ci]
@@ -204,6 +207,20 @@ def sweep(jobs, workspace: Workspace, path: int = PATH_AUTO, stream=None) -> Non
     arr = job_array(jobs)
     _check(lib().qgemm_sweep_path(arr, len(jobs), path, workspace.ptr, workspace.nbytes,
                                   _stream_ptr(stream)), "qgemm_sweep_path")
+
+
+def sweep_noalloc(jobs, path: int = PATH_AUTO, stream=None) -> None:
+    """As ``sweep`` on the library's static per-device scratch (no workspace,
+    no device allocation); job sets needing more than NOALLOC_SCRATCH_BYTES
+    are refused."""
+    arr = job_array(jobs)
+    st = lib().qgemm_sweep_noalloc(arr, len(jobs), path, _stream_ptr(stream))
+    if st == ERR_INVALID_ARG:
+        need = workspace_bytes(jobs, path)
+        if need > NOALLOC_SCRATCH_BYTES:
+            raise QgemmError(st, f"qgemm_sweep_noalloc (the jobs need {need} bytes of scratch, more "
+                                 f"than the {NOALLOC_SCRATCH_BYTES} of the static scratch)")
+    _check(st, "qgemm_sweep_noalloc")
 
 
 def validate(jobs, path: int = PATH_AUTO, workspace_ptr: int = 0, ws_bytes: int = 0) -> int:

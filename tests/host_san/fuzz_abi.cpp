@@ -16,6 +16,7 @@
 
 extern long g_launches;
 extern long g_big_launches;
+extern size_t g_scratch_bytes;
 
 #define EXPECT(c)                                                                         \
   do {                                                                                    \
@@ -134,6 +135,52 @@ void sweep_case() {
     EXPECT(qgemm_sweep_path(bad.data(), (int)bad.size(), path, ws, wsb, nullptr) == QGEMM_ERR_INVALID_ARG);
   }
   broken_sweep(jobs, path, ws, wsb);
+}
+
+// Allocation-free sweeps: a few job sets in a row on the shared scratch (the
+// stand-in kernels check that every launch finds its slots empty).  A set
+// whose workspace exceeds the scratch is rejected before any launch.
+void noalloc_case() {
+  for (int i = 0, n = (int)rnd(2, 4); i < n; i++) {
+    const int path = (int)rnd(0, 2);
+    std::vector<qgemm_job> jobs = make_jobs(path);
+    const size_t wsb = qgemm_workspace_bytes(jobs.data(), (int)jobs.size(), path);
+    EXPECT(wsb > 0);
+    const long before = g_launches;
+    g_calls++;
+    if (wsb <= g_scratch_bytes) {
+      EXPECT(qgemm_sweep_noalloc(jobs.data(), (int)jobs.size(), path, nullptr) == QGEMM_OK);
+      EXPECT(g_launches > before);
+    } else {
+      EXPECT(qgemm_sweep_noalloc(jobs.data(), (int)jobs.size(), path, nullptr) == QGEMM_ERR_INVALID_ARG);
+      EXPECT(g_launches == before);
+    }
+  }
+  // 13..40 panel-class jobs (group kernel: a job table at the top of the
+  // scratch, no slots), then one sweep whose slots fill the whole scratch:
+  // it must clear what the table left there
+  std::vector<qgemm_job> many;
+  for (int i = 0, n = (int)rnd(13, 40); i < n; i++) many.push_back(make_job((int)rnd(17, QGEMM_MAX_M)));
+  EXPECT(qgemm_sweep_noalloc(many.data(), (int)many.size(), QGEMM_PATH_AUTO, nullptr) == QGEMM_OK);
+  qgemm_job full;
+  std::memset(&full, 0, sizeof(full));
+  full.bits = QGEMM_FMT_Q4;
+  full.N = 64;       // one row group of 157 k tiles: 1413 units, 128 waves
+  full.K = 157 * 128;
+  full.M = 1;
+  full.ldx = full.K;
+  full.ldy = 64;
+  full.packed = alloc(qgemm_packed_bytes(full.bits, full.N, full.K));
+  full.X = (const uint16_t*)alloc((size_t)full.K * 2);
+  full.Y = (float*)alloc((size_t)full.N * 4);
+  EXPECT(qgemm_workspace_bytes(&full, 1, QGEMM_PATH_MFMA) == g_scratch_bytes);
+  EXPECT(qgemm_sweep_noalloc(&full, 1, QGEMM_PATH_MFMA, nullptr) == QGEMM_OK);
+  // an argument error is rejected as by qgemm_sweep_path
+  std::vector<qgemm_job> jobs = make_jobs(QGEMM_PATH_AUTO);
+  jobs[0].M = 0;
+  const long before = g_launches;
+  EXPECT(qgemm_sweep_noalloc(jobs.data(), (int)jobs.size(), QGEMM_PATH_AUTO, nullptr) == QGEMM_ERR_INVALID_ARG);
+  EXPECT(g_launches == before);
 }
 
 // A launch of at least 4 GiB of weights (the stream kernel's big step
@@ -319,12 +366,13 @@ int main(int argc, char** argv) {
       free_all();
       continue;
     }
-    switch (rnd(0, 5)) {
+    switch (rnd(0, 6)) {
       case 0: case 1: sweep_case(); break;
       case 2: verify_case(); break;
       case 3: round_case(); break;
       case 4: attn_case(); break;
       case 5: pack_case(); break;
+      case 6: noalloc_case(); break;
     }
     free_all();
   }

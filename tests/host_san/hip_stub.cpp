@@ -25,6 +25,7 @@
 
 long g_launches = 0;      // kernels run or recorded, for the fuzz driver
 long g_big_launches = 0;  // of which sweeps with the big step shape
+size_t g_scratch_bytes = (size_t)256 << 10;  // the stand-in scratch of the allocation-free sweep
 
 #define CHECK(c)                                                                    \
   do {                                                                              \
@@ -193,6 +194,12 @@ void sweep_footprint(int kind, int cls, int fs, int rows, const qg::SweepArgs a,
     CHECK(a.spin_limit > 0);
     CHECK(a.slot_bytes == qg::stream_slot_bytes(a.nwaves, R, kind == 1, cls));
     span_w(a.slots, (size_t)a.slot_bytes);
+    // the kernels read a non-zero slot word as a written partial: every slot
+    // is empty (zero) when a launch starts
+    {
+      const uint32_t* w = (const uint32_t*)a.slots;
+      for (int64_t i = 0; i < a.slot_bytes / 4; i++) CHECK(w[i] == 0u);
+    }
     if (a.index) {
       // uend of every job, then the job holding the first unit of each bucket
       const int64_t nb = ((int64_t)a.total >> a.bshift) + 1;
@@ -227,6 +234,21 @@ hipError_t launch_pack(const float* W, int64_t ldw, int N, int K, int bits, void
     std::memset(packed, 0, pb);  // every byte, padding included
     span_w(flag, sizeof(unsigned));
   });
+  return hipSuccess;
+}
+
+// The allocation-free sweep's scratch: host memory that starts out non-zero
+// (the library may assume nothing about it before its first call), and far
+// smaller than the device's, so that the fuzz driver's job sets fill it and
+// a sweep's slots often reach bytes an earlier sweep's job tables wrote.
+hipError_t scratch_base(uint8_t** base, size_t* bytes) {
+  static uint8_t* buf = [] {
+    uint8_t* b = (uint8_t*)std::aligned_alloc(256, g_scratch_bytes);
+    std::memset(b, 0xA5, g_scratch_bytes);
+    return b;
+  }();
+  *base = buf;
+  *bytes = g_scratch_bytes;
   return hipSuccess;
 }
 

@@ -124,6 +124,23 @@ def test_workspace_sized_by_accumulators():
     assert ws(2, qgemm.PATH_GEMV) > ws(1, qgemm.PATH_GEMV) > 0
 
 
+def test_noalloc_rejects_before_any_hip_call():
+    """The allocation-free sweep refuses argument errors and job sets whose
+    workspace exceeds its static scratch on the host, before any HIP call
+    (this runs without a GPU)."""
+    L = qgemm.lib()
+    bad = qgemm.job_array([_job(M=0)])
+    assert L.qgemm_sweep_noalloc(bad, 1, qgemm.PATH_AUTO, None) == qgemm.ERR_INVALID_ARG
+    # five launches of at least 4 GiB of weights each (classes 1..16): their
+    # slots alone exceed the scratch
+    N, K = 120000, 65536
+    jobs = [_job(packed=(2 + 2 * i) << 32, X=(20 + i) << 32, Y=(30 + i) << 32, N=N, K=K, ldx=K,
+                 ldy=N, M=M) for i, M in enumerate((1, 2, 4, 8, 16))]
+    assert qgemm.packed_bytes(4, N, K) >= 4 << 30
+    assert qgemm.workspace_bytes(jobs, qgemm.PATH_MFMA) > qgemm.NOALLOC_SCRATCH_BYTES
+    assert L.qgemm_sweep_noalloc(qgemm.job_array(jobs), 5, qgemm.PATH_MFMA, None) == qgemm.ERR_INVALID_ARG
+
+
 def test_validation_rejects_workspace_overlap():
     """The workspace is written: it may overlap no job's X, weights or Y."""
     a = _job()

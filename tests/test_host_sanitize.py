@@ -4,7 +4,8 @@ UndefinedBehaviorSanitizer (CPU only).
 tests/host_san/ holds two randomized drivers:
   * fuzz_abi: the C boundary (sweeps of 1..40 jobs of every format and path,
     launches of more than 4 GiB of weights, which take the stream kernel's
-    big step shape, the verify head, round replay, attention verify, pack)
+    big step shape, allocation-free sweeps in a row on the shared scratch,
+    the verify head, round replay, attention verify, pack)
     built from the
     library's own host sources, with the HIP runtime and the kernel launchers
     replaced by host stand-ins that touch every region each kernel would
