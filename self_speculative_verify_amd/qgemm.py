@@ -230,11 +230,13 @@ def validate(jobs, path: int = PATH_AUTO, workspace_ptr: int = 0, ws_bytes: int 
 
 def sweep_one(packed, bits: int, N: int, K: int, X, M: int, Y=None, path: int = PATH_AUTO,
               stream=None):
-    """Convenience: one matrix, fresh workspace, returns Y fp32 [M, N]."""
+    """Convenience: one matrix, fresh workspace, returns Y fp32 [M, N] (a view
+    of rows padded to a multiple of four floats, the row stride the sweep
+    requires, when no Y is given)."""
     import torch
 
     if Y is None:
-        Y = torch.empty((M, N), dtype=torch.float32, device=packed.device)
+        Y = torch.empty((M, (N + 3) // 4 * 4), dtype=torch.float32, device=packed.device)[:, :N]
     job = make_job(packed, bits, N, K, X, Y, M)
     ws = Workspace(workspace_bytes([job], path), device=packed.device, stream=stream)
     sweep([job], ws, path, stream)
