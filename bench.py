@@ -3,17 +3,22 @@
 A step is one qgemm_sweep call over the whole workload (every matrix of it,
 one launch), with weights, activations and outputs already resident in HBM.
 The headline line is the gate+up projection (34816 x 5120, 4-bit group-32,
-M = 1, single-stream decode); the same run also times the M = 6 verify
-workload (gate+up 4-bit + down 5-bit) and the full 64-layer 27B-class stack at
-M = 48 (8 slots x 6 tokens), reported in the same JSON line.
+M = 1, single-stream decode); the same run times every other workload and
+reports it in the same JSON line: the 1024 x 1024 layer (latency), the M = 6
+verify workload (gate+up 4-bit + down 5-bit), the 64-layer 27B-class 4-bit
+stack at M = 48 (8 slots x 6 tokens) and the 5-bit stack at every M of its
+sweep, each with its roofline time (the larger of the HBM and the MFMA
+term).  Workloads 2 and 3 also get the read ceiling of their launch (the
+same loads with the same geometry and nothing else, libqgemm_ceiling) and
+the sweep's fraction of it.  Then the CPU oracle on the same workloads.
 
 Weight GB/s counts code and scale bytes (bits/8 per weight + 2 bytes per 32);
 tokens/s per sweep is M / step time.  The workloads that fit in the 256 MB
 last-level cache rotate over enough packed copies (>= 1 GB) that every step
 streams its weights from HBM.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only 2|3|4|5|6|7|8|9|10]
-       [--no-cpu] [--stack-layers L]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only 1|2|3|4|5|6|7|8|9|10]
+       [--no-cpu] [--stack-layers L] [--ceiling] [--timeline]
        python bench.py --copy-calib MIB   (a plain device copy of MIB MiB, the
        reference for scaling the HBM byte counters)
 """
@@ -29,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA, MI355X
 
 # HBM bytes per launch of the headline sweep kernel, from rocprofv3 FETCH_SIZE
 # and WRITE_SIZE runs scaled by the same counters on a plain copy (profiles/
@@ -179,6 +185,10 @@ class Bench:
         s = ms / 1e3
         gbps = self.weight_bytes / s / 1e9
         alg = self.weight_bytes + self.xbytes + self.ybytes
+        # roofline time: the larger of the HBM term (algorithmic bytes) and
+        # the dense fp16 MFMA term (2 M N K flops)
+        flops = sum(2 * self.M * m.N * m.K for m in self.wl.matrices)
+        t_hbm, t_mfma = alg / (HBM_PEAK_GBPS * 1e9), flops / (MFMA_F16_PEAK_TFLOPS * 1e12)
         return {
             "workload": self.wl.name,
             "M": self.M,
@@ -191,7 +201,57 @@ class Bench:
             "alg_GBps": round(alg / s / 1e9, 1),
             "weight_bytes": self.weight_bytes,
             "rotated_copies": len(self.copies),
+            "roofline": {"bound": "hbm" if t_hbm >= t_mfma else "mfma",
+                         "ms": round(max(t_hbm, t_mfma) * 1e3, 5),
+                         "frac": round(max(t_hbm, t_mfma) / s, 4)},
         }
+
+
+def ceiling(b, steps, warmup):
+    """The read ceiling of the sweep launch of Bench b (a stream-kernel launch,
+    M <= 16): libqgemm_ceiling's kernel over the same rotated weight copies and
+    X panels, with the sweep's wave count.  Returns its time per launch."""
+    import ctypes
+
+    import torch
+
+    import __graft_entry__
+
+    __graft_entry__.ensure_built("qgemm_ceiling")
+    L = ctypes.CDLL(__graft_entry__.LIBS["qgemm_ceiling"])
+
+    class CJob(ctypes.Structure):
+        _fields_ = [("packed", ctypes.c_void_p), ("X", ctypes.c_void_p), ("N", ctypes.c_int64),
+                    ("K", ctypes.c_int64), ("ldx", ctypes.c_int64), ("bits", ctypes.c_int32)]
+
+    L.qgemm_read_ceiling.argtypes = [ctypes.POINTER(CJob), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    L.qgemm_read_ceiling.restype = ctypes.c_int
+    mats = b.wl.matrices
+    units = sum(-(-(-(-m.N // 16)) // 4) * (m.K // 128) * (11 if m.bits == 5 else 9) for m in mats)
+    nwaves = max(1, min(2048, units // 11))   # the stream kernels' wave count for these units
+    arrays = [(CJob * len(mats))(*[CJob(p.data_ptr(), b.X[m.K].data_ptr(), m.N, m.K, m.K, m.bits)
+                                   for p, m in zip(cp, mats)]) for cp in b.copies]
+    sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+    sp = torch.cuda.current_stream().cuda_stream
+
+    def launch(i):
+        a = arrays[i % len(arrays)]
+        if L.qgemm_read_ceiling(a, len(mats), nwaves, b.M, sink.data_ptr(), sp) != 0:
+            raise RuntimeError("qgemm_read_ceiling failed")
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        launch(warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"us": round(ms * 1e3, 3), "weight_GBps": round(b.weight_bytes / (ms / 1e3) / 1e9, 1),
+            "waves": nwaves}
 
 
 def round_bench(args):
@@ -404,31 +464,128 @@ def timeline(args):
     L.qgemm_timeline_set(None)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def _timed(fn, min_s=0.5, max_reps=50):
+    """Seconds per call of fn: one call, repeated while under min_s in total."""
+    t0 = time.perf_counter()
+    fn()
+    reps = 1
+    while time.perf_counter() - t0 < min_s and reps < max_reps:
+        fn()
+        reps += 1
+    return (time.perf_counter() - t0) / reps
+
+
+def _sampled_rows(m, step):
+    """Every step-th 16-row block of matrix m (generation is seeded per row, so
+    the rows are the matrix's own); returns (W rows, number of blocks)."""
+    import numpy as np
+
+    from synth import synth, workloads
+
+    nrb = -(-m.N // 16)
+    blocks = list(range(0, nrb, step))
+    W = np.concatenate([synth.weights(m.seed, m.K, 16 * b, min(16, m.N - 16 * b), workloads.SIGMA,
+                                      outlier_thresh=m.thresh, outlier_mult=workloads.OUTLIER_MULT)
+                        for b in blocks])
+    return W, len(blocks), nrb
+
+
 def cpu_baseline():
-    """The oracle, untuned, on the host cores: the full M = 1 sweep of the
-    34816 x 5120 4-bit gate+up matrix (generation and packing untimed)."""
+    """The oracle (oracle.sweep: plain C, fp64, scalar decode from the packed
+    bytes), untuned, on the host cores this process may use; generation and
+    packing untimed.  Workloads 1-3 in full on every core, plus one thread
+    (workload 1 in full, 2 and 3 on a 1/4 and 1/16 sample of row blocks);
+    the 64-layer stacks (workloads 4 and 5) on a 1/16 sample of the row
+    blocks of layer 0's four matrices, at M = 1 and at every M the GPU line
+    reports, scaled by 16 x 64: the sweep is independent per output column,
+    so its work is linear in the rows swept and the same in every layer."""
+    import numpy as np
+
     from oracle import oracle
     from synth import synth, workloads
 
-    wl = workloads.workload(2)
-    m = wl.matrices[0]
-    W = synth.weights(m.seed, m.K, 0, m.N, workloads.SIGMA)
-    packed = oracle.quantize_pack(W, m.bits)
-    del W
-    X = synth.x_fp16(wl.x_seed(m.K), 1, m.K)
-    threads = oracle._threads(None)
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        oracle.sweep(packed, m.N, m.K, m.bits, X, nthreads=threads)
-        reps += 1
-        if time.perf_counter() - t0 > 10.0 or reps >= 20:
-            break
-    dt = (time.perf_counter() - t0) / reps
-    wb = workloads.weight_bytes(m.bits, m.N, m.K)
-    return {"value": round(wb / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"full M=1 sweep of the 34816x5120 4-bit matrix, {reps} repetitions, "
-                      f"{dt * 1e3:.1f} ms each (fp64, scalar decode from the packed bytes)"}
+    threads = oracle.cpu_share()
+    per = {}
+
+    def entry(wl, M, t, scale, sample, one=None):
+        wb = sum(workloads.weight_bytes(m.bits, m.N, m.K) for m in wl.matrices)
+        full_s = t * scale
+        e = {"workload": wl.name, "M": M, "s_per_sweep": round(full_s, 4),
+             "weight_GBps": round(wb / full_s / 1e9, 4), "tokens_per_s": round(M / full_s, 3),
+             "threads": threads, "sample": sample}
+        if one is not None:
+            e["one_thread"] = one
+        return e
+
+    def x_of(wl, K, M):
+        return synth.x_fp16(wl.x_seed(K), M, K)
+
+    # workloads 1-3: every matrix in full on every core; one thread on a sample
+    for cfg, one_step in ((1, 1), (2, 4), (3, 16)):
+        wl = workloads.workload(cfg)
+        M = wl.Ms[0]
+        mats = []
+        for m in wl.matrices:
+            W = synth.weights(m.seed, m.K, 0, m.N, workloads.SIGMA)
+            mats.append((m, oracle.quantize_pack(W, m.bits), x_of(wl, m.K, M)))
+            del W
+        t_all = _timed(lambda: [oracle.sweep(p, m.N, m.K, m.bits, X, nthreads=threads) for m, p, X in mats])
+        samples = []
+        for m, p, X in mats:
+            nrb = -(-m.N // 16)
+            cols = np.concatenate([np.arange(16 * b, min(16 * b + 16, m.N)) for b in range(0, nrb, one_step)])
+            samples.append((m, p, X, cols, m.N / cols.size))
+        t_one = _timed(lambda: [oracle.sweep(p, m.N, m.K, m.bits, X, cols=c, nthreads=1)
+                                for m, p, X, c, _ in samples])
+        scale_one = samples[0][4]   # the same row-block fraction of every matrix
+        wb = sum(workloads.weight_bytes(m.bits, m.N, m.K) for m in wl.matrices)
+        one = {"s_per_sweep": round(t_one * scale_one, 4),
+               "weight_GBps": round(wb / (t_one * scale_one) / 1e9, 4),
+               "sample": "full" if one_step == 1 else f"every {one_step}th 16-row block, scaled x{scale_one:.2f}"}
+        per[str(cfg)] = entry(wl, M, t_all, 1.0, "full", one)
+        log(f"[bench] cpu baseline workload {cfg}: {json.dumps(per[str(cfg)])}")
+        del mats, samples
+
+    # the stacks: a 1/16 row-block sample of layer 0, scaled to 64 layers
+    for cfg, Ms in ((4, [1, 48]), (5, workloads.workload(5).Ms)):
+        wl = workloads.workload(cfg)
+        layer0 = wl.matrices[:4]
+        mats, scale = [], None
+        for m in layer0:
+            W, nb, nrb = _sampled_rows(m, 16)
+            mats.append((m, oracle.quantize_pack(W, m.bits), W.shape[0]))
+            scale = nrb / nb
+            del W
+        res = {}
+        for M in Ms:
+            Xs = {K: x_of(wl, K, M) for K in wl.distinct_K}
+            t = _timed(lambda: [oracle.sweep(p, n, m.K, m.bits, Xs[m.K], nthreads=threads) for m, p, n in mats],
+                       min_s=0.0, max_reps=1)
+            res[str(M)] = entry(wl, M, t, scale * (len(wl.matrices) // 4),
+                                f"every 16th 16-row block of layer 0's 4 matrices, scaled x{scale:.2f} x "
+                                f"{len(wl.matrices) // 4} layers")
+            log(f"[bench] cpu baseline workload {cfg} M={M}: {json.dumps(res[str(M)])}")
+        per[str(cfg)] = res
+
+    head = per["2"]
+    return {"value": head["weight_GBps"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "workload 2 (34816x5120 4-bit, M=1) swept in full on every core; per_config: "
+                      "workloads 1-3 in full plus one-thread figures, the 64-layer stacks on a 1/16 "
+                      "row-block sample of layer 0 scaled to the stack",
+            "cpu_model": cpu_model(), "one_thread": head["one_thread"], "per_config": per}
 
 
 def main():
@@ -437,7 +594,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", type=int, default=0,
-                    help="time one workload (2, 3 or 4) only; 5 times the 5-bit stack at every M of its "
+                    help="time one workload (1, 2, 3 or 4) only; 5 times the 5-bit stack at every M of its "
                          "sweep; 6 times the verify head; 7 and 8 the group-64 and zero-point 4-bit "
                          "stacks at M = 1, 8, 48; 9 a round of per-matrix sweeps plus the verify head, "
                          "issued call by call and replayed as one graph; 10 the attention verify")
@@ -446,6 +603,9 @@ def main():
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB")
     ap.add_argument("--timeline-dump", default="", metavar="DIR",
                     help="with --timeline: also save the raw stamps (numpy) under DIR")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="the read ceiling of the sweep launches of workloads 2 and 3 (same geometry, "
+                         "loads only) beside their sweep times")
     ap.add_argument("--timeline", action="store_true",
                     help="per-wave stamps of the stream kernel on workloads 2 and 3 (diagnostic build)")
     args = ap.parse_args()
@@ -519,23 +679,60 @@ def main():
             print(json.dumps(r), flush=True)
         return
 
-    results = {}
-    order = [args.only] if args.only else [2, 3, 4]
-    for cfg in order:
+    if args.ceiling:
+        for cfg in (2, 3):
+            b = Bench(cfg)
+            ms_sweep, _ = b.run(args.steps, args.warmup)
+            c = ceiling(b, args.steps, args.warmup)
+            c.update({"workload": b.wl.name, "M": b.M, "sweep_us": round(ms_sweep * 1e3, 3),
+                      "sweep_frac_of_ceiling": round(c["us"] / (ms_sweep * 1e3), 4)})
+            print(json.dumps(c), flush=True)
+            del b
+            torch.cuda.empty_cache()
+        return
+
+    if args.only in (1, 2, 3, 4):
+        b = Bench(args.only, layers=args.stack_layers if args.only == 4 else None)
+        ms, wall = b.run(args.steps, args.warmup)
+        r = b.report(ms)
+        r["wall_s"] = round(wall, 4)
+        print(json.dumps(r), flush=True)
+        return
+
+    # the default line: every workload (1: latency; 2, 3: with their read
+    # ceiling; 4 at M = 48; 5 at every M of its sweep), then the oracle
+    configs = {}
+    for cfg in (2, 3, 1, 4, 5):
         log(f"[bench] workload {cfg}: building")
-        b = Bench(cfg, layers=args.stack_layers if cfg == 4 else None)
+        b = Bench(cfg, layers=args.stack_layers if cfg in (4, 5) else None)
         log(f"[bench] workload {cfg}: {len(b.wl.matrices)} matrices, {b.packed_bytes / 1e6:.1f} MB "
             f"packed x {len(b.copies)} copies; timing {args.steps} steps")
-        ms, wall = b.run(args.steps, args.warmup)
-        results[cfg] = b.report(ms)
-        results[cfg]["wall_s"] = round(wall, 4)
-        log(f"[bench] workload {cfg}: {json.dumps(results[cfg])}")
+        if cfg == 5:
+            configs["5"] = {}
+            for M in b.wl.Ms:
+                b.set_M(M)
+                ms, wall = b.run(args.steps, args.warmup)
+                configs["5"][str(M)] = b.report(ms)
+                log(f"[bench] workload 5 M={M}: {json.dumps(configs['5'][str(M)])}")
+        else:
+            ms, wall = b.run(args.steps, args.warmup)
+            r = b.report(ms)
+            r["wall_s"] = round(wall, 4)
+            if cfg in (2, 3):
+                c = ceiling(b, args.steps, args.warmup)
+                c["sweep_frac_of_ceiling"] = round(c["us"] / (ms * 1e3), 4)
+                r["read_ceiling"] = c
+            if cfg == 1:
+                r["us_per_sweep"] = round(ms * 1e3, 3)
+            configs[str(cfg)] = r
+            log(f"[bench] workload {cfg}: {json.dumps(r)}")
         del b
         torch.cuda.empty_cache()
 
-    head = results[order[0]]
-    # dominant kernel: one sweep launch per step, so the event time per step is
-    # the kernel's average duration (launch gaps included)
+    head = configs["2"]
+    # dominant kernel: the headline sweep is one stream-kernel launch per
+    # step, timed with events on the stream it is launched on, so the event
+    # time per step is the kernel's average duration (launch gaps included)
     roof = {
         "bound": "hbm",
         "achieved": head["alg_GBps"],
@@ -560,13 +757,11 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": head["workload"], "M": head["M"],
-                   "matrices": head["matrices"]},
+        "config": {"workload": head["workload"], "M": head["M"], "matrices": head["matrices"]},
         "hbm_frac": head["hbm_frac"],
+        "read_ceiling_frac": head["read_ceiling"]["sweep_frac_of_ceiling"],
         "tokens_per_s": head["tokens_per_s"],
-        "per_M": {str(r["M"]): {k: r[k] for k in ("workload", "ms_per_sweep", "weight_GBps",
-                                                   "hbm_frac", "tokens_per_s")}
-                  for r in results.values()},
+        "configs": configs,
         "roofline": roof,
     }
     if not args.no_cpu:

@@ -92,14 +92,34 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def _threads(n):
-    if n:
-        return int(n)
+def cpu_share() -> int:
+    """Host cores this process may use: the CPUs it may run on, capped by its
+    cgroup's CPU quota when one is set (a container can see every core of the
+    machine but be entitled to fewer)."""
     try:
         c = len(os.sched_getaffinity(0))
     except (AttributeError, OSError):
         c = os.cpu_count() or 1
-    return max(1, min(c, 16))
+    for path in ("/sys/fs/cgroup/cpu.max", "/sys/fs/cgroup/cpu/cpu.cfs_quota_us"):
+        try:
+            with open(path) as fh:
+                parts = fh.read().split()
+        except OSError:
+            continue
+        if path.endswith("cpu.max"):
+            if parts and parts[0] != "max":
+                c = min(c, max(1, -(-int(parts[0]) // int(parts[1]))))
+        else:
+            quota = int(parts[0]) if parts else -1
+            if quota > 0:
+                with open("/sys/fs/cgroup/cpu/cpu.cfs_period_us") as fh:
+                    c = min(c, max(1, -(-quota // int(fh.read().split()[0]))))
+        break
+    return max(1, c)
+
+
+def _threads(n):
+    return int(n) if n else cpu_share()
 
 
 class NonFiniteError(ValueError):

@@ -33,6 +33,31 @@ def test_exports_match_header():
         assert hasattr(L, n), n
 
 
+def test_ceiling_library_loads_and_rejects_bad_arguments():
+    """The read-ceiling measurement library (bench.py) exports its one entry
+    point and refuses bad arguments before any HIP call."""
+    __graft_entry__.ensure_built("qgemm_ceiling")
+    L = ctypes.CDLL(__graft_entry__.LIBS["qgemm_ceiling"])
+    fn = L.qgemm_read_ceiling
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+
+    class CJob(ctypes.Structure):
+        _fields_ = [("packed", ctypes.c_void_p), ("X", ctypes.c_void_p), ("N", ctypes.c_int64),
+                    ("K", ctypes.c_int64), ("ldx", ctypes.c_int64), ("bits", ctypes.c_int32)]
+
+    ok = dict(packed=0x100000, X=0x200000, N=34816, K=5120, ldx=5120, bits=4)
+    for kw in (dict(bits=3), dict(K=5120 - 32), dict(ldx=4096), dict(packed=0), dict(N=0)):
+        j = CJob(**{**ok, **kw})
+        assert fn(ctypes.byref(j), 1, 2048, 1, 0x300000, None) == 1, kw
+    j = CJob(**ok)
+    assert fn(ctypes.byref(j), 1, 2048, 1, None, None) == 1           # no sink
+    assert fn(ctypes.byref(j), 1, 2048, 17, 0x300000, None) == 1      # more than 16 rows
+    assert fn(ctypes.byref(j), 0, 2048, 1, 0x300000, None) == 1       # no job
+    small = CJob(**{**ok, "N": 64, "K": 128, "ldx": 128})
+    assert fn(ctypes.byref(small), 1, 2048, 1, 0x300000, None) == 1   # under 11 units per wave
+
+
 def test_packed_bytes_agrees_with_oracle():
     for bits in (4, 5):
         for N, K in [(1, 32), (15, 96), (16, 128), (1024, 1024), (34816, 5120), (5120, 17408),
