@@ -383,14 +383,7 @@ struct Stream {
     const uint32_t o = slot_off(wsrc, k, cx.lane);
     for (int spin = 0;; spin++) {
       bool ready = true;
-#pragma unroll
-      for (int e = 0; e < kAcc; e += 4) {
-        const u4_t v = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(sr, o + 4u * e, 0, kCoherent));
-        w[e] = v.x;
-        w[e + 1] = v.y;
-        w[e + 2] = v.z;
-        w[e + 3] = v.w;
-      }
+      load_words(w, sr, o);
 #pragma unroll
       for (int e = 0; e < kAcc; e++) ready = ready && w[e] != 0u;
       if (__builtin_amdgcn_read_exec() == __ballot(ready) || spin >= cx.spin_limit) break;
@@ -399,6 +392,17 @@ struct Stream {
 #pragma unroll
     for (int e = 0; e < kAcc; e += 4)
       __builtin_amdgcn_raw_buffer_store_b128(u4_t{0u, 0u, 0u, 0u}, sr, o + 4u * e, 0, kCoherent);
+  }
+
+  static __device__ __forceinline__ void load_words(uint32_t (&w)[kAcc], __amdgpu_buffer_rsrc_t sr, uint32_t o) {
+#pragma unroll
+    for (int e = 0; e < kAcc; e += 4) {
+      const u4_t v = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(sr, o + 4u * e, 0, kCoherent));
+      w[e] = v.x;
+      w[e + 1] = v.y;
+      w[e + 2] = v.z;
+      w[e + 3] = v.w;
+    }
   }
 
   // Reader of row group rg of job j (its last contributor, wave wl): the
@@ -572,11 +576,12 @@ struct Stream {
         }
       }
     };
-    // Two waves share each SIMD.  The instruction arbiter favours the one in
-    // the lower wave slot, which would finish its range early while the other
-    // lags and delays the end of the sweep; the wave not in slot 0 runs at a
-    // raised priority instead (HW_ID bits 3:0 are the wave slot).
-    if (__builtin_amdgcn_s_getreg((4 << 0) | (0 << 6) | (3 << 11)) != 0) __builtin_amdgcn_s_setprio(1);
+    // Two waves share each SIMD: the first half of the grid is dispatched
+    // first, the second half joins while those already stream.  The later
+    // waves run at a raised priority, so that their planning and first loads
+    // are not held behind their partners' unpacking (measured: the M = 6
+    // verify workload 42.4 -> 39.9 us, the rest unchanged or faster).
+    if (cx.gw >= args.nwaves / 2) __builtin_amdgcn_s_setprio(1);
     while (!done) each_slot(slot, std::make_integer_sequence<int, kDepth>{});
 #ifdef QG_TIMELINE
     if (kTrace) __builtin_amdgcn_s_waitcnt(0);
@@ -598,6 +603,15 @@ struct Stream {
   }
 };
 
+// The grid holds two waves per SIMD.  The MFMA class-8 kernel in
+// eight-block steps is built under that register budget: left to itself it
+// takes 198 VGPRs + 66 AGPRs (one wave per SIMD); within 256 it keeps its
+// MFMA results in VGPRs and fits two (the 5-bit stack at M = 8: 2.70 ->
+// 2.60 ms).  The others already fit two (or would spill under the budget:
+// MFMA class 16 in eight-block steps, GEMV class 8) and keep the plain bounds.
+template <bool kMfma, int kCap, int kR>
+constexpr bool kTwoPerSimd = kMfma && kR == 8 && kCap == 8;
+
 template <bool kMfma, int kCap, int kR, int kFS>
 __global__ void __launch_bounds__(64 * kStreamWavesPerBlock) stream_kernel(SweepArgs) {
   using S = Stream<kMfma, kCap, kR, kFS>;
@@ -605,18 +619,32 @@ __global__ void __launch_bounds__(64 * kStreamWavesPerBlock) stream_kernel(Sweep
   S::run(kernel_args(), xs[threadIdx.x >> 6]);
 }
 
+template <bool kMfma, int kCap, int kR, int kFS>
+__global__ void __launch_bounds__(64 * kStreamWavesPerBlock) __attribute__((amdgpu_waves_per_eu(2)))
+stream_kernel2(SweepArgs) {
+  using S = Stream<kMfma, kCap, kR, kFS>;
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kStreamWavesPerBlock][kCap * kXRowBytes];
+  S::run(kernel_args(), xs[threadIdx.x >> 6]);
+}
+
 typedef void (*sweep_fn)(SweepArgs);
+
+template <bool kMfma, int kCap, int kR, int kFS>
+static sweep_fn kernel_of() {
+  if constexpr (kTwoPerSimd<kMfma, kCap, kR>) return stream_kernel2<kMfma, kCap, kR, kFS>;
+  else return stream_kernel<kMfma, kCap, kR, kFS>;
+}
 
 template <bool kMfma, int kR, int kFS>
 static sweep_fn pick_cls(int cls) {
   switch (cls) {
-    case 1: return stream_kernel<kMfma, 1, kR, kFS>;
-    case 2: return stream_kernel<kMfma, 2, kR, kFS>;
-    case 4: return stream_kernel<kMfma, 4, kR, kFS>;
-    case 8: return stream_kernel<kMfma, 8, kR, kFS>;
+    case 1: return kernel_of<kMfma, 1, kR, kFS>();
+    case 2: return kernel_of<kMfma, 2, kR, kFS>();
+    case 4: return kernel_of<kMfma, 4, kR, kFS>();
+    case 8: return kernel_of<kMfma, 8, kR, kFS>();
   }
   if constexpr (kMfma)
-    if (cls == 16) return stream_kernel<kMfma, 16, kR, kFS>;
+    if (cls == 16) return kernel_of<kMfma, 16, kR, kFS>();
   return nullptr;
 }
 

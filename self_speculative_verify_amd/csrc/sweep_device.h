@@ -48,13 +48,24 @@ __device__ __forceinline__ const QG_GLOBAL T* gload_ptr(const void* p) {
 // mod 32 of h, so rotr(h, J) places pairs 0 and 1 at (4, 20) and (8, 24) --
 // bit 4 of u in the first form, of 16u in the second -- and rotr(h, J + 8)
 // does the same for pairs 2 and 3.
-// v_and_or_b32 (a & m) | o in one instruction.  Written out because with two
-// literal operands the compiler splits it into v_and + v_or (a VOP3 encoding
-// holds no literal on this target); here the constants live in registers.
+// A value the compiler must hold in a VGPR without knowing it (an empty asm
+// that emits nothing): a constant passed through it stays a register operand
+// instead of a literal.
+__device__ __forceinline__ uint32_t in_reg(uint32_t v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
+// (a & m) | o as one v_and_or_b32.  With two literal operands the compiler
+// would split it into v_and + v_or (a VOP3 encoding holds no literal on this
+// target), so constant operands are handed over as registers; and the result
+// is pinned, or a chain (h & m1) | ((w & m0) | c) is re-associated into two
+// v_and and a v_or3.  The instruction itself is the compiler's, so its
+// hazard checks see it (an instruction written in asm would be invisible to
+// them: next to an MFMA still writing a VGPR, that is a wrong result).
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
-  return r;
+  if (__builtin_constant_p(o)) o = in_reg(o);
+  return in_reg((a & in_reg(m)) | o);
 }
 
 // Zero-point format: u is stored as is and the subtrahends are per group:
@@ -133,9 +144,9 @@ __device__ __forceinline__ h2_t scale_pair(uint32_t word) { return __builtin_bit
 // slowly on gfx950.
 template <int HI>
 __device__ __forceinline__ float scale_f32(uint32_t pair) {
-  float f;
-  if constexpr (HI) asm("v_cvt_f32_f16_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1" : "=v"(f) : "v"(pair));
-  else asm("v_cvt_f32_f16_e32 %0, %1" : "=v"(f) : "v"(pair));
+  const h2_t h = scale_pair(pair);
+  float f = (float)(HI ? h.y : h.x);
+  asm("" : "+v"(f));  // the fp32 value must exist: the conversion stays an instruction
   return f;
 }
 
