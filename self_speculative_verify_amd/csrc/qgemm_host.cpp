@@ -170,11 +170,12 @@ int class_of(int kind, int M) {
 
 int cu_count();
 
-// Waves of a stream launch: kStreamWaves, but never more than
-// T / kMaxUnitWeight, so that every wave holds at least one step.  Depends on
-// the shapes only, never on M.
-int64_t stream_waves(int64_t T) {
-  return std::max<int64_t>(1, std::min<int64_t>(qg::kStreamWaves, T / qg::kMaxUnitWeight));
+// Waves of a stream launch: kStreamWaves (kStreamWavesBig for a big launch),
+// but never more than T / kMaxUnitWeight, so that every wave holds at least
+// one step.  Depends on the shapes only, never on M.
+int64_t stream_waves(int64_t T, bool big) {
+  return std::max<int64_t>(1, std::min<int64_t>(big ? qg::kStreamWavesBig : qg::kStreamWaves,
+                                                T / qg::kMaxUnitWeight));
 }
 
 Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* keys = nullptr) {
@@ -273,7 +274,7 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* k
       off = round_up(off + l.descs.size() * sizeof(JobDesc) + l.index.size() * sizeof(int32_t), 256);
     }
     if (l.kind != kGroupMfma) {
-      l.nwaves = (int)stream_waves(l.total);
+      l.nwaves = (int)stream_waves(l.total, l.big);
       l.slots_off = soff;
       soff = round_up(soff + (size_t)qg::stream_slot_bytes(l.nwaves, l.rows, l.kind == kStreamMfma, l.cls), 256);
     }

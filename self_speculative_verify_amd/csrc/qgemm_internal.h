@@ -39,8 +39,14 @@ constexpr int kXRowBytes = 272;      // LDS row stride of a staged X chunk (256 
 // (the unpack is VALU-bound) the other's loads are in flight.  A launch of at
 // least kStreamBigBytes of weights is "big": on the MFMA path its steps span
 // twice the row blocks (one X chunk serves eight weight tiles instead of four).
+// A big launch takes three workgroups per CU (3072 waves, 1.5 times what
+// is resident at two waves per SIMD): each CU's third workgroup starts when
+// one of its first two ends, which evens out the end of the sweep (measured
+// on the 5-bit stack, M = 1: 2.37 -> 2.27 ms; counts that do not give every
+// CU the same number of workgroups, or give two full rounds, are slower).
 constexpr int kStreamWavesPerBlock = 4;
 constexpr int kStreamWaves = 2048;
+constexpr int kStreamWavesBig = 3072;
 constexpr int64_t kStreamBigBytes = (int64_t)4 << 30;
 // group kernel (17..64 rows): waves per workgroup (three per SIMD where the
 // registers allow it: padded rows 32 and 48), 16-row blocks per wave
