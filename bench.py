@@ -35,17 +35,24 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA, MI355X
+PATHS = {"auto": 0, "gemv": 1, "mfma": 2}
 
 # HBM bytes per launch of the headline sweep kernel, from rocprofv3 FETCH_SIZE
 # and WRITE_SIZE runs scaled by the same counters on a plain copy (profiles/
 # has the commands and raw figures).  Valid only for the kernel sources they
 # were taken on: keyed by the SHA-256 of those sources, else reported as null.
 TRAFFIC = {
-    "7bae38b990ba5c01": {"workload": "gate+up 5120->34816 4-bit M=1", "bytes": 101789833},
+    # FETCH_SIZE 50187.3 KiB x 2.0000 (a 1 GiB device copy reads 524300 KiB)
+    # + WRITE_SIZE 4018 KiB x 1.0 (the copy writes 1048576 KiB)
+    "78d1132c0b07ce2d": {"workload": "gate+up 5120->34816 4-bit M=1", "bytes": 106893866},
 }
 KERNEL_SOURCES = ("self_speculative_verify_amd/csrc/qgemm_kernels.hip",
                   "self_speculative_verify_amd/csrc/qgemm_internal.h",
-                  "self_speculative_verify_amd/csrc/qgemm_host.cpp")
+                  "self_speculative_verify_amd/csrc/qgemm_host.cpp",
+                  "self_speculative_verify_amd/csrc/sweep_device.h",
+                  "self_speculative_verify_amd/csrc/stream_plan.h",
+                  "self_speculative_verify_amd/csrc/stream_impl.h",
+                  "self_speculative_verify_amd/csrc/stream_q4.hip")
 
 
 def kernel_sha():
@@ -71,6 +78,7 @@ class Bench:
         from synth import synth, workloads
 
         self.qgemm = qgemm
+        self.path = qgemm.PATH_AUTO
         self.wl = workloads.workload(cfg, layers) if layers else workloads.workload(cfg)
         self.M = M if M is not None else self.wl.Ms[0]
         dev = torch.device("cuda:0")
@@ -121,7 +129,7 @@ class Bench:
         self.Y = [torch.empty((M, m.N), dtype=torch.float32, device=dev) for m in self.wl.matrices]
         self.jobsets = [[q.make_job(p, m.bits, m.N, m.K, self.X[m.K], y, M)
                          for p, m, y in zip(cp, self.wl.matrices, self.Y)] for cp in self.copies]
-        ws = max(q.workspace_bytes(js) for js in self.jobsets)
+        ws = max(q.workspace_bytes(js, self.path) for js in self.jobsets)
         self.ws = q.Workspace(ws, device=dev)
         self.arrays = [q.job_array(js) for js in self.jobsets]
         self.xbytes = sum(2 * M * K for K in self.wl.distinct_K)
@@ -159,9 +167,9 @@ class Bench:
                 raise q.QgemmError(st, "qgemm_verify_head")
             return
         arr = self.arrays[i % len(self.arrays)]
-        st = q.lib().qgemm_sweep(arr, len(arr), self.ws.ptr, self.ws.nbytes, self.stream)
+        st = q.lib().qgemm_sweep_path(arr, len(arr), self.path, self.ws.ptr, self.ws.nbytes, self.stream)
         if st != q.OK:
-            raise q.QgemmError(st, "qgemm_sweep")
+            raise q.QgemmError(st, "qgemm_sweep_path")
 
     def run(self, steps, warmup):
         import torch
@@ -599,6 +607,9 @@ def main():
                          "stacks at M = 1, 8, 48; 9 a round of per-matrix sweeps plus the verify head, "
                          "issued call by call and replayed as one graph; 10 the attention verify")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--path", choices=sorted(PATHS), default="auto",
+                    help="with --only 1-5, 7, 8: the sweep path (gemv: panels of at most 8 rows)")
+    ap.add_argument("--Ms", default="", help="with --only 1-5, 7, 8: comma-separated panel heights to time")
     ap.add_argument("--stack-layers", type=int, default=64)
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB")
     ap.add_argument("--timeline-dump", default="", metavar="DIR",
@@ -671,7 +682,8 @@ def main():
         # of its sweep (same weights, fresh panels); one JSON line per M, no
         # headline
         b = Bench(args.only, layers=args.stack_layers)
-        for M in b.wl.Ms:
+        b.path = PATHS[args.path]
+        for M in ([int(m) for m in args.Ms.split(",")] if args.Ms else b.wl.Ms):
             b.set_M(M)
             ms, wall = b.run(args.steps, args.warmup)
             r = b.report(ms)
@@ -693,10 +705,14 @@ def main():
 
     if args.only in (1, 2, 3, 4):
         b = Bench(args.only, layers=args.stack_layers if args.only == 4 else None)
-        ms, wall = b.run(args.steps, args.warmup)
-        r = b.report(ms)
-        r["wall_s"] = round(wall, 4)
-        print(json.dumps(r), flush=True)
+        b.path = PATHS[args.path]
+        for M in ([int(m) for m in args.Ms.split(",")] if args.Ms else [b.M]):
+            b.set_M(M)
+            ms, wall = b.run(args.steps, args.warmup)
+            r = b.report(ms)
+            r["wall_s"] = round(wall, 4)
+            r["path"] = args.path
+            print(json.dumps(r), flush=True)
         return
 
     # the default line: every workload (1: latency; 2, 3: with their read

@@ -8,9 +8,9 @@
 // as the weight sweep's panel rows share one weight read.
 //
 // attn_partial: one workgroup per (slot, KV head, chunk of positions), one
-// wave per 16-row block of queries.  Per step of 32 positions the keys (as
-// [position][dim]) and the values (transposed, [dim][position]) go through
-// LDS, widened to binary16 when the cache is E4M3 (exactly, by the hardware
+// wave per 16-row block of queries.  Per step of 32 positions the keys and
+// the values go through LDS as they lie in the cache ([position][dim]),
+// widened to binary16 when the cache is E4M3 (exactly, by the hardware
 // conversion).  Scores are computed transposed, S^T = K Q^T, with
 // v_mfma_f32_16x16x32_f16 (A = 16 positions x 32 dims of K, B = 32 dims x
 // 16 query rows of Q), so lane l
@@ -19,7 +19,8 @@
 // maximum per row (base-2 units) and a per-lane partial sum; the
 // probabilities, rounded to binary16, are then exactly the B operand of the
 // value product O^T += V^T P^T (A = 16 dims x those 8 positions of V, read
-// from the transposed tile), whose accumulator again holds row l % 16 in
+// transposed out of the row-major tile by gfx950's transposing LDS read,
+// ds_read_b64_tr_b16), whose accumulator again holds row l % 16 in
 // lane l, so the rescaling by exp2(m_old - m_new) is one multiply per value.
 // Each chunk leaves its unnormalized output, maximum and sum in the
 // workspace; attn_combine merges the chunks of every row.
