@@ -232,6 +232,7 @@ Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* k
     d.M = j.M;
     d.fmt = j.bits;
     d.nkt = (int32_t)nkt_of(j.K);
+    qg::div_magic((uint32_t)d.nkt, d.nkt_m, d.nkt_sh);
     d.ngroups = (int32_t)(j.K / qg::kGroup);
     d.nrb = (int32_t)nrb_of(j.N);
     if (kind == kGroupMfma) {

@@ -67,10 +67,25 @@ inline __host__ __device__ constexpr int tile_bytes(int f) {
 // and every wave gets at least kMaxUnitWeight units, so every wave holds at
 // least one step.
 inline __host__ __device__ constexpr int unit_weight(int f) { return (tile_bytes(f) + kTileK / 2) / kTileK; }
+// x / unit_weight(f) for x >= 0, by constant divisors (the planning code's
+// divisions are on the path to a wave's first load)
+inline __host__ __device__ int div_unit_weight(int x, int f) {
+  return unit_weight(f) == 11 ? (int)((uint32_t)x / 11u) : (int)((uint32_t)x / 9u);
+}
+// Multiplier and shift of an exact division by d (1 <= d <= 2^17) for
+// dividends 0 <= s < 2^31 (Granlund and Montgomery, "Division by invariant
+// integers using multiplication", PLDI 1994): l = ceil(log2 d),
+// m = floor(2^(31 + l) / d) + 1 < 2^32, s / d = (s m) >> (31 + l).
+inline void div_magic(uint32_t d, uint32_t& m, int32_t& sh) {
+  int l = 0;
+  while ((1u << l) < d) l++;
+  m = (uint32_t)(((uint64_t)1 << (31 + l)) / d + 1);
+  sh = 31 + l;
+}
 constexpr int kMaxUnitWeight = 11;
 static_assert(unit_weight(kFmtQ4) == 9 && unit_weight(kFmtQ5) == 11 && unit_weight(kFmtG64) == 9 &&
                   unit_weight(kFmtZP) == 9,
-              "unit weights");
+              "unit weights (div_unit_weight knows only 9 and 11)");
 
 // One job as the kernels see it.  All sizes are derived on the host.
 struct JobDesc {
@@ -88,6 +103,8 @@ struct JobDesc {
   int32_t ngroups;       // K / 32
   int32_t nrb;           // ceil(N / 16)
   int32_t nrg;           // stream kernel: row groups, ceil(nrb / rows per step)
+  uint32_t nkt_m;        // s / nkt = (s * nkt_m) >> nkt_sh for 0 <= s < 2^31 (host-computed)
+  int32_t nkt_sh;
   int32_t grp_begin;     // group kernel: first row-block group of this job
   int32_t grp_end;
 };

@@ -89,6 +89,8 @@ struct StreamPhases {
 struct StreamPos {
   int ph, j, rg, kt;
   int nkt, nrg, nrb, fmt;
+  uint32_t nkt_m;
+  int nkt_sh;
   const uint8_t* packed;
   const uint16_t* X;
   int ldx, M, K;
@@ -116,9 +118,14 @@ QG_PLAN void stream_phase_end(const StreamPhases& P, int ph, int& j, int& s) {
   s = e ? sE : h ? sH : sT;
 }
 
+// s / nkt of job j (0 <= s < 2^31), by the job's multiplier
+QG_PLAN int div_nkt(int s, uint32_t m, int sh) { return (int)(((uint64_t)(uint32_t)s * m) >> sh); }
+
 QG_PLAN void stream_load_job(StreamPos& c, const QG_CONST JobDesc* D, int j) {
   c.j = j;
   c.nkt = D[j].nkt;
+  c.nkt_m = D[j].nkt_m;
+  c.nkt_sh = D[j].nkt_sh;
   c.nrg = D[j].nrg;
   c.nrb = D[j].nrb;
   c.fmt = D[j].fmt;
@@ -130,7 +137,7 @@ QG_PLAN void stream_load_job(StreamPos& c, const QG_CONST JobDesc* D, int j) {
 }
 QG_PLAN void stream_seek(StreamPos& c, const QG_CONST JobDesc* D, int j, int s) {
   stream_load_job(c, D, j);
-  c.rg = s / c.nkt;
+  c.rg = div_nkt(s, c.nkt_m, c.nkt_sh);
   c.kt = s - c.rg * c.nkt;
 }
 QG_PLAN void stream_start(StreamPos& c, const QG_CONST JobDesc* D, const StreamPhases& P) {
@@ -189,16 +196,16 @@ QG_PLAN void stream_plan(StreamPhases& P, const StreamGrid& g, const QG_CONST Jo
   // first step (jA, sA): the first step of job jA whose first unit is >= a
   int jA = stream_job_of(g, D, a);
   const int wA = unit_weight(D[jA].fmt), dA = a - D[jA].ubeg;
-  int sA = dA <= 0 ? 0 : (dA + wA - 1) / wA;
+  int sA = dA <= 0 ? 0 : div_unit_weight(dA + wA - 1, D[jA].fmt);
   if (sA == D[jA].nrg * D[jA].nkt) {
     jA++;
     sA = 0;
   }
   // last step (jL, sL): the last step whose first unit is <= b - 1
   const int jL = stream_job_of(g, D, b - 1);
-  const int sL = (b - 1 - D[jL].ubeg) / unit_weight(D[jL].fmt);
+  const int sL = div_unit_weight(b - 1 - D[jL].ubeg, D[jL].fmt);
   const int nktA = D[jA].nkt, nktL = D[jL].nkt;
-  const int rgA = sA / nktA, rgL = sL / nktL;
+  const int rgA = div_nkt(sA, D[jA].nkt_m, D[jA].nkt_sh), rgL = div_nkt(sL, D[jL].nkt_m, D[jL].nkt_sh);
   const bool head = sA != rgA * nktA;             // first row group began before a
   const bool tail = sL != rgL * nktL + nktL - 1;  // last row group runs past b
   const bool one = jA == jL && rgA == rgL;        // the range lies in one row group
