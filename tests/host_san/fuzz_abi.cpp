@@ -12,7 +12,10 @@
 #include <random>
 #include <vector>
 
+#include <hip/hip_runtime.h>
+
 #include "qgemm.h"
+#include "qgemm_internal.h"
 
 extern long g_launches;
 extern long g_big_launches;
@@ -353,6 +356,27 @@ void pack_case() {
 
 }  // namespace
 
+// The planning code's division by a job's k-tile count goes through
+// div_magic: exact for every count 1 .. 2^17 and dividend 0 .. 2^31 - 1 --
+// checked here at the dividends where an error would show first (around
+// multiples of the divisor and at the top of the range) and at random ones.
+void div_magic_check() {
+  for (uint32_t d = 1; d <= (1u << 17); d++) {
+    uint32_t m;
+    int32_t sh;
+    qg::div_magic(d, m, sh);
+    auto q = [&](uint64_t x) { return (uint64_t)((x * m) >> sh); };
+    const uint64_t top = (1ull << 31) - 1;
+    for (uint64_t x : {(uint64_t)0, (uint64_t)1, (uint64_t)d - 1, (uint64_t)d, (uint64_t)d + 1, top, top - top % d,
+                       top - top % d - 1, (uint64_t)rnd(0, (int64_t)top)}) {
+      EXPECT(q(x) == x / d);
+    }
+    for (uint64_t k = 2; k <= 64 && k * d <= top; k *= 2) {
+      EXPECT(q(k * d) == k && q(k * d - 1) == k - 1);
+    }
+  }
+}
+
 int main(int argc, char** argv) {
   if (argc != 3) {
     std::fprintf(stderr, "usage: fuzz_abi SEED ITERATIONS\n");
@@ -360,6 +384,7 @@ int main(int argc, char** argv) {
   }
   rng.seed(std::strtoull(argv[1], nullptr, 10));
   const long iters = std::strtol(argv[2], nullptr, 10);
+  div_magic_check();
   for (g_iter = 0; g_iter < iters; g_iter++) {
     if (g_iter % 50 == 49) {
       big_case();
