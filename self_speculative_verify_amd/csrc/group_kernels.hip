@@ -45,9 +45,10 @@ struct Group {
   static constexpr int kBufBytes = kXBytes + kW * 256;                // then 256 scale bytes per wave
   static constexpr int kYRow = kRG * kTileRows;                       // outputs n of a wave
   static_assert(kND * kThreads >= kMPad * 16, "X copies cover the panel");
-  static constexpr int kYBytes = kW * kMPad * kYRow * 4;             // output staging (reuses the ring)
-  static constexpr int kRingBytes = kBufs * kBufBytes > kYBytes ? kBufs * kBufBytes : kYBytes;
-  static constexpr int kLdsBytes = kRingBytes + kMPad * 8;           // then one argmax key per row
+  static constexpr int kYBytes = kW * kMPad * kYRow * 4;             // output staging, after the ring
+  static constexpr int kRingBytes = kBufs * kBufBytes;
+  static constexpr int kLdsBytes = kRingBytes + kYBytes + kMPad * 8;  // then one argmax key per row
+  static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
 
   template <int F>
   static constexpr bool kSide = F == kFmtQ5 || F == kFmtZP;   // a side word per row block
@@ -63,28 +64,63 @@ struct Group {
   template <int F>
   static constexpr int kLoadsTile = kND + 1 + kLoadsW<F>;
 
+  // What a wave's loads of one unit need: the unit's job (X panel and k
+  // extent) and the wave's row blocks.
+  struct Unit {
+    const uint16_t* X;
+    const uint8_t* wbase;  // tile 0 of the wave's first row block (its job's last when the wave has none)
+    int64_t ldx;
+    int64_t rstride;       // bytes of one row block's tiles
+    int K, M, nkt;
+    int nr;                // row blocks the loads cover (1 or 2)
+    uint32_t soff;         // the lane's scale-copy offset from a tile
+  };
+  template <int F>
+  static __device__ __forceinline__ Unit unit_of(const JobDesc& d, int rb0, int wave, int lane) {
+    constexpr int TB = tile_bytes(F);
+    Unit u;
+    u.X = d.X;
+    u.ldx = d.ldx;
+    u.K = d.K;
+    u.M = d.M;
+    u.nkt = d.nkt;
+    u.rstride = (int64_t)d.nkt * TB;
+    const int rbw = rb0 + kRG * wave;
+    const int nrows = d.nrb - rbw;                     // valid row blocks (may be <= 0)
+    const int rbl = nrows > 0 ? rbw : d.nrb - 1;       // waves past the job re-read its last block
+    u.nr = nrows > 0 ? (nrows < kRG ? nrows : kRG) : 1;
+    u.wbase = d.packed + (int64_t)rbl * u.rstride;
+    const int srb = ((lane >> 1) & 1) < u.nr ? (lane >> 1) & 1 : u.nr - 1;
+    // group 64: a row's two scales are one word, which both lanes of the
+    // pair copy (so words 0 and 1 of a row block are the same)
+    u.soff = (uint32_t)(srb * u.rstride) + (uint32_t)(F == kFmtG64 ? kScaleOff + 4 * (lane >> 2)
+                                                                  : kScaleOff + 8 * (lane >> 2) + 4 * (lane & 1));
+    return u;
+  }
+
   // Direct-to-LDS copy of this wave's X slots of k tile kt (clamped to the
   // last) into the buffer at LDS address buf.  Slot rows past M repeat row
   // M-1 and k is clamped into the row (padding groups then add exact zeros:
   // their codes are 0).
-  static __device__ __forceinline__ void copy_x(const JobDesc& d, int kt, uint32_t buf, int wave, int lane) {
-    kt = kt < d.nkt ? kt : d.nkt - 1;
+  static __device__ __forceinline__ void copy_x(const Unit& u, int kt, uint32_t buf, int wave, int lane) {
+    kt = kt < u.nkt ? kt : u.nkt - 1;
 #pragma unroll
     for (int i = 0; i < kND; i++) {
       const int s = 64 * (wave * kND + i) + lane;
       const int row = s >> 4;
       const int col = (s & 15) ^ (row & 15);
-      const int m = row < d.M ? row : d.M - 1;
+      const int m = row < u.M ? row : u.M - 1;
       const int kk = kt * kTileK + 8 * col;
-      const int k = kk < d.K - 8 ? kk : d.K - 8;
-      lds_copy16(d.X + (int64_t)m * d.ldx + k, buf + 1024u * (uint32_t)(wave * kND + i));
+      const int k = kk < u.K - 8 ? kk : u.K - 8;
+      lds_copy16(u.X + (int64_t)m * u.ldx + k, buf + 1024u * (uint32_t)(wave * kND + i));
     }
   }
 
   // The code loads of one tile per row block as raw buffer loads over that
   // tile alone (non-temporal).  A tile past the job's last (the prefetch
-  // running ahead of the final tiles) gets a zero-length range: its loads
-  // return zeros without touching memory but still count for the waits.
+  // running ahead of the final tiles with no next unit to run into) gets a
+  // zero-length range: its loads return zeros without touching memory but
+  // still count for the waits.
   static constexpr int kNt = 2;  // cache policy: non-temporal
   template <int F>
   static __device__ __forceinline__ void load_w(Tiles<F>& t, const uint8_t* w0, int64_t rstride,
@@ -106,25 +142,44 @@ struct Group {
   // bytes per row): lane l copies word l & 1 of row l >> 2, row block
   // (l >> 1) & 1, whose offset from the tile is soff.
   template <int F>
-  static __device__ __forceinline__ void copies(const JobDesc& d, int kx, uint32_t buf, const uint8_t* wbase,
-                                                uint32_t soff, int wave, int lane) {
+  static __device__ __forceinline__ void copies(const Unit& u, int kx, uint32_t buf, int wave, int lane) {
     constexpr int TB = tile_bytes(F);
-    const uint8_t* tile = wbase + (int64_t)(kx < d.nkt ? kx : d.nkt - 1) * TB;
-    copy_x(d, kx, buf, wave, lane);
-    lds_copy4(tile + soff, buf + (uint32_t)(kXBytes + 256 * wave));
+    const uint8_t* tile = u.wbase + (int64_t)(kx < u.nkt ? kx : u.nkt - 1) * TB;
+    copy_x(u, kx, buf, wave, lane);
+    lds_copy4(tile + u.soff, buf + (uint32_t)(kXBytes + 256 * wave));
   }
   template <int F>
-  static __device__ __forceinline__ void codes(const JobDesc& d, int kw, Tiles<F>& t, const uint8_t* wbase,
-                                               int64_t rstride, int nrows, int lane) {
+  static __device__ __forceinline__ void codes(const Unit& u, int kw, Tiles<F>& t, int lane) {
     constexpr int TB = tile_bytes(F);
-    load_w<F>(t, wbase + (int64_t)(kw < d.nkt ? kw : d.nkt - 1) * TB, rstride, nrows, kw < d.nkt ? TB : 0, lane);
+    load_w<F>(t, u.wbase + (int64_t)(kw < u.nkt ? kw : u.nkt - 1) * TB, u.rstride, u.nr, kw < u.nkt ? TB : 0, lane);
   }
 
-  // One unit: row blocks rb0 + kRG * wave + r (r < kRG) of job d, all k tiles.
+  template <typename Fn, int... P>
+  static __device__ __forceinline__ void each_p_(Fn&& f, std::integer_sequence<int, P...>) {
+    (f(std::integral_constant<int, P>{}), ...);
+  }
+
+  // The units this workgroup takes, in order: round i of the grid takes
+  // units [i G, (i + 1) G) in alternating directions, so the longest-first
+  // order of the jobs evens out across workgroups.
+  static __device__ __forceinline__ int unit_index(int i, int G, int b) { return i * G + ((i & 1) ? G - 1 - b : b); }
+
+  // This workgroup's units from round i on while their jobs have format F;
+  // returns the first round it did not run (a unit of another format, or
+  // past the end).  Within such a run the prefetch does not drain between
+  // units: the last k tiles of a unit issue the first tiles of the next one
+  // (whose job must also be format F, with the current job's k-tile count a
+  // multiple of kDepth, so its tiles land in the ring slots and code
+  // buffers its loop reads them from).  The loads past a unit's end run in
+  // exactly the order a unit's own start would issue them, so the next
+  // unit's wait counts hold unchanged.  Y leaves through LDS staging of its
+  // own, so nothing waits for the ring at a unit's end.
   template <int F>
-  static __device__ void run_unit(const JobDesc& d, int rb0, uint8_t* xs, uint32_t xs_lds, int tid) {
+  static __device__ __forceinline__ int run_units(const QG_CONST JobDesc* D, int& j, int i, int total, uint8_t* xs,
+                                  uint32_t xs_lds, int tid) {
     constexpr int TB = tile_bytes(F);
-    // Issue order: codes of tile 0, then per tile t (the prologue for
+    (void)TB;
+    // Issue order: codes of tile 0, then per tile t (the start for
     // t < kDepth - 1, else the end of tile t - kDepth + 1): copies of tile t,
     // codes of tile t + 1.  The copies of tile kt are therefore complete once
     // at most this many younger loads of this wave are outstanding: the codes
@@ -134,117 +189,159 @@ struct Group {
     // s_waitcnt encoding (gfx9): vmcnt low 4 bits, expcnt 7, lgkmcnt 15, vmcnt high 2 bits
     constexpr int kXWaitImm = (kXWait & 15) | (7 << 4) | (15 << 8) | ((kXWait >> 4) << 14);
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nkt = d.nkt;
-    const int64_t rstride = (int64_t)nkt * TB;
-    const int rbw = rb0 + kRG * wave;                  // this wave's first row block
-    const int nrows = d.nrb - rbw;                     // valid row blocks (may be <= 0)
-    const int rbl = nrows > 0 ? rbw : d.nrb - 1;       // waves past the job re-read its last block
-    const int nr = nrows > 0 ? nrows : 1;
-    const uint8_t* wbase = d.packed + (int64_t)rbl * rstride;
-    const int srb = ((lane >> 1) & 1) < nr ? (lane >> 1) & 1 : nr - 1;
-    // group 64: a row's two scales are one word, which both lanes of the
-    // pair copy (so words 0 and 1 of a row block are the same)
-    const uint32_t soff = (uint32_t)(srb * rstride) +
-                          (uint32_t)(F == kFmtG64 ? kScaleOff + 4 * (lane >> 2)
-                                                  : kScaleOff + 8 * (lane >> 2) + 4 * (lane & 1));
-    Tiles<F> buf[kDepth];
-    __builtin_amdgcn_sched_barrier(0);
-    codes<F>(d, 0, buf[0], wbase, rstride, nr, lane);
-#pragma unroll
-    for (int p = 0; p < kDepth - 1; p++) {
-      __builtin_amdgcn_sched_barrier(0);
-      copies<F>(d, p, xs_lds + (uint32_t)(p * kBufBytes), wbase, soff, wave, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      codes<F>(d, p + 1, buf[p + 1], wbase, rstride, nr, lane);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    f4_t acc[kRG][kMb];
-#pragma unroll
-    for (int r = 0; r < kRG; r++)
-#pragma unroll
-      for (int mb = 0; mb < kMb; mb++) acc[r][mb] = f4_t{0.f, 0.f, 0.f, 0.f};
-    const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+    const int G = (int)gridDim.x, b = (int)blockIdx.x;
+    uint8_t* ystage = xs + kRingBytes;
+    unsigned long long* best = (unsigned long long*)(ystage + kYBytes);
     // A fragment of group j, m block mb: row 16 mb + (lane mod 16), chunk
     // 4 j + lane / 16, at its swizzled slot
     const int mr = lane & 15, c = lane >> 4;
     uint32_t aoff[4];
 #pragma unroll
-    for (int j = 0; j < 4; j++) aoff[j] = (uint32_t)(256 * mr + 16 * ((4 * j + c) ^ mr));
+    for (int g = 0; g < 4; g++) aoff[g] = (uint32_t)(256 * mr + 16 * ((4 * g + c) ^ mr));
     const uint32_t sread = (uint32_t)(kXBytes + 256 * wave + 16 * mr);
-    for (int kt0 = 0; kt0 < nkt; kt0 += kDepth) {
+    const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+    Tiles<F> buf[kDepth];
+    // p = 0 .. kDepth - 1 as compile-time constants (the code buffers stay in registers)
+    auto each_p = [&](auto&& f) { each_p_(f, std::make_integer_sequence<int, kDepth>{}); };
+    bool primed = false;  // this unit's first tiles were issued by the previous one
+    for (;; i++) {
+      const int u = unit_index(i, G, b);
+      if (u >= total) break;
+      while (u >= D[j].grp_end) j++;
+      const QG_CONST JobDesc& d = D[j];
+      if (d.fmt != F) break;
+      const int rb0 = (u - d.grp_begin) * kW * kRG;
+      const Unit cur = unit_of<F>(d, rb0, wave, lane);
+      // the next unit, when its first tiles can be issued from this one
+      const int un = unit_index(i + 1, G, b);
+      int jn = j;
+      if (un < total)
+        while (un >= D[jn].grp_end) jn++;
+      const bool chain = un < total && D[jn].fmt == F && d.nkt % kDepth == 0;
+      const Unit nxt = chain ? unit_of<F>(D[jn], (un - D[jn].grp_begin) * kW * kRG, wave, lane) : cur;
+      const int nkt = d.nkt;
+      if (!primed) {
+        __builtin_amdgcn_sched_barrier(0);
+        codes<F>(cur, 0, buf[0], lane);
 #pragma unroll
-      for (int p = 0; p < kDepth; p++) {
-        const int kt = kt0 + p;
-        if (kt < nkt) {
-          // this wave's copies of tile kt have landed; after the barrier every
-          // wave's have, and every wave is done with tile kt - 1
-          __builtin_amdgcn_s_waitcnt(kXWaitImm);
-          __atomic_signal_fence(__ATOMIC_SEQ_CST);
-          __builtin_amdgcn_s_barrier();
-          __atomic_signal_fence(__ATOMIC_SEQ_CST);
-          const uint8_t* xb = xs + p * kBufBytes;
-          // scales of row mr: words 0, 1 of row block 0, then of row block 1
-          const u4_t sc = *(const u4_t*)(xb + sread);
-          f4_t pr[kRG][kMb];
-          // group by group: the A fragments of group j serve all kRG row blocks
+        for (int p = 0; p < kDepth - 1; p++) {
+          __builtin_amdgcn_sched_barrier(0);
+          copies<F>(cur, p, xs_lds + (uint32_t)(p * kBufBytes), wave, lane);
+          __builtin_amdgcn_sched_barrier(0);
+          codes<F>(cur, p + 1, buf[p + 1], lane);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f4_t acc[kRG][kMb];
 #pragma unroll
-          for (int j = 0; j < 4; j++) {
-            h8_t a[kMb];
+      for (int r = 0; r < kRG; r++)
 #pragma unroll
-            for (int mb = 0; mb < kMb; mb++) a[mb] = lds_h8(xb + aoff[j] + 4096 * mb);
-            // every MFMA of the group is issued before the first of its
-            // results is scaled, so the matrix-core latency overlaps
-            // group 64: the odd half of a group accumulates onto the even
-            // half's products, which are scaled once, after it
-            constexpr bool kG64 = F == kFmtG64;
+        for (int mb = 0; mb < kMb; mb++) acc[r][mb] = zero;
+      // one k tile: wait for its copies, then its MFMAs and scales
+      auto tile = [&](auto pc_, int kt) {
+        constexpr int p = decltype(pc_)::value;
+        // this wave's copies of tile kt have landed; after the barrier every
+        // wave's have, and every wave is done with tile kt - 1
+        __builtin_amdgcn_s_waitcnt(kXWaitImm);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        (void)kt;
+        const uint8_t* xb = xs + p * kBufBytes;
+        // scales of row mr: words 0, 1 of row block 0, then of row block 1
+        const u4_t sc = *(const u4_t*)(xb + sread);
+        f4_t pr[kRG][kMb];
+        // group by group: the A fragments of group g serve all kRG row blocks
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+          h8_t a[kMb];
+#pragma unroll
+          for (int mb = 0; mb < kMb; mb++) a[mb] = lds_h8(xb + aoff[g] + 4096 * mb);
+          // every MFMA of the group is issued before the first of its
+          // results is scaled, so the matrix-core latency overlaps
+          // group 64: the odd half of a group accumulates onto the even
+          // half's products, which are scaled once, after it
+          constexpr bool kG64 = F == kFmtG64;
+#pragma unroll
+          for (int r = 0; r < kRG; r++) {
+            const h8_t q = unpack_chunk<F>(buf[p].c[r][g], side_word<F>(buf[p].h[kSide<F> ? r : 0]), g);
+#pragma unroll
+            for (int mb = 0; mb < kMb; mb++)
+              pr[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb], q, (kG64 && (g & 1)) ? pr[r][mb] : zero, 0, 0, 0);
+          }
+          if (!kG64 || (g & 1)) {
 #pragma unroll
             for (int r = 0; r < kRG; r++) {
-              const h8_t q = unpack_chunk<F>(buf[p].c[r][j], side_word<F>(buf[p].h[kSide<F> ? r : 0]), j);
+              // group 32: word g / 2 of the row block holds groups (g & ~1, g | 1);
+              // group 64: word 0 holds halves (0, 1)
+              const uint32_t sp = sc[2 * r + (kG64 ? 0 : g >> 1)];
+              const int hi = kG64 ? g >> 1 : g & 1;
+              const float sj = hi ? scale_f32<1>(sp) : scale_f32<0>(sp);
 #pragma unroll
               for (int mb = 0; mb < kMb; mb++)
-                pr[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb], q, (kG64 && (j & 1)) ? pr[r][mb] : zero, 0, 0, 0);
-            }
-            if (!kG64 || (j & 1)) {
 #pragma unroll
-              for (int r = 0; r < kRG; r++) {
-                // group 32: word j / 2 of the row block holds groups (j & ~1, j | 1);
-                // group 64: word 0 holds halves (0, 1)
-                const uint32_t sp = sc[2 * r + (kG64 ? 0 : j >> 1)];
-                const int hi = kG64 ? j >> 1 : j & 1;
-                const float sj = hi ? scale_f32<1>(sp) : scale_f32<0>(sp);
-#pragma unroll
-                for (int mb = 0; mb < kMb; mb++)
-#pragma unroll
-                  for (int i = 0; i < 4; i++) acc[r][mb][i] = __builtin_fmaf(sj, pr[r][mb][i], acc[r][mb][i]);
-              }
+                for (int e = 0; e < 4; e++) acc[r][mb][e] = __builtin_fmaf(sj, pr[r][mb][e], acc[r][mb][e]);
             }
           }
         }
-        // copies of tile kt + kDepth - 1 into the buffer of tile kt - 1 (every
-        // wave is past it), codes of tile kt + kDepth.  Past the last k tile
-        // they (kept for exact wait counts) re-read the last tile into
-        // buffers no wave reads again.
+      };
+      // copies of tile kt + kDepth - 1 into the buffer of tile kt - 1 (every
+      // wave is past it), codes of tile kt + kDepth: of this unit, where past
+      // its last k tile they (kept for exact wait counts) re-read the last
+      // tile into buffers no wave reads again
+      auto refill = [&](auto pc_, int kt) {
+        constexpr int p = decltype(pc_)::value;
         __builtin_amdgcn_sched_barrier(0);
-        copies<F>(d, kt + kDepth - 1, xs_lds + (uint32_t)(((p + kDepth - 1) % kBufs) * kBufBytes), wbase, soff,
-                  wave, lane);
+        copies<F>(cur, kt + kDepth - 1, xs_lds + (uint32_t)(((p + kDepth - 1) % kBufs) * kBufBytes), wave, lane);
         __builtin_amdgcn_sched_barrier(0);
-        codes<F>(d, kt + kDepth, buf[p], wbase, rstride, nr, lane);
+        codes<F>(cur, kt + kDepth, buf[p], lane);
         __builtin_amdgcn_sched_barrier(0);
+      };
+      const int kmain = chain ? nkt - kDepth : nkt;
+      for (int kt0 = 0; kt0 < kmain; kt0 += kDepth) {
+        each_p([&](auto pc_) {
+          constexpr int p = decltype(pc_)::value;
+          const int kt = kt0 + p;
+          if (kt < nkt) tile(pc_, kt);
+          refill(pc_, kt);
+        });
       }
+      if (chain) {
+        // the last kDepth tiles (nkt is a multiple of kDepth): their loads
+        // past the end are the next unit's first tiles, in the order its own
+        // start would issue them (copies of tile t into ring slot t, codes
+        // of tile t into buf[t])
+        each_p([&](auto pc_) {
+          constexpr int p = decltype(pc_)::value;
+          tile(pc_, nkt - kDepth + p);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (p == 0) copies<F>(cur, nkt - 1, xs_lds + (uint32_t)((kDepth - 1) * kBufBytes), wave, lane);
+          else copies<F>(nxt, p - 1, xs_lds + (uint32_t)((p - 1) * kBufBytes), wave, lane);
+          __builtin_amdgcn_sched_barrier(0);
+          codes<F>(nxt, p, buf[p], lane);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
+      const int rbw = rb0 + kRG * wave;
+      if (d.nrb - rbw > 0) store_y(d, acc, rbw, ystage + kMPad * kYRow * 4 * wave, best, lane);
+      if (d.keys) {
+        // the unit's argmax keys are complete and go to the job's keys
+        __syncthreads();
+        if (tid < d.M) {
+          const unsigned long long k = best[tid];
+          if (k != 0ull) key_max(d.keys + (blockIdx.x % kKeyCopies) * kKeyRows + tid, k);
+          best[tid] = 0ull;
+        }
+      }
+      if (!chain) {
+        // the loads past the end re-read tiles into ring slots: every one has
+        // landed and every wave is past the ring before another start
+        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+        __syncthreads();
+      }
+      primed = chain;
     }
-    // every copy has landed and every wave is done with the ring
-    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
-    __syncthreads();
-    unsigned long long* best = (unsigned long long*)(xs + kRingBytes);
-    if (nrows > 0) store_y(d, acc, rbw, xs + kMPad * kYRow * 4 * wave, best, lane);
-    // the ring is free for the next unit's copies; the unit's argmax keys are
-    // complete and go to the job's keys
-    __syncthreads();
-    if (d.keys && tid < d.M) {
-      const unsigned long long k = best[tid];
-      if (k != 0ull) key_max(d.keys + (blockIdx.x % kKeyCopies) * kKeyRows + tid, k);
-      best[tid] = 0ull;
-    }
+    return i;
   }
 
   // The wave's outputs (rows m < kMPad, n = 16 rbw .. 16 rbw + 31) go through
@@ -306,21 +403,18 @@ group_kernel(SweepArgs) {
   const int tid = threadIdx.x;
   // argmax keys of the verify head start at 0 (the first unit's barriers
   // order this before any use)
-  if (tid < kMPad) ((unsigned long long*)(xs + S::kRingBytes))[tid] = 0ull;
+  if (tid < kMPad) ((unsigned long long*)(xs + S::kRingBytes + S::kYBytes))[tid] = 0ull;
   int j = 0;
-  // round i of the grid takes units [i G, (i + 1) G) in alternating
-  // directions, so the longest-first order evens out across workgroups
-  const int G = (int)gridDim.x, b = (int)blockIdx.x;
-  for (int i = 0;; i++) {
-    const int u = i * G + ((i & 1) ? G - 1 - b : b);
+  // runs of units of one format (a launch mixes formats only by job)
+  for (int i = 0;;) {
+    const int u = S::unit_index(i, (int)gridDim.x, (int)blockIdx.x);
     if (u >= args.total) break;
     while (u >= D[j].grp_end) j++;
-    const JobDesc d = D[j];
-    const int rb0 = (u - d.grp_begin) * S::kW * kGroupRows;
-    if (d.fmt == kFmtQ4) S::template run_unit<kFmtQ4>(d, rb0, xs, xs_lds, tid);
-    else if (!kAll || d.fmt == kFmtQ5) S::template run_unit<kFmtQ5>(d, rb0, xs, xs_lds, tid);
-    else if (d.fmt == kFmtG64) S::template run_unit<kFmtG64>(d, rb0, xs, xs_lds, tid);
-    else S::template run_unit<kFmtZP>(d, rb0, xs, xs_lds, tid);
+    const int f = D[j].fmt;
+    if (f == kFmtQ4) i = S::template run_units<kFmtQ4>(D, j, i, args.total, xs, xs_lds, tid);
+    else if (!kAll || f == kFmtQ5) i = S::template run_units<kFmtQ5>(D, j, i, args.total, xs, xs_lds, tid);
+    else if (f == kFmtG64) i = S::template run_units<kFmtG64>(D, j, i, args.total, xs, xs_lds, tid);
+    else i = S::template run_units<kFmtZP>(D, j, i, args.total, xs, xs_lds, tid);
   }
 }
 
