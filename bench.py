@@ -44,7 +44,7 @@ PATHS = {"auto": 0, "gemv": 1, "mfma": 2}
 TRAFFIC = {
     # FETCH_SIZE 50187.3 KiB x 2.0000 (a 1 GiB device copy reads 524300 KiB)
     # + WRITE_SIZE 4018 KiB x 1.0 (the copy writes 1048576 KiB)
-    "78d1132c0b07ce2d": {"workload": "gate+up 5120->34816 4-bit M=1", "bytes": 106893866},
+    "9b37e49fe7e3e0f3": {"workload": "gate+up 5120->34816 4-bit M=1", "bytes": 106883395},
 }
 KERNEL_SOURCES = ("self_speculative_verify_amd/csrc/qgemm_kernels.hip",
                   "self_speculative_verify_amd/csrc/qgemm_internal.h",
@@ -466,6 +466,7 @@ def timeline(args):
         }
         print(json.dumps(out), flush=True)
         if args.timeline_dump:
+            os.makedirs(args.timeline_dump, exist_ok=True)
             np.save(os.path.join(args.timeline_dump, f"timeline_cfg{cfg}.npy"), t)
         del b
         torch.cuda.empty_cache()
