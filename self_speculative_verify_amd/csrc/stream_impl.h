@@ -67,6 +67,12 @@ struct Stream {
   static constexpr bool kSide = (kFS & (kSetQ5 | kSetZP)) != 0;
   static constexpr int kOnly = kFS == kSetQ4 ? kFmtQ4 : kFS == kSetQ5 ? kFmtQ5 : kFS == kSetG64 ? kFmtG64
                                : kFS == kSetZP ? kFmtZP : 0;   // the one format, or 0
+  // The raised second dispatch half drops back to the base priority when a
+  // quarter of its work is left (MFMA, four-block steps, at most four rows;
+  // measured on gate+up 34816 x 5120 4-bit at M = 1, 2, 4: 23.2 -> 22.7,
+  // 23.6 -> 22.8, 23.4 -> 22.6 us).  Applied to every kernel the same rule
+  // made the big 5-bit stack 20 % slower and the M = 6 pair no faster.
+  static constexpr bool kEvenEnd = kMfma && kR == 4 && kCap <= 4;
 
   struct Step {
     u4_t c[kR];
@@ -526,6 +532,10 @@ struct Stream {
     float acc[kR][kA];
     zero(acc);
     bool done = false;
+    // the wave's units still to compute (kEvenEnd), and whether it runs raised
+    const int utot = b - a;
+    int urem = utot;
+    bool raised = cx.gw >= args.nwaves / 2;
     // one pipeline slot: consume buffer p (while steps are left), then refill
     // it kDepth steps ahead; p is a constant in every instance, so the
     // buffers stay in registers
@@ -542,6 +552,13 @@ struct Stream {
         }
 #endif
         compute_any(acc, buf[p], cc.fmt, xs, lane);
+        if constexpr (kEvenEnd) {
+          urem -= cc.fmt == kFmtQ5 ? unit_weight(kFmtQ5) : unit_weight(kFmtQ4);
+          if (raised && 4 * urem <= utot) {
+            __builtin_amdgcn_s_setprio(0);
+            raised = false;
+          }
+        }
 #ifdef QG_TIMELINE
         if (kTrace) {
           tb = trace_stamp(acc[kR - 1][kA - 1]);
@@ -580,8 +597,11 @@ struct Stream {
     // first, the second half joins while those already stream.  The later
     // waves run at a raised priority, so that their planning and first loads
     // are not held behind their partners' unpacking (measured: the M = 6
-    // verify workload 42.4 -> 39.9 us, the rest unchanged or faster).
-    if (cx.gw >= args.nwaves / 2) __builtin_amdgcn_s_setprio(1);
+    // verify workload 42.4 -> 39.9 us, the rest unchanged or faster).  With
+    // kEvenEnd they drop back once a quarter of their work is left, so that
+    // the first half, which has lost the arbitration until then, catches up
+    // and the two halves end together.
+    if (raised) __builtin_amdgcn_s_setprio(1);
     while (!done) each_slot(slot, std::make_integer_sequence<int, kDepth>{});
 #ifdef QG_TIMELINE
     if (kTrace) __builtin_amdgcn_s_waitcnt(0);
