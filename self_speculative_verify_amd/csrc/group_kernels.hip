@@ -11,7 +11,8 @@ namespace qg {
 // --------------------------------------------------------------------------
 // group kernel: panels of 17..64 rows (MFMA, 2..4 m blocks)
 // --------------------------------------------------------------------------
-// One workgroup of kW waves per unit = (job, kW * kRG row blocks), whole K:
+// One workgroup of kW waves per unit = (job, kW * kRG row blocks, or fewer in
+// a re-sliced last round, see rounds_of), whole K:
 // no K split, so no partial sums cross waves.  The waves walk the k tiles in
 // lockstep, one barrier per k tile.  The X chunk of a k tile (kMPad rows x 128
 // k) is copied once per workgroup straight from memory into LDS (direct-to-LDS
@@ -74,9 +75,12 @@ struct Group {
     int K, M, nkt;
     int nr;                // row blocks the loads cover (1 or 2)
     uint32_t soff;         // the lane's scale-copy offset from a tile
+    bool busy;             // the wave has rows in the unit (else its code loads are empty and it computes nothing)
   };
+  // rb0: the unit's first row block; urb: its row blocks (kUnitRB, or kFine
+  // in a re-sliced last round)
   template <int F>
-  static __device__ __forceinline__ Unit unit_of(const JobDesc& d, int rb0, int wave, int lane) {
+  static __device__ __forceinline__ Unit unit_of(const JobDesc& d, int rb0, int urb, int wave, int lane) {
     constexpr int TB = tile_bytes(F);
     Unit u;
     u.X = d.X;
@@ -87,7 +91,8 @@ struct Group {
     u.rstride = (int64_t)d.nkt * TB;
     const int rbw = rb0 + kRG * wave;
     const int nrows = d.nrb - rbw;                     // valid row blocks (may be <= 0)
-    const int rbl = nrows > 0 ? rbw : d.nrb - 1;       // waves past the job re-read its last block
+    u.busy = kRG * wave < urb && nrows > 0;
+    const int rbl = nrows > 0 ? rbw : d.nrb - 1;       // waves past the job point at its last block
     u.nr = nrows > 0 ? (nrows < kRG ? nrows : kRG) : 1;
     u.wbase = d.packed + (int64_t)rbl * u.rstride;
     const int srb = ((lane >> 1) & 1) < u.nr ? (lane >> 1) & 1 : u.nr - 1;
@@ -151,7 +156,8 @@ struct Group {
   template <int F>
   static __device__ __forceinline__ void codes(const Unit& u, int kw, Tiles<F>& t, int lane) {
     constexpr int TB = tile_bytes(F);
-    load_w<F>(t, u.wbase + (int64_t)(kw < u.nkt ? kw : u.nkt - 1) * TB, u.rstride, u.nr, kw < u.nkt ? TB : 0, lane);
+    load_w<F>(t, u.wbase + (int64_t)(kw < u.nkt ? kw : u.nkt - 1) * TB, u.rstride, u.nr, u.busy && kw < u.nkt ? TB : 0,
+              lane);
   }
 
   template <typename Fn, int... P>
@@ -164,6 +170,59 @@ struct Group {
   // order of the jobs evens out across workgroups.
   static __device__ __forceinline__ int unit_index(int i, int G, int b) { return i * G + ((i & 1) ? G - 1 - b : b); }
 
+  // The last, partial round of the grid: when its units all lie in the last
+  // job, that job's row blocks from there on are cut into units of kFine row
+  // blocks (kFine / kRG busy waves, the rest idle: their code loads are
+  // empty and they only copy X and keep the barriers) if they then still fit
+  // in one round, so that more workgroups share the round and fewer waves
+  // share each SIMD.  Measured: the 248320-row verify head at M = 48 (647
+  // units over 256 workgroups) 240 -> 236 us, the 5-bit stack at M = 32 and
+  // 48 about 1 % faster.  The gain is small because a wave's row blocks over
+  // the whole K take about as long with two busy waves per SIMD as with
+  // three.
+  static constexpr int kUnitRB = kW * kRG;
+  static constexpr int kFine = kW == 12 ? 16 : 8;
+  static_assert(kFine % (4 * kRG) == 0 && kFine < kUnitRB, "fine units keep the busy waves spread over the SIMDs");
+  struct Rounds {
+    int total;   // units, the fine ones included
+    int fbeg;    // first fine unit (total when there are none)
+    int rbf;     // the last job's first row block in fine units
+    int jl;      // the last job
+  };
+  static __device__ __forceinline__ Rounds rounds_of(const QG_CONST JobDesc* D, int njobs, int total, int G) {
+    Rounds r;
+    r.total = total;
+    r.fbeg = total;
+    r.rbf = 0;
+    r.jl = njobs - 1;
+    const int full = total - total % G;
+    const JobDesc& l = D[r.jl];
+    if (full < total && l.grp_begin <= full) {
+      const int rbf = (full - l.grp_begin) * kUnitRB;
+      const int nf = (l.nrb - rbf + kFine - 1) / kFine;
+      if (nf <= G) {
+        r.total = full + nf;
+        r.fbeg = full;
+        r.rbf = rbf;
+      }
+    }
+    return r;
+  }
+  // unit u (< R.total): its job j (searched forward from j), first row block
+  // and row blocks
+  static __device__ __forceinline__ void locate(const QG_CONST JobDesc* D, const Rounds& R, int u, int& j, int& rb0,
+                                                int& nrb) {
+    if (u >= R.fbeg) {
+      j = R.jl;
+      rb0 = R.rbf + (u - R.fbeg) * kFine;
+      nrb = kFine;
+      return;
+    }
+    while (u >= D[j].grp_end) j++;
+    rb0 = (u - D[j].grp_begin) * kUnitRB;
+    nrb = kUnitRB;
+  }
+
   // This workgroup's units from round i on while their jobs have format F;
   // returns the first round it did not run (a unit of another format, or
   // past the end).  Within such a run the prefetch does not drain between
@@ -175,8 +234,8 @@ struct Group {
   // unit's wait counts hold unchanged.  Y leaves through LDS staging of its
   // own, so nothing waits for the ring at a unit's end.
   template <int F>
-  static __device__ __forceinline__ int run_units(const QG_CONST JobDesc* D, int& j, int i, int total, uint8_t* xs,
-                                  uint32_t xs_lds, int tid) {
+  static __device__ __forceinline__ int run_units(const QG_CONST JobDesc* D, int& j, int i, const Rounds& R,
+                                                  uint8_t* xs, uint32_t xs_lds, int tid) {
     constexpr int TB = tile_bytes(F);
     (void)TB;
     // Issue order: codes of tile 0, then per tile t (the start for
@@ -206,19 +265,18 @@ struct Group {
     bool primed = false;  // this unit's first tiles were issued by the previous one
     for (;; i++) {
       const int u = unit_index(i, G, b);
-      if (u >= total) break;
-      while (u >= D[j].grp_end) j++;
+      if (u >= R.total) break;
+      int rb0, urb;
+      locate(D, R, u, j, rb0, urb);
       const QG_CONST JobDesc& d = D[j];
       if (d.fmt != F) break;
-      const int rb0 = (u - d.grp_begin) * kW * kRG;
-      const Unit cur = unit_of<F>(d, rb0, wave, lane);
+      const Unit cur = unit_of<F>(d, rb0, urb, wave, lane);
       // the next unit, when its first tiles can be issued from this one
       const int un = unit_index(i + 1, G, b);
-      int jn = j;
-      if (un < total)
-        while (un >= D[jn].grp_end) jn++;
-      const bool chain = un < total && D[jn].fmt == F && d.nkt % kDepth == 0;
-      const Unit nxt = chain ? unit_of<F>(D[jn], (un - D[jn].grp_begin) * kW * kRG, wave, lane) : cur;
+      int jn = j, rbn = 0, urbn = 0;
+      if (un < R.total) locate(D, R, un, jn, rbn, urbn);
+      const bool chain = un < R.total && D[jn].fmt == F && d.nkt % kDepth == 0;
+      const Unit nxt = chain ? unit_of<F>(D[jn], rbn, urbn, wave, lane) : cur;
       const int nkt = d.nkt;
       if (!primed) {
         __builtin_amdgcn_sched_barrier(0);
@@ -247,6 +305,8 @@ struct Group {
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         (void)kt;
+        // a wave with no rows in the unit only copies and keeps the barriers
+        if (!cur.busy) return;
         const uint8_t* xb = xs + p * kBufBytes;
         // scales of row mr: words 0, 1 of row block 0, then of row block 1
         const u4_t sc = *(const u4_t*)(xb + sread);
@@ -323,7 +383,7 @@ struct Group {
         });
       }
       const int rbw = rb0 + kRG * wave;
-      if (d.nrb - rbw > 0) store_y(d, acc, rbw, ystage + kMPad * kYRow * 4 * wave, best, lane);
+      if (cur.busy) store_y(d, acc, rbw, ystage + kMPad * kYRow * 4 * wave, best, lane);
       if (d.keys) {
         // the unit's argmax keys are complete and go to the job's keys
         __syncthreads();
@@ -405,16 +465,18 @@ group_kernel(SweepArgs) {
   // order this before any use)
   if (tid < kMPad) ((unsigned long long*)(xs + S::kRingBytes + S::kYBytes))[tid] = 0ull;
   int j = 0;
+  const typename S::Rounds R = S::rounds_of(D, args.njobs, args.total, (int)gridDim.x);
   // runs of units of one format (a launch mixes formats only by job)
   for (int i = 0;;) {
     const int u = S::unit_index(i, (int)gridDim.x, (int)blockIdx.x);
-    if (u >= args.total) break;
-    while (u >= D[j].grp_end) j++;
+    if (u >= R.total) break;
+    int rb0, urb;
+    S::locate(D, R, u, j, rb0, urb);
     const int f = D[j].fmt;
-    if (f == kFmtQ4) i = S::template run_units<kFmtQ4>(D, j, i, args.total, xs, xs_lds, tid);
-    else if (!kAll || f == kFmtQ5) i = S::template run_units<kFmtQ5>(D, j, i, args.total, xs, xs_lds, tid);
-    else if (f == kFmtG64) i = S::template run_units<kFmtG64>(D, j, i, args.total, xs, xs_lds, tid);
-    else i = S::template run_units<kFmtZP>(D, j, i, args.total, xs, xs_lds, tid);
+    if (f == kFmtQ4) i = S::template run_units<kFmtQ4>(D, j, i, R, xs, xs_lds, tid);
+    else if (!kAll || f == kFmtQ5) i = S::template run_units<kFmtQ5>(D, j, i, R, xs, xs_lds, tid);
+    else if (f == kFmtG64) i = S::template run_units<kFmtG64>(D, j, i, R, xs, xs_lds, tid);
+    else i = S::template run_units<kFmtZP>(D, j, i, R, xs, xs_lds, tid);
   }
 }
 
