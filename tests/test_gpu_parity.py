@@ -242,6 +242,27 @@ def test_edge_shapes(bits, N, K, M):
         _check(Y, Yref, X, smax, f"path={path}")
 
 
+# A group-kernel launch of more than one round whose last round is partial
+# and lies in its one job: that round is cut into finer units (16 row blocks
+# for the 12-wave kernels at M = 17..48, 8 for the 8-wave kernel at M = 49..64)
+# on a 256-workgroup grid.  301 units of 24 (or 16) row blocks, the last
+# partial, N ragged, k-tile counts with and without the unit chaining.
+RESLICE = [(4, 48, 7213 * 16 - 5, 256), (5, 32, 7213 * 16 - 11, 512), (4, 64, 4809 * 16 - 3, 160)]
+
+
+@pytest.mark.parametrize("bits,M,N,K", RESLICE)
+def test_group_last_round_resliced(bits, M, N, K):
+    say(f"resliced last round bits={bits} M={M} N={N} K={K}")
+    W = _weights(N + 3 * K + M, N, K, True)
+    ref_packed = oracle.quantize_pack(W, bits)
+    packed = packed_dev(ref_packed)
+    X = synth.x_fp16(N + K + 2 * M, M, K)
+    Yref = oracle.sweep(ref_packed, N, K, bits, X)
+    smax = oracle.max_scale(ref_packed, N, K, bits)
+    Y = run_one(packed, bits, N, K, X, M, qgemm.PATH_AUTO)
+    _check(Y, Yref, X, smax, "auto")
+
+
 def test_many_jobs_one_sweep():
     """More jobs than fit in the kernel arguments, mixed bits, M and shapes."""
     import torch
