@@ -16,5 +16,7 @@ def pytest_configure(config):
 def _native_built():
     import __graft_entry__
 
-    __graft_entry__.ensure_built("oracle", "synth", "synth_gpu")
+    # the HIP libraries too: a library older than its sources is rebuilt,
+    # so a test never runs code other than the tree's
+    __graft_entry__.ensure_built("oracle", "synth", "synth_gpu", "qgemm", "qgemm_ceiling")
     yield
