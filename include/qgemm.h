@@ -291,6 +291,47 @@ int qgemm_round_kernels(const qgemm_round* round);
 void qgemm_round_destroy(qgemm_round* round);
 
 /* ---------------------------------------------------------------------------
+ * Round cache.  Rounds keyed by everything a recording fixes, replayed on a
+ * hit and recorded on a miss, least recently used evicted past the capacity
+ * (Quasar/q27 wiki: intro bullets, fused-verify rounds replayed as
+ * shape-keyed graphs; defaults paragraph, a graph-cache cap of 64; open
+ * items, "graph-cache cap under churn", live traffic drawing 44+ keys).  A
+ * key is the whole argument list of qgemm_round_create but the workspace:
+ * every sweep's path and jobs (pointers, shapes, strides, M, bits), the
+ * head's job, draft and output pointers and the slots' contents.  Buffers
+ * that a caller allocates once per shape therefore give one key per shape.
+ * The cache owns one workspace per round (device memory it allocates,
+ * zero-fills on the caller's stream and frees on eviction).
+ *
+ *   capacity : rounds kept, 1 .. QGEMM_ROUND_CACHE_MAX
+ *   hit      : set to 1 when the call replayed a cached round, 0 when it
+ *              recorded one (or failed)
+ * qgemm_round_cache_run validates a miss as qgemm_round_create does; an
+ * eviction synchronizes the device (a replay of the evicted round may still
+ * run), so a capacity that covers the live keys keeps the replay path free
+ * of synchronization.  Calls on one cache are serialized (it is
+ * thread-safe); replays share each round's workspace, so two replays of the
+ * same round must not overlap (one stream per cache, as a decode loop has).
+ * Destroy only after the streams of its replays are synchronized. */
+#define QGEMM_ROUND_CACHE_MAX 4096
+typedef struct qgemm_round_cache_s qgemm_round_cache;
+
+qgemm_status qgemm_round_cache_create(int capacity, qgemm_round_cache** out);
+
+qgemm_status qgemm_round_cache_run(qgemm_round_cache* cache, const qgemm_round_sweep* sweeps, int nsweeps,
+                                   const qgemm_job* head, const int32_t* drafts, const qgemm_slot* slots,
+                                   int nslots, int32_t* argmax, float* maxlogit, int32_t* accepted,
+                                   void* stream, int* hit);
+
+/* Rounds held, and the calls that hit, missed and evicted so far (any
+ * pointer may be NULL). */
+qgemm_status qgemm_round_cache_stats(const qgemm_round_cache* cache, int* size, uint64_t* hits, uint64_t* misses,
+                                     uint64_t* evictions);
+
+/* Free every round and workspace (NULL is a no-op). */
+void qgemm_round_cache_destroy(qgemm_round_cache* cache);
+
+/* ---------------------------------------------------------------------------
  * Attention verify (shared KV).  The attention half of a verify round, per
  * full-attention layer: each slot's W verify positions (the accepted token
  * and its drafts, whose keys and values are already the last W of the slot's

@@ -7,7 +7,10 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <list>
 #include <mutex>
+#include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "qgemm.h"
@@ -619,6 +622,171 @@ void qgemm_round_destroy(qgemm_round* r) {
   if (r->exec) (void)hipGraphExecDestroy(r->exec);
   if (r->graph) (void)hipGraphDestroy(r->graph);
   delete r;
+}
+
+}  // extern "C"
+
+// The round cache: an LRU list of (key, round, its workspace) and a map from
+// key to list position; calls are serialized by the cache's mutex.
+struct qgemm_round_cache_s {
+  struct Entry {
+    std::string key;
+    qgemm_round* round;
+    void* ws;
+  };
+  int cap = 0;
+  std::list<Entry> lru;  // front: most recently used
+  std::unordered_map<std::string, std::list<Entry>::iterator> index;
+  std::mutex mu;
+  uint64_t hits = 0, misses = 0, evictions = 0;
+};
+
+namespace {
+
+template <typename T>
+void key_put(std::string& k, T v) {
+  k.append((const char*)&v, sizeof(v));
+}
+// field by field (never the raw structs, whose padding is not theirs to fix)
+void key_job(std::string& k, const qgemm_job& j) {
+  key_put(k, (uintptr_t)j.packed);
+  key_put(k, (uintptr_t)j.X);
+  key_put(k, (uintptr_t)j.Y);
+  key_put(k, j.N);
+  key_put(k, j.K);
+  key_put(k, j.ldx);
+  key_put(k, j.ldy);
+  key_put(k, j.M);
+  key_put(k, j.bits);
+}
+// the key of a round: everything qgemm_round_create fixes but the workspace
+std::string round_key(const qgemm_round_sweep* sweeps, int nsweeps, const qgemm_job* head, const int32_t* drafts,
+                      const qgemm_slot* slots, int nslots, const int32_t* argmax, const float* maxlogit,
+                      const int32_t* accepted) {
+  std::string k;
+  key_put(k, nsweeps);
+  for (int i = 0; i < nsweeps; i++) {
+    key_put(k, sweeps[i].path);
+    key_put(k, sweeps[i].njobs);
+    for (int j = 0; j < sweeps[i].njobs; j++) key_job(k, sweeps[i].jobs[j]);
+  }
+  key_put(k, head != nullptr);
+  if (head) {
+    key_job(k, *head);
+    key_put(k, (uintptr_t)drafts);
+    key_put(k, nslots);
+    for (int i = 0; i < nslots; i++) {
+      key_put(k, slots[i].row0);
+      key_put(k, slots[i].ndraft);
+    }
+    key_put(k, (uintptr_t)argmax);
+    key_put(k, (uintptr_t)maxlogit);
+    key_put(k, (uintptr_t)accepted);
+  }
+  return k;
+}
+
+void drop_entry(qgemm_round_cache_s::Entry& e) {
+  qgemm_round_destroy(e.round);
+  if (e.ws) (void)hipFree(e.ws);
+  e.round = nullptr;
+  e.ws = nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+qgemm_status qgemm_round_cache_create(int capacity, qgemm_round_cache** out) {
+  if (!out) return QGEMM_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (capacity < 1 || capacity > QGEMM_ROUND_CACHE_MAX) return QGEMM_ERR_INVALID_ARG;
+  qgemm_round_cache* c = new qgemm_round_cache();
+  c->cap = capacity;
+  *out = c;
+  return QGEMM_OK;
+}
+
+qgemm_status qgemm_round_cache_run(qgemm_round_cache* c, const qgemm_round_sweep* sweeps, int nsweeps,
+                                   const qgemm_job* head, const int32_t* drafts, const qgemm_slot* slots,
+                                   int nslots, int32_t* argmax, float* maxlogit, int32_t* accepted,
+                                   void* stream, int* hit) {
+  if (hit) *hit = 0;
+  if (!c || !hit) return QGEMM_ERR_INVALID_ARG;
+  if (nsweeps < 0 || (nsweeps > 0 && !sweeps) || (nsweeps == 0 && !head)) return QGEMM_ERR_INVALID_ARG;
+  for (int i = 0; i < nsweeps; i++)
+    if (sweeps[i].njobs < 1 || !sweeps[i].jobs) return QGEMM_ERR_INVALID_ARG;
+  if (head && (nslots < 0 || (nslots > 0 && !slots))) return QGEMM_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> g(c->mu);
+  const std::string key = round_key(sweeps, nsweeps, head, drafts, slots, head ? nslots : 0, argmax, maxlogit,
+                                    accepted);
+  auto it = c->index.find(key);
+  if (it != c->index.end()) {
+    c->lru.splice(c->lru.begin(), c->lru, it->second);
+    c->hits++;
+    *hit = 1;
+    return qgemm_round_launch(c->lru.front().round, stream);
+  }
+  // a miss: the round's plan first (every argument error before any HIP
+  // call), then its recording, and only then an eviction, so that a call
+  // that fails leaves the cache as it was
+  RoundPlan R;
+  qgemm_status st = round_plan(sweeps, nsweeps, head, R, nullptr);
+  if (st != QGEMM_OK) return st;
+  if (head) {
+    qg::AcceptArgs a;  // (the recording builds its own)
+    if ((st = head_args(head, drafts, slots, nslots, argmax, maxlogit, accepted, nullptr, 0, a)) != QGEMM_OK)
+      return st;
+  }
+  void* ws = nullptr;
+  if (hipMalloc(&ws, R.total) != hipSuccess) return QGEMM_ERR_HIP;
+  qgemm_round* r = nullptr;
+  if (hipMemsetAsync(ws, 0, R.total, (hipStream_t)stream) != hipSuccess) {
+    (void)hipFree(ws);
+    return QGEMM_ERR_HIP;
+  }
+  st = qgemm_round_create(sweeps, nsweeps, head, drafts, slots, nslots, argmax, maxlogit, accepted, ws, R.total,
+                          stream, &r);
+  if (st != QGEMM_OK) {
+    (void)hipStreamSynchronize((hipStream_t)stream);
+    (void)hipFree(ws);
+    return st;
+  }
+  if ((int)c->lru.size() >= c->cap) {
+    // a replay of the evicted round may still run: wait for the device
+    if (hipDeviceSynchronize() != hipSuccess) {
+      qgemm_round_destroy(r);
+      (void)hipFree(ws);
+      return QGEMM_ERR_HIP;
+    }
+    qgemm_round_cache_s::Entry& e = c->lru.back();
+    c->index.erase(e.key);
+    drop_entry(e);
+    c->lru.pop_back();
+    c->evictions++;
+  }
+  c->lru.push_front(qgemm_round_cache_s::Entry{key, r, ws});
+  c->index[key] = c->lru.begin();
+  c->misses++;
+  return qgemm_round_launch(r, stream);
+}
+
+qgemm_status qgemm_round_cache_stats(const qgemm_round_cache* c, int* size, uint64_t* hits, uint64_t* misses,
+                                     uint64_t* evictions) {
+  if (!c) return QGEMM_ERR_INVALID_ARG;
+  qgemm_round_cache* m = const_cast<qgemm_round_cache*>(c);
+  std::lock_guard<std::mutex> g(m->mu);
+  if (size) *size = (int)c->lru.size();
+  if (hits) *hits = c->hits;
+  if (misses) *misses = c->misses;
+  if (evictions) *evictions = c->evictions;
+  return QGEMM_OK;
+}
+
+void qgemm_round_cache_destroy(qgemm_round_cache* c) {
+  if (!c) return;
+  for (auto& e : c->lru) drop_entry(e);
+  delete c;
 }
 
 }  // extern "C"

@@ -26,7 +26,9 @@ EXPORTS = (
     "qgemm_status_string", "qgemm_verify_workspace_bytes", "qgemm_verify_head",
     "qgemm_round_workspace_bytes", "qgemm_round_create", "qgemm_round_launch", "qgemm_round_kernels",
     "qgemm_round_destroy", "qgemm_attn_workspace_bytes", "qgemm_attn_verify", "qgemm_sweep_noalloc",
+    "qgemm_round_cache_create", "qgemm_round_cache_run", "qgemm_round_cache_stats", "qgemm_round_cache_destroy",
 )
+ROUND_CACHE_MAX = 4096
 NOALLOC_SCRATCH_BYTES = 64 << 20
 KV_FP16, KV_FP8 = 0, 1
 ATTN_HKV, ATTN_GROUP, ATTN_D, ATTN_MAX_W, ATTN_MAX_SLOTS = 4, 6, 256, 16, 16
@@ -117,6 +119,16 @@ def lib() -> ctypes.CDLL:
         L.qgemm_round_kernels.restype = ci
         L.qgemm_round_destroy.argtypes = [vp]
         L.qgemm_round_destroy.restype = None
+        L.qgemm_round_cache_create.argtypes = [ci, ctypes.POINTER(vp)]
+        L.qgemm_round_cache_create.restype = ci
+        L.qgemm_round_cache_run.argtypes = [vp, rp, ci, jp, vp, ctypes.POINTER(Slot), ci, vp, vp, vp, vp,
+                                            ctypes.POINTER(ci)]
+        L.qgemm_round_cache_run.restype = ci
+        u64p = ctypes.POINTER(ctypes.c_uint64)
+        L.qgemm_round_cache_stats.argtypes = [vp, ctypes.POINTER(ci), u64p, u64p, u64p]
+        L.qgemm_round_cache_stats.restype = ci
+        L.qgemm_round_cache_destroy.argtypes = [vp]
+        L.qgemm_round_cache_destroy.restype = None
         ap = ctypes.POINTER(AttnSlot)
         L.qgemm_attn_workspace_bytes.argtypes = [ap, ci, ci]
         L.qgemm_attn_workspace_bytes.restype = sz
@@ -315,6 +327,41 @@ class Round:
     def destroy(self) -> None:
         if self.handle:
             lib().qgemm_round_destroy(self.handle)
+            self.handle = None
+
+
+class RoundCache:
+    """Rounds keyed by what a recording fixes (``qgemm_round_cache``):
+    ``run`` replays a cached round or records a new one, evicting the least
+    recently used past the capacity."""
+
+    def __init__(self, capacity: int = 64):
+        h = ctypes.c_void_p()
+        _check(lib().qgemm_round_cache_create(int(capacity), ctypes.byref(h)), "qgemm_round_cache_create")
+        self.handle = h.value
+
+    def run(self, sweeps, head: Job | None = None, drafts=None, slots=(), argmax=None, accepted=None,
+            maxlogit=None, stream=None) -> bool:
+        """One round; True when it replayed a cached one."""
+        arr = sweeps if isinstance(sweeps, ctypes.Array) else round_sweeps(sweeps)
+        sl = slot_array(slots) if slots else None
+        hit = ctypes.c_int(0)
+        ptr = lambda t: t.data_ptr() if t is not None else None
+        _check(lib().qgemm_round_cache_run(self.handle, arr, len(arr),
+                                           ctypes.byref(head) if head is not None else None, ptr(drafts), sl,
+                                           len(sl) if sl else 0, ptr(argmax), ptr(maxlogit), ptr(accepted),
+                                           _stream_ptr(stream), ctypes.byref(hit)), "qgemm_round_cache_run")
+        return bool(hit.value)
+
+    def stats(self) -> dict:
+        size, hits, misses, ev = ctypes.c_int(), ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
+        _check(lib().qgemm_round_cache_stats(self.handle, ctypes.byref(size), ctypes.byref(hits),
+                                             ctypes.byref(misses), ctypes.byref(ev)), "qgemm_round_cache_stats")
+        return {"size": size.value, "hits": hits.value, "misses": misses.value, "evictions": ev.value}
+
+    def destroy(self) -> None:
+        if self.handle:
+            lib().qgemm_round_cache_destroy(self.handle)
             self.handle = None
 
 

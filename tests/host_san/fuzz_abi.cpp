@@ -10,6 +10,8 @@
 #include <cstdlib>
 #include <cstring>
 #include <random>
+#include <algorithm>
+#include <list>
 #include <vector>
 
 #include <hip/hip_runtime.h>
@@ -305,6 +307,78 @@ void round_case() {
            r2 == nullptr);
 }
 
+// The round cache against a model of its LRU order: a few round
+// descriptions (some with a head), a random sequence of runs, the hit flag,
+// size and counters checked after every call; the cache owns and frees the
+// workspaces (the sanitizers see a leak or a double free).
+void round_cache_case() {
+  const int nkeys = (int)rnd(1, 4), cap = (int)rnd(1, 3);
+  std::vector<std::vector<std::vector<qgemm_job>>> jobsets(nkeys);
+  std::vector<std::vector<qgemm_round_sweep>> sws(nkeys);
+  std::vector<qgemm_job> heads(nkeys);
+  std::vector<std::vector<qgemm_slot>> slots(nkeys);
+  std::vector<int32_t*> drafts(nkeys), argmax(nkeys), acc(nkeys);
+  for (int k = 0; k < nkeys; k++) {
+    const int ns = (int)rnd(1, 3);
+    std::vector<int> paths;
+    for (int i = 0; i < ns; i++) {
+      paths.push_back((int)rnd(0, 2));
+      jobsets[k].push_back(make_jobs(paths.back()));
+    }
+    for (int i = 0; i < ns; i++)
+      sws[k].push_back({jobsets[k][i].data(), (int32_t)jobsets[k][i].size(), (int32_t)paths[i]});
+    if (rnd(0, 1)) {
+      const int M = (int)rnd(1, 64);
+      heads[k] = make_head(M);
+      slots[k] = make_slots(M);
+      drafts[k] = (int32_t*)alloc((size_t)M * 4);
+      argmax[k] = (int32_t*)alloc((size_t)M * 4);
+      acc[k] = (int32_t*)alloc(slots[k].size() * 4);
+    }
+  }
+  qgemm_round_cache* c = nullptr;
+  EXPECT(qgemm_round_cache_create(cap, &c) == QGEMM_OK && c != nullptr);
+  std::list<int> model;  // front: most recent
+  uint64_t hits = 0, misses = 0, evictions = 0;
+  for (int t = 0; t < 10; t++) {
+    const int k = (int)rnd(0, nkeys - 1);
+    const bool hk = argmax[k] != nullptr;
+    int hit = -1;
+    g_calls++;
+    EXPECT(qgemm_round_cache_run(c, sws[k].data(), (int)sws[k].size(), hk ? &heads[k] : nullptr, drafts[k],
+                                 hk ? slots[k].data() : nullptr, hk ? (int)slots[k].size() : 0, argmax[k],
+                                 nullptr, acc[k], nullptr, &hit) == QGEMM_OK);
+    auto it = std::find(model.begin(), model.end(), k);
+    const bool want = it != model.end();
+    EXPECT(hit == (want ? 1 : 0));
+    if (want) {
+      model.erase(it);
+      hits++;
+    } else {
+      misses++;
+      if ((int)model.size() >= cap) {
+        model.pop_back();
+        evictions++;
+      }
+    }
+    model.push_front(k);
+    int size = -1;
+    uint64_t h = 0, m = 0, e = 0;
+    EXPECT(qgemm_round_cache_stats(c, &size, &h, &m, &e) == QGEMM_OK);
+    EXPECT(size == (int)model.size() && h == hits && m == misses && e == evictions);
+  }
+  // an invalid miss changes nothing
+  std::vector<qgemm_job> badj = jobsets[0][0];
+  badj[0].K = 100;
+  const qgemm_round_sweep bad = {badj.data(), (int32_t)badj.size(), 0};
+  int hit = 7;
+  EXPECT(qgemm_round_cache_run(c, &bad, 1, nullptr, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr,
+                               &hit) == QGEMM_ERR_INVALID_ARG && hit == 0);
+  int size = -1;
+  EXPECT(qgemm_round_cache_stats(c, &size, nullptr, nullptr, nullptr) == QGEMM_OK && size == (int)model.size());
+  qgemm_round_cache_destroy(c);
+}
+
 void attn_case() {
   const int n = (int)rnd(1, QGEMM_ATTN_MAX_SLOTS);
   const int kv = (int)rnd(0, 1);
@@ -391,13 +465,14 @@ int main(int argc, char** argv) {
       free_all();
       continue;
     }
-    switch (rnd(0, 6)) {
+    switch (rnd(0, 7)) {
       case 0: case 1: sweep_case(); break;
       case 2: verify_case(); break;
       case 3: round_case(); break;
       case 4: attn_case(); break;
       case 5: pack_case(); break;
       case 6: noalloc_case(); break;
+      case 7: round_cache_case(); break;
     }
     free_all();
   }

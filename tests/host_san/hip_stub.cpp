@@ -345,6 +345,10 @@ hipError_t hipStreamSynchronize(hipStream_t s) {
   CHECK(!g_capturing || s != g_capturing);
   return hipSuccess;
 }
+hipError_t hipDeviceSynchronize() {
+  CHECK(!g_capturing);
+  return hipSuccess;
+}
 hipError_t hipGetDevice(int* d) {
   *d = 0;
   return hipSuccess;

@@ -263,6 +263,47 @@ def test_round_validation_rejects_before_any_launch():
     L.qgemm_round_destroy(None)
 
 
+def test_round_cache_rejects_before_any_hip_call():
+    """Creation, bad arguments and every invalid miss return before any HIP
+    call, and leave the cache as it was."""
+    L = qgemm.lib()
+    out = ctypes.c_void_p()
+    assert L.qgemm_round_cache_create(0, ctypes.byref(out)) == qgemm.ERR_INVALID_ARG
+    assert L.qgemm_round_cache_create(qgemm.ROUND_CACHE_MAX + 1, ctypes.byref(out)) == qgemm.ERR_INVALID_ARG
+    assert L.qgemm_round_cache_create(4, None) == qgemm.ERR_INVALID_ARG
+    assert out.value is None
+    cache = qgemm.RoundCache(4)
+    try:
+        hit = ctypes.c_int(7)
+        sw = qgemm.round_sweeps([([_job()], qgemm.PATH_AUTO)])
+
+        def run(c=cache.handle, sweeps=sw, n=None, h=None, slots=None, h_out=ctypes.byref(hit), am=0x50001000,
+                acc=0x50002000, d=0x50000000):
+            return L.qgemm_round_cache_run(c, sweeps, len(sweeps) if n is None else n,
+                                           ctypes.byref(h) if h is not None else None, d, slots,
+                                           len(slots) if slots else 0, am, None, acc, None, h_out)
+
+        assert run(c=None) == qgemm.ERR_INVALID_ARG
+        assert hit.value == 0
+        assert run(h_out=None) == qgemm.ERR_INVALID_ARG
+        assert run(n=-1) == qgemm.ERR_INVALID_ARG
+        assert run(sweeps=None, n=0) == qgemm.ERR_INVALID_ARG            # no sweeps and no head
+        assert run(sweeps=qgemm.round_sweeps([([_job(K=100)], 0)])) == qgemm.ERR_INVALID_ARG
+        assert run(sweeps=qgemm.round_sweeps([([_job(M=0)], 0)])) == qgemm.ERR_INVALID_ARG
+        assert run(sweeps=qgemm.round_sweeps([([_job()], 9)])) == qgemm.ERR_INVALID_ARG
+        head = _job(M=6, Y=0)
+        good = qgemm.slot_array([(0, 5)])
+        assert run(h=head, slots=qgemm.slot_array([(0, 6)])) == qgemm.ERR_INVALID_ARG
+        assert run(h=head, slots=good, am=None) == qgemm.ERR_INVALID_ARG
+        assert run(h=head, slots=good, d=None) == qgemm.ERR_INVALID_ARG
+        assert run(h=head, slots=None) == qgemm.ERR_INVALID_ARG
+        assert cache.stats() == {"size": 0, "hits": 0, "misses": 0, "evictions": 0}
+        assert L.qgemm_round_cache_stats(None, None, None, None, None) == qgemm.ERR_INVALID_ARG
+    finally:
+        cache.destroy()
+    L.qgemm_round_cache_destroy(None)
+
+
 def test_attn_validation_rejects_before_any_launch():
     L = qgemm.lib()
 

@@ -162,3 +162,43 @@ def test_round_without_head_and_two_rounds_share_nothing():
         torch.cuda.synchronize()
         r1.destroy()
         r2.destroy()
+
+
+def test_round_cache_replays_records_and_evicts():
+    """Three round descriptions through a cache of two: the first two layer
+    sweeps, the rest, and the whole round with the verify head.  Every run,
+    hit or miss, must equal the eager calls of the same sweeps bitwise on
+    fresh panels; hits, misses and least-recently-used evictions follow the
+    sequence."""
+    import torch
+
+    c = RoundCase(6, layers=1, table_jobs=13)
+    keys = [c.sweeps[:2], c.sweeps[2:], c.sweeps]
+    nm = len(c.mats)
+    mats_of = [range(0, 2), range(2, nm), range(0, nm)]
+    cache = qgemm.RoundCache(2)
+    seq = [0, 0, 1, 0, 2, 1, 0, 2, 2]
+    want_hit = [False, True, False, True, False, False, False, False, True]
+    try:
+        for t, (k, wh) in enumerate(zip(seq, want_hit)):
+            c.fill(500 + 7 * t)
+            c.poison()
+            c.eager()
+            want = c.outputs()
+            c.poison()
+            head = k == 2
+            hit = cache.run(keys[k], c.head if head else None, c.drafts if head else None, c.slots if head else (),
+                            c.argmax if head else None, c.accepted if head else None)
+            got = c.outputs()
+            say(f"  run {t}: key {k} hit={hit}")
+            assert hit == wh, (t, k, hit)
+            for i in mats_of[k]:
+                assert np.isfinite(want[0][i]).all() and np.array_equal(got[0][i], want[0][i]), (t, c.mats[i][0])
+            if head:
+                assert np.array_equal(got[0][-1], want[0][-1])
+                assert np.array_equal(got[1], want[1]) and np.array_equal(got[2], want[2])
+        st = cache.stats()
+        assert st == {"size": 2, "hits": 3, "misses": 6, "evictions": 4}, st
+    finally:
+        torch.cuda.synchronize()
+        cache.destroy()
