@@ -267,8 +267,8 @@ def round_bench(args):
     order (256 launches, as an engine that interleaves other work between
     layers issues them), then the verify head over the lm_head-class matrix,
     at M = 6 (one slot, five drafts).  Times a round issued call by call
-    against the same round replayed as one graph, and the host time to issue
-    each; one JSON line."""
+    against the same round replayed as one graph (directly, and through the
+    keyed round cache), and the host time to issue each; one JSON line."""
     import ctypes
 
     import torch
@@ -331,10 +331,21 @@ def round_bench(args):
         L.qgemm_verify_head(ctypes.byref(head), drafts.data_ptr(), slot_arr, 1, am.data_ptr(), None,
                             acc.data_ptr(), vws.ptr, vws.nbytes, sp)
 
+    # the same round through the keyed cache: recorded on the first call,
+    # replayed on every later one (the key is rebuilt and looked up per call)
+    cache = q.RoundCache(64)
+
+    def cached():
+        cache.run(rsw, head, drafts, slots, am, acc)
+
     eager_ms, eager_host = timed(eager, args.steps, args.warmup)
     graph_ms, graph_host = timed(rnd.launch, args.steps, args.warmup)
+    cached()
+    cache_ms, cache_host = timed(cached, args.steps, args.warmup)
     fused_ms, fused_host = timed(fused, args.steps, args.warmup)
     torch.cuda.synchronize()
+    cache_stats = cache.stats()
+    cache.destroy()
     rnd.destroy()
     wb = b.weight_bytes + workloads.weight_bytes(mh.bits, mh.N, mh.K)
     print(json.dumps({
@@ -342,6 +353,7 @@ def round_bench(args):
         "kernels_per_round": rnd.kernels if rnd.handle else len(jobs) + 2,
         "eager_ms": round(eager_ms, 4), "eager_host_ms": round(eager_host, 4),
         "graph_ms": round(graph_ms, 4), "graph_host_ms": round(graph_host, 4),
+        "cache_hit_ms": round(cache_ms, 4), "cache_hit_host_ms": round(cache_host, 4), "cache": cache_stats,
         "fused_launch_ms": round(fused_ms, 4),
         "graph_speedup": round(eager_ms / graph_ms, 3),
         "graph_weight_GBps": round(wb / (graph_ms / 1e3) / 1e9, 1),
