@@ -174,11 +174,20 @@ int class_of(int kind, int M) {
 int cu_count();
 
 // Waves of a stream launch: kStreamWaves (kStreamWavesBig for a big launch),
-// but never more than T / kMaxUnitWeight, so that every wave holds at least
-// one step.  Depends on the shapes only, never on M.
+// but a launch too small to give every wave kMinSteps steps takes fewer
+// waves -- down to kFloorWaves, below which every wave holds at least one
+// step, as many as that allows.  Fewer waves split a row group over fewer
+// contributors: a 5120 x 5120 matrix at M = 6 has 3200 steps, 1.6 per wave
+// of 2048 and a row group of 40 k tiles split over up to 26 of them
+// (measured: a round of 256 one-matrix sweeps 5.27 -> 4.82 ms; a 1024 x 1024
+// matrix keeps its 104 waves, which its latency needs).  Depends on the
+// shapes only, never on M.
+constexpr int64_t kMinSteps = 4, kFloorWaves = 512;
 int64_t stream_waves(int64_t T, bool big) {
-  return std::max<int64_t>(1, std::min<int64_t>(big ? qg::kStreamWavesBig : qg::kStreamWaves,
-                                                T / qg::kMaxUnitWeight));
+  const int64_t cap = big ? qg::kStreamWavesBig : qg::kStreamWaves;
+  const int64_t one = T / qg::kMaxUnitWeight;  // waves that hold at least one step each
+  const int64_t w = std::max(T / (kMinSteps * qg::kMaxUnitWeight), std::min(one, kFloorWaves));
+  return std::max<int64_t>(1, std::min(cap, w));
 }
 
 Plan make_plan(const qgemm_job* jobs, int njobs, int path, unsigned long long* keys = nullptr) {
