@@ -189,6 +189,26 @@ class Bench:
         ms = e0.elapsed_time(e1) / steps
         return ms, wall
 
+    def run_calls(self, calls, warmup):
+        """Per-call event times (us): an event pair on the stream around
+        each call; p10, median and p90 over the calls."""
+        import numpy as np
+        import torch
+
+        self.stream = torch.cuda.current_stream().cuda_stream
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        for i, (e0, e1) in enumerate(ev):
+            e0.record()
+            self.step(warmup + i)
+            e1.record()
+        torch.cuda.synchronize()
+        us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev])
+        p10, med, p90 = (round(float(x), 3) for x in np.percentile(us, [10, 50, 90]))
+        return {"calls": calls, "p10": p10, "median": med, "p90": p90}
+
     def report(self, ms):
         s = ms / 1e3
         gbps = self.weight_bytes / s / 1e9
@@ -753,6 +773,9 @@ def main():
                 r["read_ceiling"] = c
             if cfg == 1:
                 r["us_per_sweep"] = round(ms * 1e3, 3)
+            # per call (an event pair around each): the spread behind the mean
+            if cfg in (1, 2, 3):
+                r["per_call_us"] = b.run_calls(50, 10)
             configs[str(cfg)] = r
             log(f"[bench] workload {cfg}: {json.dumps(r)}")
         del b
