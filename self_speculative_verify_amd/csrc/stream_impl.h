@@ -522,7 +522,8 @@ struct Stream {
     const int b = a + cx.q + (cx.gw < cx.rem ? 1 : 0);
     Phases P;
     const StreamGrid grid = {args.index, args.njobs, args.bshift, cx.q, cx.rem};
-    stream_plan(P, grid, D, cx.gw, a, b);
+    if (args.njobs == 1) stream_plan<true>(P, grid, D, cx.gw, a, b);
+    else stream_plan<false>(P, grid, D, cx.gw, a, b);
 
     Pos pc, cc;
     stream_start(pc, D, P);

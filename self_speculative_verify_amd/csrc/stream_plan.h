@@ -192,9 +192,14 @@ QG_PLAN int stream_job_of(const StreamGrid& g, const QG_CONST JobDesc* D, int u)
 }
 
 // The phases of wave gw's range [a, b) (a non-empty set of steps).
+// kOne: the launch has one job, so both lookups are job 0 and its
+// descriptor's loads wait for no search (a launch of one matrix, the common
+// case, reaches its first load sooner: gate+up M = 1 22.0 -> 21.6 us, the
+// 1024 x 1024 sweep 7.0 -> 6.7 us).
+template <bool kOne = false>
 QG_PLAN void stream_plan(StreamPhases& P, const StreamGrid& g, const QG_CONST JobDesc* D, int gw, int a, int b) {
   // first step (jA, sA): the first step of job jA whose first unit is >= a
-  int jA = stream_job_of(g, D, a);
+  int jA = kOne ? 0 : stream_job_of(g, D, a);
   const int wA = unit_weight(D[jA].fmt), dA = a - D[jA].ubeg;
   int sA = dA <= 0 ? 0 : div_unit_weight(dA + wA - 1, D[jA].fmt);
   if (sA == D[jA].nrg * D[jA].nkt) {
@@ -202,7 +207,7 @@ QG_PLAN void stream_plan(StreamPhases& P, const StreamGrid& g, const QG_CONST Jo
     sA = 0;
   }
   // last step (jL, sL): the last step whose first unit is <= b - 1
-  const int jL = stream_job_of(g, D, b - 1);
+  const int jL = kOne ? 0 : stream_job_of(g, D, b - 1);
   const int sL = div_unit_weight(b - 1 - D[jL].ubeg, D[jL].fmt);
   const int nktA = D[jA].nkt, nktL = D[jL].nkt;
   const int rgA = div_nkt(sA, D[jA].nkt_m, D[jA].nkt_sh), rgL = div_nkt(sL, D[jL].nkt_m, D[jL].nkt_sh);

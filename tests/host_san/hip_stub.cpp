@@ -91,6 +91,13 @@ void stream_schedule_check(const qg::SweepArgs& a, const std::vector<qg::JobDesc
     const qg::StreamGrid g = {a.index, a.njobs, a.bshift, a.q, a.rem};
     qg::stream_plan(P, g, D.data(), w, u0, u1);
     CHECK((P.mask & 15) != 0);
+    if (a.njobs == 1) {
+      // the one-job plan the kernels take for such launches: the same phases
+      qg::StreamPhases P1;
+      qg::stream_plan<true>(P1, g, D.data(), w, u0, u1);
+      CHECK(P1.mask == P.mask && P1.jA == P.jA && P1.sA == P.sA && P1.jH == P.jH && P1.sH == P.sH &&
+            P1.jT == P.jT && P1.sT == P.sT && P1.jE == P.jE && P1.sE == P.sE);
+    }
     qg::StreamPos c;
     qg::stream_start(c, D.data(), P);
     int steps = 0;
