@@ -44,7 +44,7 @@ PATHS = {"auto": 0, "gemv": 1, "mfma": 2}
 TRAFFIC = {
     # FETCH_SIZE 50187.3 KiB x 2.0000 (a 1 GiB device copy reads 524300 KiB)
     # + WRITE_SIZE 4018 KiB x 1.0 (the copy writes 1048576 KiB)
-    "c1a229b05e113cc5": {"workload": "gate+up 5120->34816 4-bit M=1", "bytes": 107273124},
+    "05a3643de4055f21": {"workload": "gate+up 5120->34816 4-bit M=1", "bytes": 107305610},
 }
 KERNEL_SOURCES = ("self_speculative_verify_amd/csrc/qgemm_kernels.hip",
                   "self_speculative_verify_amd/csrc/qgemm_internal.h",
