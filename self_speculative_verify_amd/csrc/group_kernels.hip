@@ -410,6 +410,15 @@ struct Group {
   // writes row 8 t + L / 8, outputs 4 (L mod 8) .. + 3.
   static __device__ __forceinline__ void store_y(const JobDesc& d, const f4_t (&acc)[kRG][kMb], int rbw,
                                                  uint8_t* st, unsigned long long* best, int lane) {
+    // At 48 rows the compiler hoists the staging addresses below (two dozen
+    // per lane) out of the unit loop and, short of registers at three waves
+    // per SIMD, spills them: every wave then wrote and read back about 6 KB
+    // of scratch before its first loads, and the first unit started about
+    // 7 us after the kernel.  An opaque copy of the lane index keeps them in
+    // the loop (recomputed once per unit, no scratch; the verify head at
+    // M = 48 237 -> 229 us).  At 32 and 64 rows the hoisted form spills at
+    // most a few words and measured about 1 % faster.
+    if constexpr (kMPad == 48) asm volatile("" : "+v"(lane));
     const int mr = lane & 15, c = lane >> 4;
 #pragma unroll
     for (int r = 0; r < kRG; r++)
