@@ -181,7 +181,7 @@ struct Group {
   // the whole K take about as long with two busy waves per SIMD as with
   // three.
   static constexpr int kUnitRB = kW * kRG;
-  static constexpr int kFine = kW == 12 ? 16 : 8;
+  static constexpr int kFine = kW == 12 ? 16 : 8;   // busy waves: two per SIMD at 12 waves, else one
   static_assert(kFine % (4 * kRG) == 0 && kFine < kUnitRB, "fine units keep the busy waves spread over the SIMDs");
   struct Rounds {
     int total;   // units, the fine ones included
@@ -410,15 +410,16 @@ struct Group {
   // writes row 8 t + L / 8, outputs 4 (L mod 8) .. + 3.
   static __device__ __forceinline__ void store_y(const JobDesc& d, const f4_t (&acc)[kRG][kMb], int rbw,
                                                  uint8_t* st, unsigned long long* best, int lane) {
-    // At 48 rows the compiler hoists the staging addresses below (two dozen
-    // per lane) out of the unit loop and, short of registers at three waves
-    // per SIMD, spills them: every wave then wrote and read back about 6 KB
-    // of scratch before its first loads, and the first unit started about
-    // 7 us after the kernel.  An opaque copy of the lane index keeps them in
-    // the loop (recomputed once per unit, no scratch; the verify head at
-    // M = 48 237 -> 229 us).  At 32 and 64 rows the hoisted form spills at
-    // most a few words and measured about 1 % faster.
-    if constexpr (kMPad == 48) asm volatile("" : "+v"(lane));
+    // Left to itself the compiler hoists the staging addresses below (two
+    // dozen per lane) out of the unit loop and, short of registers, spills
+    // them: at 48 rows every wave then wrote and read back about 6 KB of
+    // scratch before its first loads, and the first unit started about 7 us
+    // after the kernel.  An opaque copy of the lane index keeps them in the
+    // loop (recomputed once per unit, no scratch; the verify head at M = 48
+    // 237 -> 229 us), and at 32 rows it is what lets four waves per SIMD fit
+    // in 128 VGPRs.  At 64 rows the hoisted form spills at most a few words
+    // and measured about 1 % faster.
+    if constexpr (kMPad <= 48) asm volatile("" : "+v"(lane));
     const int mr = lane & 15, c = lane >> 4;
 #pragma unroll
     for (int r = 0; r < kRG; r++)
@@ -462,7 +463,7 @@ struct Group {
 };
 
 template <int kMPad, bool kAll>
-__global__ void __launch_bounds__(64 * group_waves(kMPad)) __attribute__((amdgpu_waves_per_eu(kMPad >= 64 ? 2 : 3)))
+__global__ void __launch_bounds__(64 * group_waves(kMPad)) __attribute__((amdgpu_waves_per_eu(group_waves(kMPad) / 4)))
 group_kernel(SweepArgs) {
   using S = Group<kMPad>;
   __shared__ __attribute__((aligned(1024))) uint8_t xs[S::kLdsBytes];
