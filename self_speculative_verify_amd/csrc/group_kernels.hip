@@ -46,7 +46,13 @@ struct Group {
   static constexpr int kBufBytes = kXBytes + kW * 256;                // then 256 scale bytes per wave
   static constexpr int kYRow = kRG * kTileRows;                       // outputs n of a wave
   static_assert(kND * kThreads >= kMPad * 16, "X copies cover the panel");
-  static constexpr int kYBytes = kW * kMPad * kYRow * 4;             // output staging, after the ring
+  // 48 rows: the staging would not fit beside the ring at 16 waves, so the
+  // outputs are stored from the MFMA layout (64-byte row pieces, once per
+  // unit), and each row block's products are scaled right after its MFMAs
+  // (half the product registers live, which keeps the kernel in 128 VGPRs)
+  static constexpr bool kDirectY = kMPad == 48;
+  static constexpr bool kPerBlock = kMPad == 48;
+  static constexpr int kYBytes = kDirectY ? 0 : kW * kMPad * kYRow * 4;   // output staging, after the ring
   static constexpr int kRingBytes = kBufs * kBufBytes;
   static constexpr int kLdsBytes = kRingBytes + kYBytes + kMPad * 8;  // then one argmax key per row
   static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
@@ -175,13 +181,13 @@ struct Group {
   // blocks (kFine / kRG busy waves, the rest idle: their code loads are
   // empty and they only copy X and keep the barriers) if they then still fit
   // in one round, so that more workgroups share the round and fewer waves
-  // share each SIMD.  Measured: the 248320-row verify head at M = 48 (647
-  // units over 256 workgroups) 240 -> 236 us, the 5-bit stack at M = 32 and
-  // 48 about 1 % faster.  The gain is small because a wave's row blocks over
-  // the whole K take about as long with two busy waves per SIMD as with
-  // three.
+  // share each SIMD.  Measured with 12-wave workgroups (16-row fine units):
+  // the 248320-row verify head at M = 48 (647 units over 256 workgroups)
+  // 240 -> 236 us, the 5-bit stack at M = 32 and 48 about 1 % faster.  The
+  // gain is small because a wave's row blocks over the whole K take about as
+  // long with two busy waves per SIMD as with three.
   static constexpr int kUnitRB = kW * kRG;
-  static constexpr int kFine = kW == 12 ? 16 : 8;   // busy waves: two per SIMD at 12 waves, else one
+  static constexpr int kFine = 8;   // four busy waves, one per SIMD
   static_assert(kFine % (4 * kRG) == 0 && kFine < kUnitRB, "fine units keep the busy waves spread over the SIMDs");
   struct Rounds {
     int total;   // units, the fine ones included
@@ -322,6 +328,22 @@ struct Group {
           // group 64: the odd half of a group accumulates onto the even
           // half's products, which are scaled once, after it
           constexpr bool kG64 = F == kFmtG64;
+          if constexpr (kPerBlock && !kG64) {
+#pragma unroll
+            for (int r = 0; r < kRG; r++) {
+              const h8_t q = unpack_chunk<F>(buf[p].c[r][g], side_word<F>(buf[p].h[kSide<F> ? r : 0]), g);
+              f4_t pq[kMb];
+#pragma unroll
+              for (int mb = 0; mb < kMb; mb++) pq[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb], q, zero, 0, 0, 0);
+              const uint32_t sp = sc[2 * r + (g >> 1)];
+              const float sj = (g & 1) ? scale_f32<1>(sp) : scale_f32<0>(sp);
+#pragma unroll
+              for (int mb = 0; mb < kMb; mb++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) acc[r][mb][e] = __builtin_fmaf(sj, pq[mb][e], acc[r][mb][e]);
+            }
+            continue;
+          }
 #pragma unroll
           for (int r = 0; r < kRG; r++) {
             const h8_t q = unpack_chunk<F>(buf[p].c[r][g], side_word<F>(buf[p].h[kSide<F> ? r : 0]), g);
@@ -410,15 +432,43 @@ struct Group {
   // writes row 8 t + L / 8, outputs 4 (L mod 8) .. + 3.
   static __device__ __forceinline__ void store_y(const JobDesc& d, const f4_t (&acc)[kRG][kMb], int rbw,
                                                  uint8_t* st, unsigned long long* best, int lane) {
+    if constexpr (kDirectY) {
+      // lane (c, mr) holds rows 16 mb + 4 c + i of output n = 16 (rbw + r) + mr;
+      // the lane index is opaque so the addresses stay in the unit loop
+      asm volatile("" : "+v"(lane));
+      const int mr = lane & 15, c = lane >> 4;
+      QG_GLOBAL float* Y = (QG_GLOBAL float*)d.Y;
+#pragma unroll
+      for (int mb = 0; mb < kMb; mb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int m = 16 * mb + 4 * c + i;
+          unsigned long long k = 0ull;
+#pragma unroll
+          for (int r = 0; r < kRG; r++) {
+            const int n = kTileRows * (rbw + r) + mr;
+            if (m < d.M && n < d.N && Y) Y[(int64_t)m * d.ldy + n] = acc[r][mb][i];
+            if (d.keys && n < d.N) k = umax64(k, logit_key(acc[r][mb][i], n));
+          }
+          if (d.keys) {
+            // verify head: the best of the row's 32 outputs (16 lanes), into
+            // the workgroup's key of row m
+            k = lanes_max<1, 16>(k);
+            if (mr == 0 && m < d.M && k != 0ull)
+              __hip_atomic_fetch_max(best + m, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          }
+        }
+      return;
+    }
     // Left to itself the compiler hoists the staging addresses below (two
     // dozen per lane) out of the unit loop and, short of registers, spills
-    // them: at 48 rows every wave then wrote and read back about 6 KB of
-    // scratch before its first loads, and the first unit started about 7 us
-    // after the kernel.  An opaque copy of the lane index keeps them in the
-    // loop (recomputed once per unit, no scratch; the verify head at M = 48
-    // 237 -> 229 us), and at 32 rows it is what lets four waves per SIMD fit
-    // in 128 VGPRs.  At 64 rows the hoisted form spills at most a few words
-    // and measured about 1 % faster.
+    // them: at 48 rows with 12-wave workgroups every wave then wrote and read
+    // back about 6 KB of scratch before its first loads, and the first unit
+    // started about 7 us after the kernel.  An opaque copy of the lane index
+    // keeps them in the loop (recomputed once per unit, no scratch; the
+    // verify head at M = 48 237 -> 229 us then), and at 32 rows it is what
+    // lets four waves per SIMD fit in 128 VGPRs.  At 64 rows the hoisted
+    // form spills at most a few words and measured about 1 % faster.
     if constexpr (kMPad <= 48) asm volatile("" : "+v"(lane));
     const int mr = lane & 15, c = lane >> 4;
 #pragma unroll

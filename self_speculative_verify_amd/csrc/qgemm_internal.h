@@ -51,8 +51,8 @@ constexpr int64_t kStreamBigBytes = (int64_t)4 << 30;
 // group kernel (17..64 rows): waves per workgroup (three per SIMD where the
 // registers allow it: padded rows 32 and 48), 16-row blocks per wave
 // Waves of a group-kernel workgroup (one workgroup per CU): four per SIMD at
-// 32 rows (127 VGPRs), three at 48, two at 64.
-constexpr int group_waves(int mpad) { return mpad >= 64 ? 8 : mpad <= 32 ? 16 : 12; }
+// 32 and 48 rows (128 VGPRs), two at 64.
+constexpr int group_waves(int mpad) { return mpad >= 64 ? 8 : 16; }
 constexpr int kGroupRows = 2;
 
 // Stream kernels walk "steps": one k tile of a row group of stream_rows(big)
