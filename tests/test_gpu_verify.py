@@ -115,6 +115,7 @@ CASES = [
     ("two slots 5-bit", 4099, 320, 5, 12, [(0, 5), (6, 5)]),
     ("no drafts", 2050, 128, 4, 1, [(0, 0)]),
     ("eight slots group kernel", 5000, 512, 4, 48, [(6 * i, 5) for i in range(8)]),
+    ("padded rows class 48", 2999, 192, 5, 37, [(6 * i, 5) for i in range(5)] + [(30, 6)]),
     ("ragged slots class 32", 1000, 96, 5, 17, [(0, 3), (4, 6), (11, 5)]),
     ("class 64", 777, 160, 4, 64, [(8 * i, 7) for i in range(8)]),
     ("one row N=16", 16, 64, 4, 2, [(0, 1)]),
