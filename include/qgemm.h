@@ -328,7 +328,10 @@ qgemm_status qgemm_round_cache_run(qgemm_round_cache* cache, const qgemm_round_s
 qgemm_status qgemm_round_cache_stats(const qgemm_round_cache* cache, int* size, uint64_t* hits, uint64_t* misses,
                                      uint64_t* evictions);
 
-/* Free every round and workspace (NULL is a no-op). */
+/* Free every round and workspace (NULL is a no-op).  When the cache holds
+ * rounds it first synchronizes the device, since replays of them may still
+ * run on any stream; a call must not overlap a qgemm_round_cache_run on the
+ * same cache. */
 void qgemm_round_cache_destroy(qgemm_round_cache* cache);
 
 /* ---------------------------------------------------------------------------

@@ -794,6 +794,8 @@ qgemm_status qgemm_round_cache_stats(const qgemm_round_cache* c, int* size, uint
 
 void qgemm_round_cache_destroy(qgemm_round_cache* c) {
   if (!c) return;
+  // replays of the held rounds may still run on the callers' streams
+  if (!c->lru.empty()) (void)hipDeviceSynchronize();
   for (auto& e : c->lru) drop_entry(e);
   delete c;
 }
