@@ -243,11 +243,12 @@ def test_edge_shapes(bits, N, K, M):
 
 
 # A group-kernel launch of more than one round whose last round is partial
-# and lies in its one job: that round is cut into finer units (16 row blocks
-# for the 12-wave kernels at M = 17..48, 8 for the 8-wave kernel at M = 49..64)
-# on a 256-workgroup grid.  301 units of 24 (or 16) row blocks, the last
-# partial, N ragged, k-tile counts with and without the unit chaining.
-RESLICE = [(4, 48, 7213 * 16 - 5, 256), (5, 32, 7213 * 16 - 11, 512), (4, 64, 4809 * 16 - 3, 160)]
+# and lies in its one job: that round is cut into units of 8 row blocks on a
+# 256-workgroup grid.  At M = 17..48 (16-wave workgroups, 32 row blocks a
+# unit) 9000 row blocks are 282 units, the last partial; at M = 49..64
+# (8-wave workgroups, 16 row blocks) 4809 row blocks are 301.  N ragged,
+# k-tile counts with and without the unit chaining.
+RESLICE = [(4, 48, 9000 * 16 - 5, 256), (5, 32, 9000 * 16 - 11, 512), (4, 64, 4809 * 16 - 3, 160)]
 
 
 @pytest.mark.parametrize("bits,M,N,K", RESLICE)
