@@ -42,9 +42,9 @@ PATHS = {"auto": 0, "gemv": 1, "mfma": 2}
 # has the commands and raw figures).  Valid only for the kernel sources they
 # were taken on: keyed by the SHA-256 of those sources, else reported as null.
 TRAFFIC = {
-    # FETCH_SIZE 50379.6 KiB x 1.9999 (a 1 GiB device copy reads 524305 KiB)
+    # FETCH_SIZE 50380.0 KiB x 1.9999 (a 1 GiB device copy reads 524305 KiB)
     # + WRITE_SIZE 4018 KiB x 1.0 (the copy writes 1048576 KiB)
-    "c2e6aec8d93602c8": {"workload": "gate+up 5120->34816 4-bit M=1", "bytes": 107288484},
+    "42f71eff0fb17887": {"workload": "gate+up 5120->34816 4-bit M=1", "bytes": 107289400},
 }
 KERNEL_SOURCES = ("self_speculative_verify_amd/csrc/qgemm_kernels.hip",
                   "self_speculative_verify_amd/csrc/qgemm_internal.h",

@@ -63,7 +63,9 @@ struct Stream {
   static constexpr int kAcc = kR * kA;                         // partial-sum floats per lane
   static_assert(kAcc % 4 == 0, "slot words move in 16-byte stores");
   static constexpr int kXP = (kCap * 16 + 63) / 64;            // 16-byte X pieces per lane and step
-  static constexpr int kDepth = 2;                             // steps in flight
+  // steps in flight: one for MFMA class 16 in eight-block steps, whose two
+  // step buffers would leave it one wave per SIMD (see kTwoPerSimd)
+  static constexpr int kDepth = (kMfma && kCap == 16 && kR == 8) ? 1 : 2;
   static constexpr bool kSide = (kFS & (kSetQ5 | kSetZP)) != 0;
   static constexpr int kOnly = kFS == kSetQ4 ? kFmtQ4 : kFS == kSetQ5 ? kFmtQ5 : kFS == kSetG64 ? kFmtG64
                                : kFS == kSetZP ? kFmtZP : 0;   // the one format, or 0
@@ -664,10 +666,13 @@ struct Stream {
 // eight-block steps is built under that register budget: left to itself it
 // takes 198 VGPRs + 66 AGPRs (one wave per SIMD); within 256 it keeps its
 // MFMA results in VGPRs and fits two (the 5-bit stack at M = 8: 2.70 ->
-// 2.60 ms).  The others already fit two (or would spill under the budget:
-// MFMA class 16 in eight-block steps, GEMV class 8) and keep the plain bounds.
+// 2.60 ms).  Class 16 in eight-block steps took 254 VGPRs + 136 AGPRs (one
+// wave per SIMD); with one step in flight instead of two it fits two in 245
+// VGPRs (the 5-bit stack at M = 9 / 12 / 16: 3.04 / 3.07 / 3.14 -> 2.85 /
+// 2.93 / 3.02 ms).  The others already fit two (or, GEMV class 8, would
+// spill under the budget) and keep the plain bounds.
 template <bool kMfma, int kCap, int kR>
-constexpr bool kTwoPerSimd = kMfma && kR == 8 && kCap == 8;
+constexpr bool kTwoPerSimd = kMfma && kR == 8 && kCap >= 8;
 
 template <bool kMfma, int kCap, int kR, int kFS>
 __global__ void __launch_bounds__(64 * kStreamWavesPerBlock) stream_kernel(SweepArgs) {
